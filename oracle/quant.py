@@ -1,0 +1,212 @@
+"""Quantizers of the FP8 blockwise linear layer (CPU oracle).
+
+Test infrastructure: see the package docstring.
+
+Inputs are bf16 values given as fp32 (or fp64) arrays holding exactly the bf16
+values.  Outputs are uint8 E4M3 codes plus scales.
+
+Definitions followed
+--------------------
+* Quantize / dequantize: q = clamp(round(x/s), -448, 448), x_hat = q*s,
+  round = round-to-nearest-even; the clamp keeps outliers from becoming NaN
+  ([SGL19] "从浮点到 FP8 的基本公式").
+* Dynamic per-token-group activation scale: each run of 128 consecutive
+  channels of a row gets s_g = max|x| / 448 and q = round(x / s_g); the
+  scales form an [M, ceil(K/128)] fp32 grid, row-major by default
+  ([GLM17] "第 1 站:RMSNorm 的两个出口"; [SGL19] "Triton 分块内核在做什么").
+* Per-tensor scale s = max|W| / 448 ([SGL19] "从浮点到 FP8 的基本公式").
+* Block-wise weight scale: the same rule restricted to each b_n x b_k
+  sub-matrix (128x128), on a ceil(N/b_n) x ceil(K/b_k) grid whose last
+  row/column of blocks may be partial ([SGL19] "建权重:先决定 scale 的形状",
+  "从浮点到 FP8 的基本公式").
+* MXFP8: 1x32 blocks, one UE8M0 (power-of-two, uint8) scale each
+  ([SGLFP8] "1. Fp8Config 초기화", "4. 블록 양자화 스케일 관리"); the scale
+  exponent is rounded UP so the block never overflows:
+  scale = 2^ceil(log2(max(amax, 1e-10) / 448))
+  ([GLM17] "第 4 站:索引器——FP8 与排名稳定性").
+* RMSNorm: y = x / sqrt(mean(x^2) + eps) * g, statistics in high precision,
+  bf16 output ([GLM17] "第 1 站:RMSNorm 的两个出口").
+
+Readings where the pages leave a step open
+------------------------------------------
+(i)   x/s is one IEEE fp32 division, then one RNE rounding to E4M3 (the scale
+      is fp32, and the kernel computes in fp32).
+(ii)  s = amax/448 is an fp32 division, not a multiply by 1/448.
+(iii) amax is floored at fp32(1e-10) before dividing (the only floor the pages
+      print, in the UE8M0 rule); a zero group gets s = fp32(1e-10)/448, q = 0.
+(iv)  clamp to +-448 before the cast.
+(v)   the sign of zero is kept (-0 and negatives rounding to zero -> 0x80).
+(vi)  RMSNorm: r = 1/sqrt(sum(x^2)/K + eps) is evaluated in fp64 from an
+      exactly rounded sum and rounded once to fp32; y = bf16(fp32(fp32(x*r)*g)).
+      The quantizer consumes the bf16 y.
+(vii) MX exponent: e = the smallest integer with max(amax, 1e-10) <= 448*2^e,
+      stored as the byte e + 127; q = E4M3(x * 2^-e) (exact scaling).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from . import bf16, e4m3
+
+FP8_MAX = np.float32(448.0)
+AMAX_FLOOR = np.float32(1e-10)
+UE8M0_BIAS = 127
+
+
+def _ngroups(K: int, g: int) -> int:
+    return -(-K // g)
+
+
+def group_scale(amax) -> np.ndarray:
+    """fp32 scale from a group's max |x|: max(amax, 1e-10) / 448 in fp32."""
+    a = np.maximum(np.asarray(amax, dtype=np.float32), AMAX_FLOOR)
+    return (a / FP8_MAX).astype(np.float32)          # IEEE fp32 division
+
+
+def quantize_with_scale(x, s) -> np.ndarray:
+    """E4M3 codes of clamp(RN32(x / s), -448, 448); x, s broadcastable fp32."""
+    x = np.asarray(x, dtype=np.float32)
+    s = np.asarray(s, dtype=np.float32)
+    t = (x / s).astype(np.float32)                    # IEEE fp32 division
+    t = np.clip(t, -FP8_MAX, FP8_MAX)
+    return e4m3.encode(t)
+
+
+def quant_group(x, group: int = 128):
+    """Dynamic per-token-group quantization with fp32 scales.
+
+    x: [M, K] bf16 values (fp32 array).  Returns (q uint8 [M, K],
+    s float32 [M, ceil(K/group)]) with s in row-major order.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    M, K = x.shape
+    G = _ngroups(K, group)
+    q = np.empty((M, K), dtype=np.uint8)
+    s = np.empty((M, G), dtype=np.float32)
+    for g in range(G):
+        cols = slice(g * group, min(K, (g + 1) * group))
+        xs = x[:, cols]
+        amax = np.max(np.abs(xs), axis=1)
+        sg = group_scale(amax)
+        s[:, g] = sg
+        q[:, cols] = quantize_with_scale(xs, sg[:, None])
+    return q, s
+
+
+def quant_static(x, scale):
+    """Static per-tensor activation quantization with a given fp32 scalar."""
+    x = np.asarray(x, dtype=np.float32)
+    return quantize_with_scale(x, np.float32(scale))
+
+
+def mx_exponent(amax) -> np.ndarray:
+    """Smallest integer e with max(amax, 1e-10) <= 448 * 2^e (reading vii)."""
+    a = np.maximum(np.asarray(amax, dtype=np.float32), AMAX_FLOOR).astype(np.float64)
+    e = np.ceil(np.log2(a / 448.0)).astype(np.int64)      # estimate ...
+    # ... then settled by exact comparisons (448 * 2^e is exact in fp64)
+    e = np.where(a <= np.ldexp(448.0, e - 1), e - 1, e)
+    e = np.where(a > np.ldexp(448.0, e), e + 1, e)
+    return e
+
+
+def quant_mx(x, group: int = 32):
+    """MXFP8: 1 x group blocks with UE8M0 scale bytes.
+
+    Returns (q uint8 [M, K], scale bytes uint8 [M, ceil(K/group)]).
+    """
+    x = np.asarray(x, dtype=np.float32)
+    M, K = x.shape
+    G = _ngroups(K, group)
+    q = np.empty((M, K), dtype=np.uint8)
+    sb = np.empty((M, G), dtype=np.uint8)
+    for g in range(G):
+        cols = slice(g * group, min(K, (g + 1) * group))
+        xs = x[:, cols].astype(np.float64)
+        e = mx_exponent(np.max(np.abs(xs), axis=1))
+        sb[:, g] = (e + UE8M0_BIAS).astype(np.uint8)
+        t = np.ldexp(xs, -e[:, None])                    # exact power-of-two scaling
+        q[:, cols] = e4m3.encode(np.clip(t, -448.0, 448.0))
+    return q, sb
+
+
+def quant_weight_block(w, block_n: int = 128, block_k: int = 128):
+    """Block-wise weight quantization: one fp32 scale per block_n x block_k.
+
+    Returns (q uint8 [N, K], s float32 [ceil(N/block_n), ceil(K/block_k)]).
+    """
+    w = np.asarray(w, dtype=np.float32)
+    N, K = w.shape
+    NB, KB = _ngroups(N, block_n), _ngroups(K, block_k)
+    q = np.empty((N, K), dtype=np.uint8)
+    s = np.empty((NB, KB), dtype=np.float32)
+    for i in range(NB):
+        rows = slice(i * block_n, min(N, (i + 1) * block_n))
+        for j in range(KB):
+            cols = slice(j * block_k, min(K, (j + 1) * block_k))
+            blk = w[rows, cols]
+            sb = group_scale(np.max(np.abs(blk)))
+            s[i, j] = sb
+            q[rows, cols] = quantize_with_scale(blk, sb)
+    return q, s
+
+
+def quant_tensor(w):
+    """Per-tensor quantization: one fp32 scale for the whole matrix."""
+    w = np.asarray(w, dtype=np.float32)
+    s = group_scale(np.max(np.abs(w)))
+    return quantize_with_scale(w, s), np.float32(s)
+
+
+def rms_inv(x, eps: float):
+    """Per-row r = RN32(1/sqrt(sum(x^2)/K + eps)) plus near-tie information.
+
+    The sum of squares of bf16 values is taken exactly rounded (math.fsum of
+    exact fp64 squares); mean, +eps, sqrt and reciprocal run in fp64.
+    Returns (r float32 [M], r_alt float32 [M], ambiguous bool [M]): a row is
+    ambiguous when its fp64 value lies within 2^-40 (relative) of the midpoint
+    between two fp32 numbers -- there any fp64 evaluation order may round to
+    either neighbour, and r_alt is the other one.
+    """
+    x64 = np.asarray(x, dtype=np.float64)
+    M, K = x64.shape
+    ss = np.array([math.fsum(row) for row in (x64 * x64)], dtype=np.float64)
+    r64 = 1.0 / np.sqrt(ss / K + float(np.float32(eps)))
+    r = r64.astype(np.float32)
+    up = np.nextafter(r, np.float32(np.inf))
+    dn = np.nextafter(r, np.float32(0))
+    other = np.where(r64 >= r.astype(np.float64), up, dn).astype(np.float32)
+    mid = (r.astype(np.float64) + other.astype(np.float64)) * 0.5
+    ambiguous = np.abs(r64 - mid) <= np.abs(r64) * 2.0 ** -40
+    return r, other, ambiguous
+
+
+def rmsnorm_apply(x, g, r):
+    """y = bf16(fp32(fp32(x * r) * g)) for given per-row fp32 r; uint16 bits."""
+    x32 = np.asarray(x, dtype=np.float32)
+    g32 = np.asarray(g, dtype=np.float32)
+    t = (x32 * np.asarray(r, dtype=np.float32)[:, None]).astype(np.float32)
+    t = (t * g32[None, :]).astype(np.float32)
+    return bf16.round_from_f64(t.astype(np.float64))
+
+
+def rmsnorm(x, g, eps: float):
+    """RMSNorm with bf16 output.  Returns (y bits uint16 [M,K], r, r_alt, ambiguous)."""
+    r, r_alt, amb = rms_inv(x, eps)
+    return rmsnorm_apply(x, g, r), r, r_alt, amb
+
+
+def rmsnorm_quant(x, g, eps: float, group: int = 128, r=None):
+    """RMSNorm -> bf16 -> dynamic group quantization (reading vi).
+
+    Returns dict(q, s, y, r, r_alt, ambiguous).  Pass ``r`` to evaluate the
+    same pipeline with a chosen per-row factor (used for near-tie rows).
+    """
+    if r is None:
+        r, r_alt, amb = rms_inv(x, eps)
+    else:
+        r_alt, amb = None, None
+    y = rmsnorm_apply(x, g, r)
+    q, s = quant_group(bf16.to_f32(y), group)
+    return {"q": q, "s": s, "y": y, "r": r, "r_alt": r_alt, "ambiguous": amb}

@@ -1,0 +1,148 @@
+"""Planted mistakes in the oracle (CPU only): each plausible slip must fail a pin.
+
+Every case patches one oracle function with a subtly wrong variant and runs
+the relevant pin check; the check has to raise.  Nothing here touches a GPU.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import e4m3, gemm, quant
+
+
+def _encode_ties_away(v):
+    v = np.asarray(v, np.float64)
+    a = np.abs(v)
+    pos = e4m3.DECODE_TABLE[:127]
+    lo = np.clip(np.searchsorted(pos, a, side="right") - 1, 0, 126)
+    hi = np.minimum(lo + 1, 126)
+    mid = (pos[lo] + pos[hi]) / 2
+    code = np.where(a < mid, lo, hi)                 # ties go up: wrong
+    return (code | (np.signbit(v).astype(np.int64) << 7)).astype(np.uint8)
+
+
+def _encode_truncate(v):
+    v = np.asarray(v, np.float64)
+    pos = e4m3.DECODE_TABLE[:127]
+    lo = np.clip(np.searchsorted(pos, np.abs(v), side="right") - 1, 0, 126)
+    return (lo | (np.signbit(v).astype(np.int64) << 7)).astype(np.uint8)
+
+
+def _check_encode_vs_torch(enc):
+    rng = np.random.default_rng(0)
+    vals = np.clip(rng.uniform(-448, 448, 50_000).astype(np.float32), -448, 448)
+    pos = e4m3.DECODE_TABLE[:127]
+    vals = np.concatenate([vals, ((pos[:-1] + pos[1:]) / 2).astype(np.float32)])
+    ref = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(enc(vals), ref)
+
+
+@pytest.mark.parametrize("bad", [_encode_ties_away, _encode_truncate])
+def test_encoder_mistakes_are_caught(bad):
+    _check_encode_vs_torch(e4m3.encode)          # the real one passes
+    with pytest.raises(AssertionError):
+        _check_encode_vs_torch(bad)
+
+
+def _check_group_invariants(qfun):
+    rng = np.random.default_rng(1)
+    x = torch.from_numpy(rng.standard_normal((32, 512)).astype(np.float32)).to(torch.bfloat16).float().numpy()
+    q, s = qfun(x)
+    dq = np.abs(e4m3.decode(q)).reshape(32, 4, 128).max(axis=2)
+    assert np.all(dq == 448.0)
+    amax = np.abs(x).reshape(32, 4, 128).max(axis=2)
+    np.testing.assert_allclose(s, amax / 448.0, rtol=2.0 ** -23)
+    # equivariance under powers of two
+    q2, s2 = qfun(np.ldexp(x, 3))
+    np.testing.assert_array_equal(q2, q)
+
+
+def _group_scale_wrong_constant(x):
+    x = np.asarray(x, np.float32)
+    s = (np.abs(x).reshape(x.shape[0], -1, 128).max(axis=2) / np.float32(240)).astype(np.float32)
+    return quant.quantize_with_scale(x, np.repeat(s, 128, axis=1)), s
+
+
+def _group_off_by_one_group(x):
+    q, s = quant.quant_group(x)
+    return q, np.roll(s, 1, axis=1)
+
+
+@pytest.mark.parametrize("bad", [_group_scale_wrong_constant, _group_off_by_one_group])
+def test_group_quant_mistakes_are_caught(bad):
+    _check_group_invariants(quant.quant_group)
+    with pytest.raises(AssertionError):
+        _check_group_invariants(bad)
+
+
+def _check_gemm(gfun):
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((6, 384)).astype(np.float32)
+    w = (rng.standard_normal((260, 384)) / 20).astype(np.float32)
+    qa, sa = quant.quant_group(x)
+    qw, sw = quant.quant_weight_block(w)
+    _, acc = gfun(qa, sa, qw, sw)
+    np.testing.assert_allclose(acc, gemm.gemm_dequant_reference(qa, sa, qw, sw), rtol=1e-12)
+
+
+def _gemm_transposed_wscale(qa, sa, qw, sw):
+    # uses the weight-scale grid of block (b, j//128) instead of (j//128, b)
+    sw_t = np.resize(np.asarray(sw).T, np.asarray(sw).shape)
+    return gemm.gemm_blockscale(qa, sa, qw, sw_t)
+
+
+def _gemm_drop_last_block(qa, sa, qw, sw):
+    qa = qa.copy()
+    qa[:, 256:] = 0
+    return gemm.gemm_blockscale(qa, sa, qw, sw)
+
+
+def _gemm_scales_outside_sum(qa, sa, qw, sw):
+    A, W = e4m3.decode(qa), e4m3.decode(qw)
+    acc = (A @ W.T) * sa.mean(axis=1)[:, None] * np.repeat(sw.mean(axis=1), 128)[None, :W.shape[0]]
+    return None, acc
+
+
+@pytest.mark.parametrize("bad", [_gemm_transposed_wscale, _gemm_drop_last_block,
+                                 _gemm_scales_outside_sum])
+def test_gemm_mistakes_are_caught(bad):
+    _check_gemm(gemm.gemm_blockscale)
+    with pytest.raises(AssertionError):
+        _check_gemm(bad)
+
+
+def _check_mx_exponent(efun):
+    a = np.ldexp(np.linspace(1, 2, 4097)[:-1], 3).astype(np.float32)
+    e = efun(a)
+    t = np.ldexp(a.astype(np.float64), -e)
+    assert np.all(t <= 448) and np.all(t > 224)
+
+
+def _mx_exponent_round_nearest(amax):
+    a = np.maximum(np.asarray(amax, np.float32), np.float32(1e-10)).astype(np.float64)
+    return np.rint(np.log2(a / 448.0)).astype(np.int64)
+
+
+def _mx_exponent_floor(amax):
+    a = np.maximum(np.asarray(amax, np.float32), np.float32(1e-10)).astype(np.float64)
+    return np.floor(np.log2(a / 448.0)).astype(np.int64)
+
+
+@pytest.mark.parametrize("bad", [_mx_exponent_round_nearest, _mx_exponent_floor])
+def test_mx_exponent_mistakes_are_caught(bad):
+    _check_mx_exponent(quant.mx_exponent)
+    with pytest.raises(AssertionError):
+        _check_mx_exponent(bad)
+
+
+def test_rmsnorm_missing_eps_or_sqrt_is_caught():
+    K = 64
+    c = np.float32(0.001)
+    x = np.full((1, K), c, np.float32)
+    r, _, _ = quant.rms_inv(x, 1e-6)
+    expect = np.float32(1.0 / math.sqrt(float(c) ** 2 + float(np.float32(1e-6))))
+    assert r[0] == expect
+    assert np.float32(1.0 / math.sqrt(float(c) ** 2)) != expect       # eps dropped
+    assert np.float32(1.0 / (float(c) ** 2 + 1e-6)) != expect          # sqrt dropped
