@@ -1,0 +1,275 @@
+#!/usr/bin/env python3
+"""Throughput of the FP8 blockwise linear layer on one MI355X (gfx950).
+
+A step is one forward pass of the linear layer over one batch of synthetic
+activations already resident in HBM: the activation quantizer (fused with
+RMSNorm for the prefill-with-norm workload) followed by the scaled GEMM.  The
+weight is quantized once before timing (it is offline preparation).  Inputs
+and outputs rotate over several buffer sets whose total exceeds the 256 MB
+Infinity Cache, so HBM rates are not inflated by cache hits.
+
+Prints ONE JSON line.  `value` = 2*M*N*K per step / step time (whole layer,
+quantizer included); `roofline` is for the dominant kernel (the GEMM), timed
+per launch with HIP events on the stream it runs on; `cpu_baseline` is the CPU
+oracle timed on a bounded sample of the same workload on this host.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "block-FP8 GEMM TFLOP/s & % FP8 MFMA peak; group-quant HBM GB/s"
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA, 5.0 PFLOP/s
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E, 8 TB/s
+MALL_DEFEAT_BYTES = 640 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="prefill_norm",
+                    choices=["tiny", "decode", "prefill_norm", "large", "mx", "pertensor"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample (0 = skip)")
+    return ap.parse_args()
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "fp8_block_scaled_token_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(f.encode())
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per GEMM launch from committed rocprofv3 counters, or None
+    when the kernels have changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    t = json.load(open(path))
+    if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    rec = t.get("workloads", {}).get(workload)
+    return None if rec is None else rec.get("traffic_bytes")
+
+
+def main() -> int:
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1; sharding is described in DESIGN.md)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import fp8_block_scaled_token_amd as fq
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    fq.load_library()
+
+    name = args.workload
+    wl = workloads.WORKLOADS["mx" if name == "pertensor" else name]
+    M, N, K = wl.M, wl.N, wl.K
+    d = wl.make("cpu")
+    x_cpu, w_cpu = d["x"], d["w"]
+    KB, NB = math.ceil(K / 128), math.ceil(N / 128)
+
+    # ---- weights: quantized once (offline preparation, not timed)
+    wd = w_cpu.cuda()
+    if name == "mx":
+        qw, sw = fq.quant_weight_mx(wd)
+    elif name == "pertensor":
+        qw, sw = fq.quant_weight_tensor(wd)
+    else:
+        qw, sw = fq.quant_weight_block(wd)
+    gamma = d["gamma"].cuda() if wl.norm else None
+    del wd
+    sx_static = None
+    if name == "pertensor":
+        amax = float(x_cpu.float().abs().max())
+        sx_static = torch.tensor([np.float32(np.float32(amax) / np.float32(448.0))], device="cuda")
+
+    # ---- rotating activation / output sets (beat the Infinity Cache)
+    set_bytes = M * K * 2 + M * K + M * KB * 4 + M * N * 2
+    nsets = max(1, min(8, math.ceil(MALL_DEFEAT_BYTES / set_bytes)))
+    xg = x_cpu.cuda()
+    sets = []
+    for _ in range(nsets):
+        s = {"x": xg.clone(), "q": torch.empty(M, K, dtype=torch.uint8, device="cuda")}
+        if name == "mx":
+            s["s"] = torch.empty(M, math.ceil(K / 32), dtype=torch.uint8, device="cuda")
+        elif name == "pertensor":
+            s["s"] = sx_static
+        else:
+            s["s"] = torch.empty(M, KB, dtype=torch.float32, device="cuda")
+        s["y"] = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        sets.append(s)
+    del xg
+
+    def quant(s):
+        if wl.norm:
+            fq.fp8q_rmsnorm_quant(s["x"], gamma, d["eps"], fq.ROW_MAJOR, s["q"], s["s"])
+        elif name == "mx":
+            fq.fp8q_quant_act_group(s["x"], 32, fq.SCALE_UE8M0, fq.ROW_MAJOR, None, s["q"], s["s"])
+        elif name == "pertensor":
+            fq.fp8q_quant_act_group(s["x"], 128, fq.SCALE_F32, fq.ROW_MAJOR, sx_static, s["q"], None)
+        else:
+            fq.fp8q_quant_act_group(s["x"], 128, fq.SCALE_F32, fq.ROW_MAJOR, None, s["q"], s["s"])
+
+    def gemm(s):
+        if name == "mx":
+            fq.fp8q_gemm_mxfp8(s["q"], s["s"], qw, sw, None, s["y"])
+        elif name == "pertensor":
+            fq.fp8q_gemm_blockscale(s["q"], s["s"], fq.ROW_MAJOR, qw, sw, None, s["y"], fq.GRAN_PER_TENSOR)
+        else:
+            fq.fp8q_gemm_blockscale(s["q"], s["s"], fq.ROW_MAJOR, qw, sw, None, s["y"], fq.GRAN_BLOCK128)
+
+    for i in range(args.warmup):
+        s = sets[i % nsets]
+        quant(s)
+        gemm(s)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        s = sets[i % nsets]
+        ev[i][0].record(stream)
+        quant(s)
+        ev[i][1].record(stream)
+        gemm(s)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    quant_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    gemm_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    ms_per_step = wall * 1e3 / args.steps
+    flops = 2.0 * M * N * K
+    value = flops / (ms_per_step * 1e-3) / 1e12
+
+    # algorithmic bytes
+    if name == "mx":
+        q_bytes = M * K * 2 + M * K + M * math.ceil(K / 32)
+        g_bytes = M * K + N * K + (M + N) * math.ceil(K / 32) + 2 * M * N
+    elif name == "pertensor":
+        q_bytes = M * K * 2 + M * K
+        g_bytes = M * K + N * K + 8 + 2 * M * N
+    else:
+        q_bytes = M * K * 2 + M * K + 4 * M * KB + (2 * K if wl.norm else 0)
+        g_bytes = M * K + N * K + 4 * M * KB + 4 * NB * KB + 2 * M * N
+    gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
+    gemm_gbps = g_bytes / (gemm_ms * 1e-3) / 1e9
+    quant_gbps = q_bytes / (quant_ms * 1e-3) / 1e9
+    hbm_bound = M <= 64
+    traffic = measured_traffic(name)
+    if hbm_bound:
+        roof = {"bound": "hbm", "achieved": round(gemm_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(gemm_gbps / PEAK_HBM_GBPS, 4), "traffic": traffic}
+    else:
+        roof = {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_FP8_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "traffic": traffic}
+
+    kernel_q = {"prefill_norm": "rmsnorm_quant", "mx": "quant_group32mx",
+                "pertensor": "quant_static"}.get(name, "quant_group128")
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate)", "data": "synthetic",
+        "config": {"workload": name, "M": M, "N": N, "K": K, "norm": wl.norm,
+                   "scales": {"mx": "1x32 ue8m0", "pertensor": "per-tensor fp32"}.get(name, "group128 + 128x128 fp32"),
+                   "rotating_buffer_sets": nsets},
+        "roofline": roof,
+        "gemm": {"us": round(gemm_ms * 1e3, 2), "TFLOP/s": round(gemm_tflops, 1),
+                 "frac_fp8_peak": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "GB/s": round(gemm_gbps, 1),
+                 "algorithmic_bytes": g_bytes},
+        "quant": {"kernel": kernel_q, "us": round(quant_ms * 1e3, 2), "GB/s": round(quant_gbps, 1),
+                  "frac_hbm": round(quant_gbps / PEAK_HBM_GBPS, 4), "algorithmic_bytes": q_bytes},
+        "cpu_baseline": None,
+    }
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(name, wl, d, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def cpu_baseline(name, wl, d, target_s):
+    """Time the CPU oracle (as it stands) on a bounded row sample."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = None
+    from oracle import gemm as og
+    from oracle import quant as oq
+
+    M, N, K = wl.M, wl.N, wl.K
+    xh = d["x"].float().numpy()
+    wh = d["w"].float().numpy()
+    if name == "mx":
+        qw, sw = oq.quant_mx(wh)
+    elif name == "pertensor":
+        qw, sw = oq.quant_tensor(wh)
+        sx = np.float32(np.float32(np.abs(xh).max()) / np.float32(448.0))
+    else:
+        qw, sw = oq.quant_weight_block(wh)
+    gh = d["gamma"].float().numpy() if wl.norm else None
+
+    def run(rows):
+        xs = xh[:rows]
+        if wl.norm:
+            r = oq.rmsnorm_quant(xs, gh, d["eps"])
+            og.gemm_blockscale(r["q"], r["s"], qw, sw)
+        elif name == "mx":
+            qa, ea = oq.quant_mx(xs)
+            og.gemm_mx(qa, ea, qw, sw)
+        elif name == "pertensor":
+            og.gemm_pertensor(oq.quant_static(xs, sx), sx, qw, sw)
+        else:
+            qa, sa = oq.quant_group(xs)
+            og.gemm_blockscale(qa, sa, qw, sw)
+
+    rows = min(M, 4)
+    t0 = time.perf_counter()
+    run(rows)
+    t = time.perf_counter() - t0
+    if t < target_s and rows < M:
+        rows = int(min(M, max(rows, rows * target_s / max(t, 1e-3))))
+        t0 = time.perf_counter()
+        run(rows)
+        t = time.perf_counter() - t0
+    tflops = 2.0 * rows * N * K / t / 1e12
+    return {"value": tflops, "unit": "TFLOP/s", "cores": blas_threads or len(os.sched_getaffinity(0)),
+            "kind": "oracle",
+            "sample": f"{rows} of {M} activation rows through the oracle's quantizer + GEMM "
+                      f"({t:.1f} s; weight quantized beforehand, untimed)",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,270 @@
+"""fp8_block_scaled_token_amd -- Python binding of libfp8q (MI355X / gfx950).
+
+Argument marshalling only: every computation runs in the HIP kernels of
+libfp8q.so, reached through its C ABI (include/fp8q.h).  torch supplies device
+memory and the current stream.  There is no fallback: if the library is
+missing or the device is not gfx950 the calls raise.
+
+Functions named ``fp8q_*`` mirror the C entry points one to one (tensors in
+place of pointers, sizes read from the tensors).  The short-named helpers
+(``quant_act_group`` ...) allocate the outputs and call them.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "load_library", "FP8QError", "abi_version",
+    "fp8q_quant_act_group", "fp8q_rmsnorm_quant", "fp8q_quant_weight_block",
+    "fp8q_gemm_blockscale", "fp8q_gemm_mxfp8",
+    "quant_act_group", "quant_act_static", "quant_act_mx", "rmsnorm_quant",
+    "quant_weight_block", "quant_weight_mx", "quant_weight_tensor",
+    "gemm_blockscale", "gemm_pertensor", "gemm_mxfp8",
+    "SCALE_F32", "SCALE_UE8M0", "ROW_MAJOR", "COL_MAJOR", "GRAN_BLOCK128", "GRAN_PER_TENSOR",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8q.so")
+
+SCALE_F32, SCALE_UE8M0 = 0, 1
+ROW_MAJOR, COL_MAJOR = 0, 1
+GRAN_BLOCK128, GRAN_PER_TENSOR = 0, 1
+
+_STATUS = {0: "ok", 1: "null", 2: "shape", 3: "unsupported", 4: "misaligned",
+           5: "device", 6: "launch", 7: "value"}
+
+#: exported symbol -> (restype, argtypes); mirrors include/fp8q.h
+_P, _I64, _I32, _F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+SIGNATURES = {
+    "fp8q_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "fp8q_abi_version": (ctypes.c_int, []),
+    "fp8q_quant_act_group": (ctypes.c_int, [_P, _I64, _I64, _I64, _I32, _I32, _I32, _P, _P, _I64, _P, _P]),
+    "fp8q_rmsnorm_quant": (ctypes.c_int, [_P, _P, _F, _I64, _I64, _I64, _I32, _P, _I64, _P, _P, _I64, _P]),
+    "fp8q_quant_weight_block": (ctypes.c_int, [_P, _I64, _I64, _I64, _I32, _I32, _I32, _P, _I64, _P, _P]),
+    "fp8q_gemm_blockscale": (ctypes.c_int, [_P, _I64, _P, _I32, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _P]),
+    "fp8q_gemm_mxfp8": (ctypes.c_int, [_P, _I64, _P, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _I64, _P]),
+}
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class FP8QError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        msg = load_library().fp8q_status_string(status).decode()
+        super().__init__(f"{what}: {msg} (status {status}, {_STATUS.get(status, '?')})")
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfp8q.so once (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise ImportError(f"{path} not found: build it with `python -m fp8_block_scaled_token_amd.build`")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = lib
+    return _lib
+
+
+def abi_version() -> int:
+    return load_library().fp8q_abi_version()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise FP8QError(status, what)
+
+
+def _rows(t: torch.Tensor, dtype: torch.dtype, name: str):
+    """(rows, K, ld) of a row-major 2-D tensor with unit column stride."""
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != 2 or (t.size(1) > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name} must be a 2-D row-major tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    return t.size(0), t.size(1), t.stride(0)
+
+
+def _u8(t: torch.Tensor) -> torch.Tensor:
+    return t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t
+
+
+# --------------------------------------------------------------------------
+# one-to-one mirrors of the C entry points
+
+
+def fp8q_quant_act_group(x, group_size, fmt, layout, static_scale, q, scales, stream=None):
+    M, K, ldx = _rows(x, torch.bfloat16, "x")
+    q = _u8(q)
+    Mq, Kq, ldq = _rows(q, torch.uint8, "q")
+    if (Mq, Kq) != (M, K):
+        raise ValueError("q shape must match x")
+    _check(load_library().fp8q_quant_act_group(_ptr(x), M, K, ldx, group_size, fmt, layout,
+                                               _ptr(static_scale), _ptr(q), ldq, _ptr(scales),
+                                               _stream(stream)), "fp8q_quant_act_group")
+
+
+def fp8q_rmsnorm_quant(x, gamma, eps, layout, q, scales, y_out=None, stream=None):
+    M, K, ldx = _rows(x, torch.bfloat16, "x")
+    q = _u8(q)
+    _, _, ldq = _rows(q, torch.uint8, "q")
+    ldy = 0
+    if y_out is not None:
+        _, _, ldy = _rows(y_out, torch.bfloat16, "y_out")
+    if gamma.dtype != torch.bfloat16 or gamma.numel() != K or not gamma.is_contiguous():
+        raise ValueError("gamma must be a contiguous bf16 tensor of K elements")
+    _check(load_library().fp8q_rmsnorm_quant(_ptr(x), _ptr(gamma), float(eps), M, K, ldx, layout,
+                                             _ptr(q), ldq, _ptr(scales), _ptr(y_out), ldy,
+                                             _stream(stream)), "fp8q_rmsnorm_quant")
+
+
+def fp8q_quant_weight_block(w, block_n, block_k, fmt, q, scale_inv, stream=None):
+    N, K, ldw = _rows(w, torch.bfloat16, "w")
+    q = _u8(q)
+    _, _, ldq = _rows(q, torch.uint8, "q")
+    _check(load_library().fp8q_quant_weight_block(_ptr(w), N, K, ldw, block_n, block_k, fmt,
+                                                  _ptr(q), ldq, _ptr(scale_inv), _stream(stream)),
+           "fp8q_quant_weight_block")
+
+
+def fp8q_gemm_blockscale(a, a_scales, a_layout, w, w_scale_inv, bias, y, gran, stream=None):
+    a, w = _u8(a), _u8(w)
+    M, K, lda = _rows(a, torch.uint8, "a")
+    N, Kw, ldw = _rows(w, torch.uint8, "w")
+    My, Ny, ldy = _rows(y, torch.bfloat16, "y")
+    if Kw != K or (My, Ny) != (M, N):
+        raise ValueError("shape mismatch between a, w and y")
+    _check(load_library().fp8q_gemm_blockscale(_ptr(a), lda, _ptr(a_scales), a_layout, _ptr(w), ldw,
+                                               _ptr(w_scale_inv), _ptr(bias), _ptr(y), ldy, M, N, K,
+                                               gran, _stream(stream)), "fp8q_gemm_blockscale")
+
+
+def fp8q_gemm_mxfp8(a, a_scales, w, w_scales, bias, y, stream=None):
+    a, w = _u8(a), _u8(w)
+    M, K, lda = _rows(a, torch.uint8, "a")
+    N, Kw, ldw = _rows(w, torch.uint8, "w")
+    My, Ny, ldy = _rows(y, torch.bfloat16, "y")
+    if Kw != K or (My, Ny) != (M, N):
+        raise ValueError("shape mismatch between a, w and y")
+    _check(load_library().fp8q_gemm_mxfp8(_ptr(a), lda, _ptr(a_scales), _ptr(w), ldw, _ptr(w_scales),
+                                          _ptr(bias), _ptr(y), ldy, M, N, K, _stream(stream)),
+           "fp8q_gemm_mxfp8")
+
+
+# --------------------------------------------------------------------------
+# allocating helpers
+
+
+def _cdiv(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def _q_like(M: int, K: int, device) -> torch.Tensor:
+    """uint8 [M, K] view of an [M, ld] buffer with ld a multiple of 16."""
+    ld = _cdiv(K, 16) * 16
+    return torch.empty(M, ld, dtype=torch.uint8, device=device)[:, :K]
+
+
+def quant_act_group(x: torch.Tensor, layout: int = ROW_MAJOR, stream=None):
+    """(q uint8 [M,K], scales fp32 [M, ceil(K/128)] or [ceil(K/128), M])."""
+    M, K = x.shape
+    G = _cdiv(K, 128)
+    q = _q_like(M, K, x.device)
+    s = torch.empty((G, M) if layout == COL_MAJOR else (M, G), dtype=torch.float32, device=x.device)
+    fp8q_quant_act_group(x, 128, SCALE_F32, layout, None, q, s, stream)
+    return q, s
+
+
+def quant_act_mx(x: torch.Tensor, stream=None):
+    """(q uint8 [M,K], UE8M0 scale bytes uint8 [M, ceil(K/32)])."""
+    M, K = x.shape
+    q = _q_like(M, K, x.device)
+    s = torch.empty(M, _cdiv(K, 32), dtype=torch.uint8, device=x.device)
+    fp8q_quant_act_group(x, 32, SCALE_UE8M0, ROW_MAJOR, None, q, s, stream)
+    return q, s
+
+
+def quant_act_static(x: torch.Tensor, scale: torch.Tensor, stream=None):
+    """q uint8 [M,K] with a given device fp32 scalar scale."""
+    M, K = x.shape
+    q = _q_like(M, K, x.device)
+    fp8q_quant_act_group(x, 128, SCALE_F32, ROW_MAJOR, scale, q, None, stream)
+    return q
+
+
+def rmsnorm_quant(x, gamma, eps: float = 1e-6, layout: int = ROW_MAJOR, return_y: bool = False, stream=None):
+    """(q, scales[, y]) of RMSNorm(x) followed by group-128 quantization."""
+    M, K = x.shape
+    G = _cdiv(K, 128)
+    q = _q_like(M, K, x.device)
+    s = torch.empty((G, M) if layout == COL_MAJOR else (M, G), dtype=torch.float32, device=x.device)
+    y = torch.empty(M, K, dtype=torch.bfloat16, device=x.device) if return_y else None
+    fp8q_rmsnorm_quant(x, gamma, eps, layout, q, s, y, stream)
+    return (q, s, y) if return_y else (q, s)
+
+
+def quant_weight_block(w: torch.Tensor, stream=None):
+    """(q uint8 [N,K], scale_inv fp32 [ceil(N/128), ceil(K/128)])."""
+    N, K = w.shape
+    q = _q_like(N, K, w.device)
+    s = torch.empty(_cdiv(N, 128), _cdiv(K, 128), dtype=torch.float32, device=w.device)
+    fp8q_quant_weight_block(w, 128, 128, SCALE_F32, q, s, stream)
+    return q, s
+
+
+def quant_weight_mx(w: torch.Tensor, stream=None):
+    N, K = w.shape
+    q = _q_like(N, K, w.device)
+    s = torch.empty(N, _cdiv(K, 32), dtype=torch.uint8, device=w.device)
+    fp8q_quant_weight_block(w, 1, 32, SCALE_UE8M0, q, s, stream)
+    return q, s
+
+
+def quant_weight_tensor(w: torch.Tensor, stream=None):
+    N, K = w.shape
+    q = _q_like(N, K, w.device)
+    s = torch.empty(1, dtype=torch.float32, device=w.device)
+    fp8q_quant_weight_block(w, N, K, SCALE_F32, q, s, stream)
+    return q, s
+
+
+def _y(M: int, N: int, device) -> torch.Tensor:
+    ld = _cdiv(N, 8) * 8
+    return torch.empty(M, ld, dtype=torch.bfloat16, device=device)[:, :N]
+
+
+def gemm_blockscale(a, a_scales, w, w_scale_inv, bias=None, a_layout: int = ROW_MAJOR, stream=None):
+    y = _y(a.shape[0], w.shape[0], a.device)
+    fp8q_gemm_blockscale(a, a_scales, a_layout, w, w_scale_inv, bias, y, GRAN_BLOCK128, stream)
+    return y
+
+
+def gemm_pertensor(a, a_scale, w, w_scale, bias=None, stream=None):
+    y = _y(a.shape[0], w.shape[0], a.device)
+    fp8q_gemm_blockscale(a, a_scale, ROW_MAJOR, w, w_scale, bias, y, GRAN_PER_TENSOR, stream)
+    return y
+
+
+def gemm_mxfp8(a, a_scales, w, w_scales, bias=None, stream=None):
+    y = _y(a.shape[0], w.shape[0], a.device)
+    fp8q_gemm_mxfp8(a, a_scales, w, w_scales, bias, y, stream)
+    return y

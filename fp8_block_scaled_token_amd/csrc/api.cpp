@@ -1,0 +1,187 @@
+// C ABI of fp8q: argument checking, device check, and kernel dispatch.
+// The declarations and their contracts are in include/fp8q.h.
+#include "fp8q.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "launch.h"
+
+namespace {
+
+using fp8q_status = fp8q_status_t;
+
+constexpr int kMaxDevices = 64;
+// 0 = not checked yet, 1 = gfx950, 2 = something else
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+fp8q_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FP8Q_ERR_DEVICE;
+  if (dev < kMaxDevices) {
+    const int c = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (c == 1) return FP8Q_OK;
+    if (c == 2) return FP8Q_ERR_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FP8Q_ERR_DEVICE;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices) g_arch_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? FP8Q_OK : FP8Q_ERR_DEVICE;
+}
+
+fp8q_status launch_status(hipError_t e) { return e == hipSuccess ? FP8Q_OK : FP8Q_ERR_LAUNCH; }
+
+// A row-major matrix operand: rows x K elements with stride ld, 16-byte rows.
+fp8q_status check_matrix(const void* p, int64_t K, int64_t ld, int elem_bytes) {
+  if (p == nullptr) return FP8Q_ERR_NULL;
+  if (ld < K) return FP8Q_ERR_SHAPE;
+  if (!aligned16(p) || (ld * elem_bytes) % 16 != 0) return FP8Q_ERR_MISALIGNED;
+  return FP8Q_OK;
+}
+
+#define FP8Q_TRY(expr)                 \
+  do {                                 \
+    const fp8q_status s_ = (expr);     \
+    if (s_ != FP8Q_OK) return s_;      \
+  } while (0)
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+
+}  // namespace
+
+extern "C" {
+
+const char* fp8q_status_string(fp8q_status_t s) {
+  switch (s) {
+    case FP8Q_OK: return "ok";
+    case FP8Q_ERR_NULL: return "null pointer argument";
+    case FP8Q_ERR_SHAPE: return "invalid shape (negative extent, K <= 0, or ld < K)";
+    case FP8Q_ERR_UNSUPPORTED: return "unsupported group/block/format/layout combination";
+    case FP8Q_ERR_MISALIGNED: return "misaligned pointer or stride (rows must start on 16-byte boundaries)";
+    case FP8Q_ERR_DEVICE: return "current HIP device is not gfx950 (or device query failed)";
+    case FP8Q_ERR_LAUNCH: return "kernel launch failed";
+    case FP8Q_ERR_VALUE: return "invalid scalar argument";
+  }
+  return "unknown status";
+}
+
+int fp8q_abi_version(void) { return FP8Q_ABI_VERSION; }
+
+fp8q_status_t fp8q_quant_act_group(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                   int32_t group_size, int32_t fmt, int32_t layout,
+                                   const float* static_scale, uint8_t* q, int64_t ldq,
+                                   void* scales, void* stream) {
+  if (M < 0 || K <= 0 || M > kMaxDim || K > kMaxDim) return FP8Q_ERR_SHAPE;
+  if (static_scale == nullptr) {
+    const bool g128 = group_size == 128 && fmt == FP8Q_SCALE_F32;
+    const bool g32 = group_size == 32 && fmt == FP8Q_SCALE_UE8M0;
+    if (!g128 && !g32) return FP8Q_ERR_UNSUPPORTED;
+    if (layout != FP8Q_SCALES_ROW_MAJOR && layout != FP8Q_SCALES_COL_MAJOR) return FP8Q_ERR_UNSUPPORTED;
+  }
+  if (M == 0) return FP8Q_OK;
+  FP8Q_TRY(check_matrix(x, K, ldx, 2));
+  FP8Q_TRY(check_matrix(q, K, ldq, 1));
+  if (static_scale == nullptr && scales == nullptr) return FP8Q_ERR_NULL;
+  if (static_scale == nullptr && fmt == FP8Q_SCALE_F32 && (reinterpret_cast<uintptr_t>(scales) & 3u))
+    return FP8Q_ERR_MISALIGNED;
+  FP8Q_TRY(check_device());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int colm = layout == FP8Q_SCALES_COL_MAJOR;
+  hipError_t e;
+  if (static_scale != nullptr)
+    e = fp8q::launch_quant_static(x, M, K, ldx, static_scale, q, ldq, st);
+  else if (group_size == 128)
+    e = fp8q::launch_quant_group128(x, M, K, ldx, q, ldq, static_cast<float*>(scales), colm, st);
+  else
+    e = fp8q::launch_quant_group32mx(x, M, K, ldx, q, ldq, static_cast<uint8_t*>(scales), colm, st);
+  return launch_status(e);
+}
+
+fp8q_status_t fp8q_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, float eps, int64_t M,
+                                 int64_t K, int64_t ldx, int32_t layout, uint8_t* q, int64_t ldq,
+                                 float* scales, uint16_t* y_out, int64_t ldy, void* stream) {
+  if (M < 0 || K <= 0 || M > kMaxDim || K > kMaxDim) return FP8Q_ERR_SHAPE;
+  if (layout != FP8Q_SCALES_ROW_MAJOR && layout != FP8Q_SCALES_COL_MAJOR) return FP8Q_ERR_UNSUPPORTED;
+  if (!(eps > 0.0f) || !std::isfinite(eps)) return FP8Q_ERR_VALUE;
+  if (M == 0) return FP8Q_OK;
+  FP8Q_TRY(check_matrix(x, K, ldx, 2));
+  FP8Q_TRY(check_matrix(q, K, ldq, 1));
+  if (gamma == nullptr || scales == nullptr) return FP8Q_ERR_NULL;
+  if (!aligned16(gamma)) return FP8Q_ERR_MISALIGNED;
+  if (reinterpret_cast<uintptr_t>(scales) & 3u) return FP8Q_ERR_MISALIGNED;
+  if (y_out != nullptr) FP8Q_TRY(check_matrix(y_out, K, ldy, 2));
+  FP8Q_TRY(check_device());
+  return launch_status(fp8q::launch_rmsnorm_quant(x, gamma, eps, M, K, ldx, q, ldq, scales,
+                                                   layout == FP8Q_SCALES_COL_MAJOR, y_out, ldy,
+                                                   static_cast<hipStream_t>(stream)));
+}
+
+fp8q_status_t fp8q_quant_weight_block(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
+                                      int32_t block_n, int32_t block_k, int32_t fmt, uint8_t* q,
+                                      int64_t ldq, void* scale_inv, void* stream) {
+  if (N < 0 || K <= 0 || N > kMaxDim || K > kMaxDim) return FP8Q_ERR_SHAPE;
+  enum { BLOCK, MX, TENSOR } kind;
+  if (block_n == 128 && block_k == 128 && fmt == FP8Q_SCALE_F32) kind = BLOCK;
+  else if (block_n == 1 && block_k == 32 && fmt == FP8Q_SCALE_UE8M0) kind = MX;
+  else if (block_n == N && block_k == K && fmt == FP8Q_SCALE_F32) kind = TENSOR;
+  else return FP8Q_ERR_UNSUPPORTED;
+  if (N == 0) return FP8Q_OK;
+  FP8Q_TRY(check_matrix(w, K, ldw, 2));
+  FP8Q_TRY(check_matrix(q, K, ldq, 1));
+  if (scale_inv == nullptr) return FP8Q_ERR_NULL;
+  if (kind != MX && (reinterpret_cast<uintptr_t>(scale_inv) & 3u)) return FP8Q_ERR_MISALIGNED;
+  FP8Q_TRY(check_device());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (kind == BLOCK) e = fp8q::launch_weight_block128(w, N, K, ldw, q, ldq, static_cast<float*>(scale_inv), st);
+  else if (kind == MX) e = fp8q::launch_quant_group32mx(w, N, K, ldw, q, ldq, static_cast<uint8_t*>(scale_inv), 0, st);
+  else e = fp8q::launch_weight_tensor(w, N, K, ldw, q, ldq, static_cast<float*>(scale_inv), st);
+  return launch_status(e);
+}
+
+fp8q_status_t fp8q_gemm_blockscale(const uint8_t* a, int64_t lda, const float* a_scales,
+                                   int32_t a_layout, const uint8_t* w, int64_t ldw,
+                                   const float* w_scale_inv, const uint16_t* bias, uint16_t* y,
+                                   int64_t ldy, int64_t M, int64_t N, int64_t K, int32_t gran,
+                                   void* stream) {
+  if (M < 0 || N < 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8Q_ERR_SHAPE;
+  if (gran != FP8Q_GRAN_BLOCK128 && gran != FP8Q_GRAN_PER_TENSOR) return FP8Q_ERR_UNSUPPORTED;
+  if (a_layout != FP8Q_SCALES_ROW_MAJOR && a_layout != FP8Q_SCALES_COL_MAJOR) return FP8Q_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return FP8Q_OK;
+  FP8Q_TRY(check_matrix(a, K, lda, 1));
+  FP8Q_TRY(check_matrix(w, K, ldw, 1));
+  FP8Q_TRY(check_matrix(y, N, ldy, 2));
+  if (a_scales == nullptr || w_scale_inv == nullptr) return FP8Q_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(a_scales) & 3u) || (reinterpret_cast<uintptr_t>(w_scale_inv) & 3u))
+    return FP8Q_ERR_MISALIGNED;
+  if (bias != nullptr && (reinterpret_cast<uintptr_t>(bias) & 1u)) return FP8Q_ERR_MISALIGNED;
+  FP8Q_TRY(check_device());
+  return launch_status(fp8q::launch_gemm_blockscale(a, lda, a_scales, a_layout == FP8Q_SCALES_COL_MAJOR,
+                                                     w, ldw, w_scale_inv, bias, y, ldy, M, N, K,
+                                                     gran == FP8Q_GRAN_PER_TENSOR,
+                                                     static_cast<hipStream_t>(stream)));
+}
+
+fp8q_status_t fp8q_gemm_mxfp8(const uint8_t* a, int64_t lda, const uint8_t* a_scales,
+                              const uint8_t* w, int64_t ldw, const uint8_t* w_scales,
+                              const uint16_t* bias, uint16_t* y, int64_t ldy, int64_t M,
+                              int64_t N, int64_t K, void* stream) {
+  if (M < 0 || N < 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8Q_ERR_SHAPE;
+  if (M == 0 || N == 0) return FP8Q_OK;
+  FP8Q_TRY(check_matrix(a, K, lda, 1));
+  FP8Q_TRY(check_matrix(w, K, ldw, 1));
+  FP8Q_TRY(check_matrix(y, N, ldy, 2));
+  if (a_scales == nullptr || w_scales == nullptr) return FP8Q_ERR_NULL;
+  if (bias != nullptr && (reinterpret_cast<uintptr_t>(bias) & 1u)) return FP8Q_ERR_MISALIGNED;
+  FP8Q_TRY(check_device());
+  return launch_status(fp8q::launch_gemm_mxfp8(a, lda, a_scales, w, ldw, w_scales, bias, y, ldy, M,
+                                                N, K, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

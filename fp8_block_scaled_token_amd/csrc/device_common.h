@@ -1,0 +1,154 @@
+// Device helpers shared by the fp8q kernels (gfx950 only).
+//
+// Arithmetic notes
+// * The library is compiled with -ffp-contract=off: every multiply and add is
+//   rounded as written; fused multiply-adds appear only where __builtin_fmaf
+//   is spelled out.
+// * fp32 denormals are kept (no flush-to-zero) and fp32 division is the
+//   compiler's correctly rounded IEEE division.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8q {
+
+constexpr float kFp8Max = 448.0f;   // largest finite OCP E4M3 value
+constexpr float kAmaxFloor = 1e-10f;
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- bf16 <-> f32
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Unpack 8 bf16 (one 16-byte chunk) into fp32.
+__device__ __forceinline__ void unpack8(const uint4& c, float v[8]) {
+  v[0] = bf16_lo(c.x); v[1] = bf16_hi(c.x);
+  v[2] = bf16_lo(c.y); v[3] = bf16_hi(c.y);
+  v[4] = bf16_lo(c.z); v[5] = bf16_hi(c.z);
+  v[6] = bf16_lo(c.w); v[7] = bf16_hi(c.w);
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs; overflow -> inf).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// ------------------------------------------------------------------ E4M3 encode
+
+// Two fp32 values (already clamped to +-448) -> two E4M3 bytes in the low or
+// high half of `old`, using the hardware conversion (round to nearest even).
+template <bool HI>
+__device__ __forceinline__ uint32_t cvt_pk_e4m3(float a, float b, uint32_t old) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
+}
+
+__device__ __forceinline__ float clamp448(float t) {
+  return __builtin_amdgcn_fmed3f(t, -kFp8Max, kFp8Max);
+}
+
+// Encode 8 clamped fp32 values into 8 E4M3 bytes.
+__device__ __forceinline__ uint2 encode8(const float t[8]) {
+  uint32_t w0 = cvt_pk_e4m3<false>(t[0], t[1], 0u);
+  w0 = cvt_pk_e4m3<true>(t[2], t[3], w0);
+  uint32_t w1 = cvt_pk_e4m3<false>(t[4], t[5], 0u);
+  w1 = cvt_pk_e4m3<true>(t[6], t[7], w1);
+  return make_uint2(w0, w1);
+}
+
+// ------------------------------------------------------------ x / s in fp32
+
+// Correctly rounded fp32 quotient x / s for the quantizer's operand domain,
+// given r = RN(1/s): y = RN(x*r) is refined once with the exact residual
+// x - y*s (an FMA) -- Markstein's correction.  For every bf16 x with |x| <=
+// amax and s = RN(max(amax, 1e-10)/448), amax a bf16 value, this equals IEEE
+// x / s; that domain is finite and is checked exhaustively by a host-side test.
+__device__ __forceinline__ float div_by_scale(float x, float s, float r) {
+  float y = x * r;
+  float e = __builtin_fmaf(-y, s, x);
+  return __builtin_fmaf(e, r, y);
+}
+
+// ------------------------------------------------------- cross-lane max / sum
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Max over each aligned group of 4 lanes (quad), result in every lane.
+__device__ __forceinline__ float max_quad(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
+  return v;
+}
+
+// Max over each aligned row of 16 lanes, result in every lane.
+__device__ __forceinline__ float max_row16(float v) {
+  v = max_quad(v);
+  v = fmaxf(v, dpp_f<0x141>(v));  // row_half_mirror: lanes 0-3 <-> 4-7
+  v = fmaxf(v, dpp_f<0x140>(v));  // row_mirror: lanes 0-7 <-> 8-15
+  return v;
+}
+
+// Max over the whole 64-lane wave (every lane gets the result).
+__device__ __forceinline__ float max_wave(float v) {
+  v = max_row16(v);
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+
+__device__ __forceinline__ double sum_wave_f64(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// ------------------------------------------------------------- memory access
+
+__device__ __forceinline__ uint4 ld16(const void* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+__device__ __forceinline__ void st8(void* p, uint2 v) { *reinterpret_cast<uint2*>(p) = v; }
+
+// Load 8 bf16 starting at column k0 of a row of logical length K; columns >= K
+// read as zero.  Whole chunk via one 16-byte load when it lies inside [0, K);
+// otherwise element by element.
+__device__ __forceinline__ uint4 load8_bf16_masked(const uint16_t* row, int64_t k0, int64_t K) {
+  if (k0 + 8 <= K) return ld16(row + k0);
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  for (int e = 0; e < 8; ++e) {
+    if (k0 + e < K) w[e >> 1] |= (uint32_t)row[k0 + e] << ((e & 1) * 16);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Store 8 bytes at column k0 of a row of logical length K (bytes >= K dropped).
+__device__ __forceinline__ void store8_masked(uint8_t* row, int64_t k0, int64_t K, uint2 v) {
+  if (k0 + 8 <= K) { st8(row + k0, v); return; }
+  for (int e = 0; e < 8; ++e) {
+    if (k0 + e < K) {
+      uint32_t w = e < 4 ? v.x : v.y;
+      row[k0 + e] = (uint8_t)(w >> ((e & 3) * 8));
+    }
+  }
+}
+
+__device__ __forceinline__ void store8_bf16_masked(uint16_t* row, int64_t k0, int64_t K, uint4 v) {
+  if (k0 + 8 <= K) { *reinterpret_cast<uint4*>(row + k0) = v; return; }
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  for (int e = 0; e < 8; ++e)
+    if (k0 + e < K) row[k0 + e] = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
+}
+
+}  // namespace fp8q

@@ -1,0 +1,35 @@
+// Host-side launchers of the fp8q kernels (argument checking lives in api.cpp).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8q {
+
+hipError_t launch_quant_group128(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                 uint8_t* q, int64_t ldq, float* scales, int col_major,
+                                 hipStream_t stream);
+hipError_t launch_quant_group32mx(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                  uint8_t* q, int64_t ldq, uint8_t* scales, int col_major,
+                                  hipStream_t stream);
+hipError_t launch_quant_static(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                               const float* scale, uint8_t* q, int64_t ldq, hipStream_t stream);
+hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, float eps, int64_t M,
+                                int64_t K, int64_t ldx, uint8_t* q, int64_t ldq, float* scales,
+                                int col_major, uint16_t* y_out, int64_t ldy, hipStream_t stream);
+hipError_t launch_weight_block128(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
+                                  uint8_t* q, int64_t ldq, float* scale_inv, hipStream_t stream);
+hipError_t launch_weight_tensor(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q,
+                                int64_t ldq, float* scale_inv, hipStream_t stream);
+
+// Scaled GEMMs: Y[M,N] (bf16) = A[M,K] (E4M3) * W[N,K]^T (E4M3).
+//   gran 0: 128-block fp32 scales; gran 1: per-tensor fp32 scalars.
+hipError_t launch_gemm_blockscale(const uint8_t* a, int64_t lda, const float* sa, int sa_col_major,
+                                  const uint8_t* w, int64_t ldw, const float* sw,
+                                  const uint16_t* bias, uint16_t* y, int64_t ldy, int64_t M,
+                                  int64_t N, int64_t K, int per_tensor, hipStream_t stream);
+hipError_t launch_gemm_mxfp8(const uint8_t* a, int64_t lda, const uint8_t* sa, const uint8_t* w,
+                             int64_t ldw, const uint8_t* sw, const uint16_t* bias, uint16_t* y,
+                             int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+}  // namespace fp8q

@@ -1,0 +1,406 @@
+// Quantizer kernels of the FP8 blockwise linear layer (gfx950).
+//
+//  * quant_group128   dynamic per-token-group activation quantizer, fp32 scale
+//                     per 128 channels ([GLM17] "第 1 站:RMSNorm 的两个出口";
+//                     [SGL19] "Triton 分块内核在做什么").
+//  * quant_group32mx  MXFP8 1x32 blocks with UE8M0 scale bytes ([SGLFP8]
+//                     "4. 블록 양자화 스케일 관리"; round-up exponent of [GLM17]
+//                     "第 4 站:索引器——FP8 与排名稳定性").
+//  * quant_static     per-tensor static scale ([SGL19] "激活量化的三种选择").
+//  * rmsnorm_quant    RMSNorm -> bf16 -> group-128 quantizer in one pass.
+//  * weight_block     128x128 weight blocks and the per-tensor weight scale
+//                     ([SGL19] "建权重:先决定 scale 的形状", "从浮点到 FP8 的基本公式").
+//
+// Page titles: [SGL19] "SGLang 源码完全拆解(十九):量化方法的注册与层分派",
+// [SGLFP8] "[SGLang] FP8", [GLM17] "GLM-5.3 推理全链路(十七):精度账本".
+//
+// Work layout of the row quantizers: one 64-lane wave owns a segment of
+// 512*CH consecutive elements of one row.  Load c of lane l covers the 8
+// elements [seg0 + 512c + 8l, +8): every load instruction of the wave reads one
+// contiguous kilobyte, and the 16 lanes of a DPP row hold exactly one
+// 128-element group (4 lanes hold one 32-element MX block), so group maxima
+// are DPP reductions with no LDS traffic.  Quantization is HBM-bound: the
+// kernels keep all CH loads of a lane in flight before using any of them.
+#include "device_common.h"
+#include "launch.h"
+
+namespace fp8q {
+
+// --------------------------------------------------------------------------
+// Group-128 dynamic quantizer (fp32 scales)
+
+__device__ __forceinline__ void quant_chunk_g128(const uint4& raw, float amax_row16,
+                                                 uint2& out, float& s_out) {
+  float v[8];
+  unpack8(raw, v);
+  const float s = fmaxf(amax_row16, kAmaxFloor) / kFp8Max;   // IEEE division
+  const float r = 1.0f / s;                                   // IEEE division
+  float t[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) t[e] = clamp448(div_by_scale(v[e], s, r));
+  out = encode8(t);
+  s_out = s;
+}
+
+__device__ __forceinline__ float absmax8(const uint4& raw) {
+  float v[8];
+  unpack8(raw, v);
+  float m = fabsf(v[0]);
+#pragma unroll
+  for (int e = 1; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
+  return m;
+}
+
+template <int CH>
+__global__ __launch_bounds__(256) void quant_group128_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
+    uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ scales, int col_major,
+    int64_t segs_per_row) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;
+  const int64_t row = wave / segs_per_row;
+  if (row >= M) return;
+  const int64_t seg0 = (wave - row * segs_per_row) * (512 * CH);
+  const uint16_t* xr = x + row * ldx;
+  uint8_t* qr = q + row * ldq;
+  const int64_t G = (K + 127) >> 7;
+
+  uint4 raw[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int64_t k0 = seg0 + 512 * c + 8 * lane;
+    raw[c] = (k0 < K) ? load8_bf16_masked(xr, k0, K) : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int64_t k0 = seg0 + 512 * c + 8 * lane;
+    const float amax = max_row16(absmax8(raw[c]));
+    uint2 o;
+    float s;
+    quant_chunk_g128(raw[c], amax, o, s);
+    if (k0 < K) store8_masked(qr, k0, K, o);
+    const int64_t g = (seg0 + 512 * c) / 128 + (lane >> 4);
+    if ((lane & 15) == 0 && g < G) {
+      if (col_major) scales[g * M + row] = s;
+      else scales[row * G + g] = s;
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// MXFP8 1x32 quantizer (UE8M0 scale bytes)
+
+// Scale byte e + 127 for a block max a (>= 1e-10, a normal fp32 number
+// m * 2^E, 1 <= m < 2): 448 = 1.75 * 2^8, so the smallest e with a <= 448*2^e
+// is E - 8 when m <= 1.75 and E - 7 otherwise.
+__device__ __forceinline__ uint32_t ue8m0_byte(float amax) {
+  const uint32_t b = __float_as_uint(fmaxf(amax, kAmaxFloor));
+  const uint32_t biased = b >> 23;            // E + 127 (a > 0, normal)
+  const uint32_t man = b & 0x7FFFFFu;
+  return biased - 8u + (man > 0x600000u ? 1u : 0u);
+}
+
+template <int CH>
+__global__ __launch_bounds__(256) void quant_group32mx_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
+    uint8_t* __restrict__ q, int64_t ldq, uint8_t* __restrict__ scales, int col_major,
+    int64_t segs_per_row) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;
+  const int64_t row = wave / segs_per_row;
+  if (row >= M) return;
+  const int64_t seg0 = (wave - row * segs_per_row) * (512 * CH);
+  const uint16_t* xr = x + row * ldx;
+  uint8_t* qr = q + row * ldq;
+  const int64_t G = (K + 31) >> 5;
+
+  uint4 raw[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int64_t k0 = seg0 + 512 * c + 8 * lane;
+    raw[c] = (k0 < K) ? load8_bf16_masked(xr, k0, K) : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int64_t k0 = seg0 + 512 * c + 8 * lane;
+    const float amax = max_quad(absmax8(raw[c]));
+    const uint32_t byte = ue8m0_byte(amax);
+    // 2^-e = 2^(127 - byte) as an fp32 bit pattern (byte <= 253 for bf16 input)
+    const float inv = __uint_as_float((254u - byte) << 23);
+    float v[8], t[8];
+    unpack8(raw[c], v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[e] = clamp448(v[e] * inv);   // exact scaling
+    const uint2 o = encode8(t);
+    if (k0 < K) store8_masked(qr, k0, K, o);
+    const int64_t g = (seg0 + 512 * c) / 32 + (lane >> 2);
+    if ((lane & 3) == 0 && g < G) {
+      if (col_major) scales[g * M + row] = (uint8_t)byte;
+      else scales[row * G + g] = (uint8_t)byte;
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// Static per-tensor quantizer
+
+template <int CH>
+__global__ __launch_bounds__(256) void quant_static_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
+    const float* __restrict__ scale, uint8_t* __restrict__ q, int64_t ldq,
+    int64_t segs_per_row) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;
+  const int64_t row = wave / segs_per_row;
+  if (row >= M) return;
+  const int64_t seg0 = (wave - row * segs_per_row) * (512 * CH);
+  const uint16_t* xr = x + row * ldx;
+  uint8_t* qr = q + row * ldq;
+  const float s = *scale;
+  uint4 raw[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int64_t k0 = seg0 + 512 * c + 8 * lane;
+    raw[c] = (k0 < K) ? load8_bf16_masked(xr, k0, K) : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int64_t k0 = seg0 + 512 * c + 8 * lane;
+    float v[8], t[8];
+    unpack8(raw[c], v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[e] = clamp448(v[e] / s);   // IEEE division
+    if (k0 < K) store8_masked(qr, k0, K, encode8(t));
+  }
+}
+
+// --------------------------------------------------------------------------
+// RMSNorm fused with the group-128 quantizer: one wave per row.
+
+template <int CH, bool ONE_PASS>
+__global__ __launch_bounds__(256) void rmsnorm_quant_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma, float eps,
+    int64_t M, int64_t K, int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
+    float* __restrict__ scales, int col_major, uint16_t* __restrict__ y_out, int64_t ldy) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;
+  if (row >= M) return;
+  const uint16_t* xr = x + row * ldx;
+  uint8_t* qr = q + row * ldq;
+  const int64_t G = (K + 127) >> 7;
+  constexpr int64_t SEG = 512 * CH;
+  const int64_t nseg = ONE_PASS ? 1 : (K + SEG - 1) / SEG;
+
+  // pass 1: sum of squares in fp64 (bf16 squares are exact in fp64)
+  uint4 raw[CH];
+  double ss = 0.0;
+  for (int64_t sg = 0; sg < nseg; ++sg) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int64_t k0 = sg * SEG + 512 * c + 8 * lane;
+      raw[c] = (k0 < K) ? load8_bf16_masked(xr, k0, K) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      float v[8];
+      unpack8(raw[c], v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const double d = (double)v[e];
+        ss = __builtin_fma(d, d, ss);
+      }
+    }
+  }
+  ss = sum_wave_f64(ss);
+  const float r = (float)(1.0 / sqrt(ss / (double)K + (double)eps));
+
+  // pass 2: normalize, round to bf16, quantize per 128-group
+  for (int64_t sg = 0; sg < nseg; ++sg) {
+    if (!ONE_PASS) {
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const int64_t k0 = sg * SEG + 512 * c + 8 * lane;
+        raw[c] = (k0 < K) ? load8_bf16_masked(xr, k0, K) : make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int64_t k0 = sg * SEG + 512 * c + 8 * lane;
+      const uint4 gr = (k0 < K) ? load8_bf16_masked(gamma, k0, K) : make_uint4(0, 0, 0, 0);
+      float v[8], g[8];
+      unpack8(raw[c], v);
+      unpack8(gr, g);
+      uint32_t yb[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const float y0 = (v[e] * r) * g[e];
+        const float y1 = (v[e + 1] * r) * g[e + 1];
+        yb[e >> 1] = pack_bf16x2(y0, y1);
+      }
+      const uint4 ybits = make_uint4(yb[0], yb[1], yb[2], yb[3]);
+      if (y_out != nullptr && k0 < K) store8_bf16_masked(y_out + row * ldy, k0, K, ybits);
+      const float amax = max_row16(absmax8(ybits));
+      uint2 o;
+      float s;
+      quant_chunk_g128(ybits, amax, o, s);
+      if (k0 < K) store8_masked(qr, k0, K, o);
+      const int64_t gi = (sg * SEG + 512 * c) / 128 + (lane >> 4);
+      if ((lane & 15) == 0 && gi < G) {
+        if (col_major) scales[gi * M + row] = s;
+        else scales[row * G + gi] = s;
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// Weight blocks.  One 256-thread workgroup per 128x128 block: thread t holds
+// the 8-column chunk (t % 16) of rows t/16 + 16i, i = 0..7 (each 16-lane row
+// of a wave reads one 256-byte block row contiguously).
+//   MODE 0: block scale = block amax / 448; quantize; write scale.
+//   MODE 1: per-tensor pass 1 -- fold the block amax into *slot (integer max
+//           of the non-negative fp32 bit patterns: order independent).
+//   MODE 2: per-tensor pass 2 -- quantize with s from the tensor amax in *slot.
+
+template <int MODE>
+__global__ __launch_bounds__(256) void weight_block_kernel(
+    const uint16_t* __restrict__ w, int64_t N, int64_t K, int64_t ldw,
+    uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ scale_out,
+    uint32_t* __restrict__ slot, int64_t KB) {
+  __shared__ float red[4];
+  const int t = threadIdx.x;
+  const int64_t bn = blockIdx.y, bk = blockIdx.x;
+  const int64_t k0 = bk * 128 + 8 * (t & 15);
+  uint4 raw[8];
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t n = bn * 128 + (t >> 4) + 16 * i;
+    raw[i] = (n < N && k0 < K) ? load8_bf16_masked(w + n * ldw, k0, K) : make_uint4(0, 0, 0, 0);
+    if (MODE != 2) m = fmaxf(m, absmax8(raw[i]));
+  }
+  float amax;
+  if (MODE != 2) {
+    m = max_wave(m);
+    if ((t & 63) == 0) red[t >> 6] = m;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    if (MODE == 1) {
+      if (t == 0) atomicMax(slot, __float_as_uint(amax));
+      return;
+    }
+  } else {
+    amax = __uint_as_float(*slot);
+  }
+  const float s = fmaxf(amax, kAmaxFloor) / kFp8Max;
+  const float r = 1.0f / s;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t n = bn * 128 + (t >> 4) + 16 * i;
+    if (n < N && k0 < K) {
+      float v[8], tt[8];
+      unpack8(raw[i], v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) tt[e] = clamp448(div_by_scale(v[e], s, r));
+      store8_masked(q + n * ldq, k0, K, encode8(tt));
+    }
+  }
+  if (MODE == 0 && t == 0) scale_out[bn * KB + bk] = s;
+}
+
+__global__ void zero_slot_kernel(uint32_t* slot) { *slot = 0u; }
+
+// amax bits in slot -> fp32 scale, in place (after MODE 2 has read it).
+__global__ void finalize_tensor_scale_kernel(uint32_t* slot) {
+  const float amax = __uint_as_float(*slot);
+  *reinterpret_cast<float*>(slot) = fmaxf(amax, kAmaxFloor) / kFp8Max;
+}
+
+// --------------------------------------------------------------------------
+// Host launchers
+
+static inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Row quantizers: segments of 512*CH elements per wave; CH is chosen so that
+// short rows do not leave most lanes idle.
+hipError_t launch_quant_group128(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                 uint8_t* q, int64_t ldq, float* scales, int col_major,
+                                 hipStream_t stream) {
+  const int ch = K <= 512 ? 1 : (K <= 1024 ? 2 : 4);
+  const int64_t segs = ceil_div(K, 512 * ch);
+  const int64_t waves = M * segs;
+  const dim3 grid((unsigned)ceil_div(waves, 4)), block(256);
+  if (ch == 1)
+    hipLaunchKernelGGL(quant_group128_kernel<1>, grid, block, 0, stream, x, M, K, ldx, q, ldq, scales, col_major, segs);
+  else if (ch == 2)
+    hipLaunchKernelGGL(quant_group128_kernel<2>, grid, block, 0, stream, x, M, K, ldx, q, ldq, scales, col_major, segs);
+  else
+    hipLaunchKernelGGL(quant_group128_kernel<4>, grid, block, 0, stream, x, M, K, ldx, q, ldq, scales, col_major, segs);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_group32mx(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                  uint8_t* q, int64_t ldq, uint8_t* scales, int col_major,
+                                  hipStream_t stream) {
+  const int ch = K <= 512 ? 1 : (K <= 1024 ? 2 : 4);
+  const int64_t segs = ceil_div(K, 512 * ch);
+  const int64_t waves = M * segs;
+  const dim3 grid((unsigned)ceil_div(waves, 4)), block(256);
+  if (ch == 1)
+    hipLaunchKernelGGL(quant_group32mx_kernel<1>, grid, block, 0, stream, x, M, K, ldx, q, ldq, scales, col_major, segs);
+  else if (ch == 2)
+    hipLaunchKernelGGL(quant_group32mx_kernel<2>, grid, block, 0, stream, x, M, K, ldx, q, ldq, scales, col_major, segs);
+  else
+    hipLaunchKernelGGL(quant_group32mx_kernel<4>, grid, block, 0, stream, x, M, K, ldx, q, ldq, scales, col_major, segs);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_static(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                               const float* scale, uint8_t* q, int64_t ldq, hipStream_t stream) {
+  const int64_t segs = ceil_div(K, 512 * 4);
+  const dim3 grid((unsigned)ceil_div(M * segs, 4)), block(256);
+  hipLaunchKernelGGL(quant_static_kernel<4>, grid, block, 0, stream, x, M, K, ldx, scale, q, ldq, segs);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, float eps, int64_t M,
+                                int64_t K, int64_t ldx, uint8_t* q, int64_t ldq, float* scales,
+                                int col_major, uint16_t* y_out, int64_t ldy, hipStream_t stream) {
+  const dim3 grid((unsigned)ceil_div(M, 4)), block(256);
+#define FP8Q_RMS(CH, ONE) \
+  hipLaunchKernelGGL((rmsnorm_quant_kernel<CH, ONE>), grid, block, 0, stream, x, gamma, eps, M, K, ldx, q, ldq, scales, col_major, y_out, ldy)
+  if (K <= 512) FP8Q_RMS(1, true);
+  else if (K <= 1024) FP8Q_RMS(2, true);
+  else if (K <= 2048) FP8Q_RMS(4, true);
+  else if (K <= 4096) FP8Q_RMS(8, true);
+  else if (K <= 6144) FP8Q_RMS(12, true);
+  else if (K <= 8192) FP8Q_RMS(16, true);
+  else FP8Q_RMS(8, false);
+#undef FP8Q_RMS
+  return hipGetLastError();
+}
+
+hipError_t launch_weight_block128(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
+                                  uint8_t* q, int64_t ldq, float* scale_inv, hipStream_t stream) {
+  const int64_t KB = ceil_div(K, 128);
+  const dim3 grid((unsigned)KB, (unsigned)ceil_div(N, 128)), block(256);
+  hipLaunchKernelGGL(weight_block_kernel<0>, grid, block, 0, stream, w, N, K, ldw, q, ldq, scale_inv,
+                     (uint32_t*)nullptr, KB);
+  return hipGetLastError();
+}
+
+hipError_t launch_weight_tensor(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q,
+                                int64_t ldq, float* scale_inv, hipStream_t stream) {
+  const int64_t KB = ceil_div(K, 128);
+  const dim3 grid((unsigned)KB, (unsigned)ceil_div(N, 128)), block(256);
+  uint32_t* slot = reinterpret_cast<uint32_t*>(scale_inv);
+  hipLaunchKernelGGL(zero_slot_kernel, dim3(1), dim3(1), 0, stream, slot);
+  hipLaunchKernelGGL(weight_block_kernel<1>, grid, block, 0, stream, w, N, K, ldw, q, ldq,
+                     (float*)nullptr, slot, KB);
+  hipLaunchKernelGGL(weight_block_kernel<2>, grid, block, 0, stream, w, N, K, ldw, q, ldq,
+                     (float*)nullptr, slot, KB);
+  hipLaunchKernelGGL(finalize_tensor_scale_kernel, dim3(1), dim3(1), 0, stream, slot);
+  return hipGetLastError();
+}
+
+}  // namespace fp8q

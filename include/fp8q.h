@@ -1,0 +1,192 @@
+/*
+ * fp8q -- FP8 blockwise linear layer for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of the hot path: a dynamic per-token-group activation quantizer
+ * (optionally fused after RMSNorm), a 128x128 weight-block quantizer, and
+ * W8A8 GEMMs with per-K-block fp32 rescaling (plus per-tensor and MXFP8
+ * variants).  Plain pointers and sizes only; every compute step runs in
+ * hand-written HIP kernels on the caller's stream.
+ *
+ * Sources (page title, section):
+ *   [SGL19]  "SGLang 源码完全拆解(十九):量化方法的注册与层分派"
+ *   [SGLFP8] "[SGLang] FP8"
+ *   [GLM17]  "GLM-5.3 推理全链路(十七):精度账本"
+ *   [MKBK]   "量化" (HF quantization configs)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Types.  bf16 and E4M3 values travel as their bit patterns (uint16_t and
+ *   uint8_t).  E4M3 is the OCP "fn" variant: max 448, no infinities.
+ *   UE8M0 scale bytes encode 2^(byte-127).
+ * Layout.  Matrices are row-major with a leading dimension (row stride, in
+ *   elements) `ld` >= the logical row length.  Every row buffer must be
+ *   readable for its full `ld` elements (kernels read whole 16-byte chunks
+ *   inside a row, but never write outside the logical [rows, K] region).
+ * Alignment.  Matrix base pointers are 16-byte aligned; bf16 strides are
+ *   multiples of 8 elements and E4M3 strides multiples of 16, so that every
+ *   row starts on a 16-byte boundary.  Scale arrays are naturally aligned.
+ * Memory.  Pointers are device pointers (except where stated).  The caller
+ *   allocates every input and output; the library never allocates, frees,
+ *   synchronizes or keeps pointers.  Work is enqueued asynchronously on
+ *   `stream` (a hipStream_t; NULL = the null stream); buffers must stay alive
+ *   until the stream has passed it.
+ * Errors.  Arguments are checked before anything is launched ("fail at
+ *   setup, not in the kernel", as the pages' config checks do: [SGL19]
+ *   "配置对象还要过三道硬件检查"); on any error nothing is enqueued.  A launch
+ *   failure reported by HIP returns FP8Q_ERR_LAUNCH.  The library prints
+ *   nothing and never aborts.  M == 0 or N == 0 is a successful no-op.
+ * Values.  Inputs must be finite; NaN/Inf inputs give unspecified (but
+ *   memory-safe) outputs.
+ * Determinism.  No atomics on floating-point data and fixed reduction
+ *   orders: repeated calls give identical bits.  Calls are re-entrant across
+ *   streams (no mutable global state except a per-device architecture cache).
+ */
+#ifndef FP8Q_H
+#define FP8Q_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8Q_ABI_VERSION 1
+
+typedef enum {
+  FP8Q_OK = 0,
+  FP8Q_ERR_NULL = 1,         /* a required pointer is NULL                      */
+  FP8Q_ERR_SHAPE = 2,        /* negative extent, K <= 0, or ld < row length     */
+  FP8Q_ERR_UNSUPPORTED = 3,  /* group/block/format/layout combination not offered */
+  FP8Q_ERR_MISALIGNED = 4,   /* pointer or stride breaks the alignment rule     */
+  FP8Q_ERR_DEVICE = 5,       /* current device is not gfx950, or HIP query failed */
+  FP8Q_ERR_LAUNCH = 6,       /* HIP reported an error when launching            */
+  FP8Q_ERR_VALUE = 7         /* invalid scalar argument (e.g. eps <= 0)         */
+} fp8q_status_t;
+
+typedef enum { FP8Q_SCALE_F32 = 0, FP8Q_SCALE_UE8M0 = 1 } fp8q_scale_fmt_t;
+typedef enum { FP8Q_SCALES_ROW_MAJOR = 0, FP8Q_SCALES_COL_MAJOR = 1 } fp8q_scale_layout_t;
+typedef enum { FP8Q_GRAN_BLOCK128 = 0, FP8Q_GRAN_PER_TENSOR = 1 } fp8q_gran_t;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* fp8q_status_string(fp8q_status_t s);
+
+/* FP8Q_ABI_VERSION of the loaded library. */
+int fp8q_abi_version(void);
+
+/*
+ * fp8q_quant_act_group -- dynamic per-token-group activation quantization.
+ *
+ * [GLM17] "第 1 站:RMSNorm 的两个出口" and [SGL19] "Triton 分块内核在做什么":
+ * each run of `group_size` consecutive channels of a row gets its own scale
+ * and is encoded to E4M3 with saturation ([SGL19] "从浮点到 FP8 的基本公式":
+ * q = clamp(round(x/s), -448, 448), round-to-nearest-even).
+ *
+ *   x       bf16 [M, ldx]    input rows (logical length K).
+ *   q       E4M3 [M, ldq]    output codes (only columns < K are written).
+ *   scales  output, one per (row, group); G = ceil(K / group_size):
+ *     group_size 128, fmt FP8Q_SCALE_F32: float, s = fp32(max(amax,1e-10)/448);
+ *       q = E4M3(clamp(fp32(x / s))).
+ *     group_size 32, fmt FP8Q_SCALE_UE8M0 (MXFP8, [SGLFP8] "4. 블록 양자화
+ *       스케일 관리"): uint8 byte = e + 127 with e the smallest integer such
+ *       that max(amax, 1e-10) <= 448 * 2^e (the round-up rule of [GLM17]
+ *       "第 4 站:索引器"); q = E4M3(x * 2^-e).
+ *   layout  FP8Q_SCALES_ROW_MAJOR: scales[row * G + g];
+ *           FP8Q_SCALES_COL_MAJOR: scales[g * M + row] (the [groups, rows]
+ *           layout of [GLM17] "第 7 站:MoE").
+ *   static_scale  if non-NULL: per-tensor static quantization with the given
+ *           device fp32 scalar s ([SGL19] "激活量化的三种选择": a fixed
+ *           input_scale); q = E4M3(clamp(fp32(x / s))); group_size, fmt and
+ *           layout are ignored and `scales` may be NULL.  s must be > 0.
+ * Errors: group_size/fmt pairs other than (128, F32) and (32, UE8M0) ->
+ *   FP8Q_ERR_UNSUPPORTED.
+ */
+fp8q_status_t fp8q_quant_act_group(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                   int32_t group_size, int32_t fmt, int32_t layout,
+                                   const float* static_scale,
+                                   uint8_t* q, int64_t ldq, void* scales, void* stream);
+
+/*
+ * fp8q_rmsnorm_quant -- RMSNorm fused with group-128 dynamic quantization.
+ *
+ * [GLM17] "第 1 站:RMSNorm 的两个出口": y = x / sqrt(mean(x^2) + eps) * g with
+ * bf16 input/output and high-precision statistics, followed by the per-token
+ * group quantizer.  Computed per row as
+ *   r = fp32(1 / sqrt(sum_k x_k^2 / K + eps))   (sum and root in fp64),
+ *   y_k = bf16(fp32(fp32(x_k * r) * g_k)),
+ *   (q, scales) = fp8q_quant_act_group(y, group 128, F32)  -- same bits as the
+ *   unfused sequence.
+ *
+ *   x      bf16 [M, ldx];  gamma bf16 [K];  eps > 0 (finite).
+ *   q      E4M3 [M, ldq];  scales float, layout as in fp8q_quant_act_group.
+ *   y_out  optional bf16 [M, ldy] copy of the normalized rows (NULL = skip).
+ */
+fp8q_status_t fp8q_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, float eps,
+                                 int64_t M, int64_t K, int64_t ldx, int32_t layout,
+                                 uint8_t* q, int64_t ldq, float* scales,
+                                 uint16_t* y_out, int64_t ldy, void* stream);
+
+/*
+ * fp8q_quant_weight_block -- offline weight quantization.
+ *
+ * [SGL19] "建权重:先决定 scale 的形状": a [N, K] weight (row = output channel)
+ * gets one scale per block_n x block_k sub-matrix on a ceil(N/block_n) x
+ * ceil(K/block_k) grid; partial edge blocks are masked, not padded.  The
+ * scale is the dequantization multiplier (weight_scale_inv), s = max|W|/448
+ * over the block ([SGL19] "从浮点到 FP8 的基本公式").
+ *
+ *   (block_n, block_k, fmt):
+ *     (128, 128, FP8Q_SCALE_F32)  -> float scale_inv [ceil(N/128), ceil(K/128)]
+ *     (1, 32, FP8Q_SCALE_UE8M0)   -> uint8 scale_inv [N, ceil(K/32)] (MXFP8;
+ *                                    any other MX block is rejected, the strict
+ *                                    reading of [SGLFP8] "1. Fp8Config 초기화")
+ *     (N, K, FP8Q_SCALE_F32)      -> per-tensor: one float at scale_inv[0]
+ *                                    (scale_inv is also used as scratch).
+ *   w bf16 [N, ldw];  q E4M3 [N, ldq].
+ */
+fp8q_status_t fp8q_quant_weight_block(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
+                                      int32_t block_n, int32_t block_k, int32_t fmt,
+                                      uint8_t* q, int64_t ldq, void* scale_inv, void* stream);
+
+/*
+ * fp8q_gemm_blockscale -- Y = A * W^T with FP8 operands and fp32 scales.
+ *
+ * gran FP8Q_GRAN_BLOCK128 ([SGL19] "一条 GEMM 的三种缩放组合",
+ * "Triton 分块内核在做什么"):
+ *   Y[i,j] = bf16( sum_b P_b[i,j] * s_a[i,b] * s_w[j/128, b] + bias[j] ),
+ *   P_b = sum over K block b (128 wide) of A[i,k]*W[j,k] (fp32 accumulate).
+ *   a_scales float [M, ceil(K/128)] (a_layout ROW_MAJOR) or
+ *            [ceil(K/128), M] (COL_MAJOR);
+ *   w_scale_inv float [ceil(N/128), ceil(K/128)].
+ * gran FP8Q_GRAN_PER_TENSOR: Y = bf16(s_a * s_w * sum_k A[i,k]*W[j,k] + bias[j])
+ *   with a_scales and w_scale_inv each pointing at one float.
+ *
+ *   a    E4M3 [M, lda];  w E4M3 [N, ldw] (row = output channel);
+ *   bias optional bf16 [N] (NULL = none);  y bf16 [M, ldy].
+ */
+fp8q_status_t fp8q_gemm_blockscale(const uint8_t* a, int64_t lda, const float* a_scales,
+                                   int32_t a_layout, const uint8_t* w, int64_t ldw,
+                                   const float* w_scale_inv, const uint16_t* bias,
+                                   uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                                   int32_t gran, void* stream);
+
+/*
+ * fp8q_gemm_mxfp8 -- MXFP8 GEMM: 1x32 blocks on both operands.
+ *
+ * [SGLFP8] "4. 블록 양자화 스케일 관리" (uint8 UE8M0 scales) and [SGL19]
+ * "Triton 分块内核在做什么" (the scale multiply becomes an exponent add):
+ *   Y[i,j] = bf16( sum_b P_b[i,j] * 2^(ea[i,b]-127) * 2^(ew[j,b]-127) + bias[j] ),
+ *   b over 32-wide K blocks.
+ *   a E4M3 [M, lda], a_scales uint8 [M, ceil(K/32)] row-major;
+ *   w E4M3 [N, ldw], w_scales uint8 [N, ceil(K/32)] row-major;
+ *   bias optional bf16 [N];  y bf16 [M, ldy].
+ */
+fp8q_status_t fp8q_gemm_mxfp8(const uint8_t* a, int64_t lda, const uint8_t* a_scales,
+                              const uint8_t* w, int64_t ldw, const uint8_t* w_scales,
+                              const uint16_t* bias, uint16_t* y, int64_t ldy,
+                              int64_t M, int64_t N, int64_t K, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8Q_H */

@@ -1,0 +1,130 @@
+"""C-ABI checks that need no GPU: exports, binding signatures, argument
+validation (every case here returns before any device access), and the
+exhaustive host-side proof of the quantizer's division sequence."""
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8q.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+(fp8q_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import fp8_block_scaled_token_amd as fq
+    if not os.path.exists(fq.LIB_PATH):
+        pytest.fail("libfp8q.so is not built (run __graft_entry__.build())")
+    return fq.load_library()
+
+
+def test_header_declares_the_five_entry_points():
+    names = _declared_functions()
+    for n in ("fp8q_quant_act_group", "fp8q_rmsnorm_quant", "fp8q_quant_weight_block",
+              "fp8q_gemm_blockscale", "fp8q_gemm_mxfp8", "fp8q_status_string", "fp8q_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    import fp8_block_scaled_token_amd as fq
+    out = subprocess.run(["nm", "-D", "--defined-only", fq.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\sT\s+(fp8q_\w+)", out))
+    for n in _declared_functions():
+        assert n in exported, n
+        assert getattr(lib, n) is not None
+
+
+def test_binding_covers_every_declared_symbol():
+    import fp8_block_scaled_token_amd as fq
+    assert sorted(fq.SIGNATURES) == _declared_functions()
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.fp8q_abi_version() == 1
+    for s in range(8):
+        assert len(lib.fp8q_status_string(s)) > 0
+    assert lib.fp8q_status_string(99) == b"unknown status"
+
+
+# fake but aligned addresses: validation must reject the call before any use
+A = ctypes.c_void_p(0x100000)
+B = ctypes.c_void_p(0x200000)
+C = ctypes.c_void_p(0x300000)
+ODD = ctypes.c_void_p(0x100008)
+
+
+def test_quant_act_group_validation(lib):
+    f = lib.fp8q_quant_act_group
+    assert f(A, -1, 128, 128, 128, 0, 0, None, B, 128, C, None) == 2      # M < 0
+    assert f(A, 4, 0, 128, 128, 0, 0, None, B, 128, C, None) == 2         # K == 0
+    assert f(A, 4, 128, 128, 64, 0, 0, None, B, 128, C, None) == 3       # group 64
+    assert f(A, 4, 128, 128, 128, 1, 0, None, B, 128, C, None) == 3      # UE8M0 with 128
+    assert f(A, 4, 128, 128, 32, 0, 0, None, B, 128, C, None) == 3       # f32 with 32
+    assert f(A, 4, 128, 128, 128, 0, 7, None, B, 128, C, None) == 3      # bad layout
+    assert f(A, 0, 128, 128, 128, 0, 0, None, None, 128, None, None) == 0  # M == 0: no-op
+    assert f(None, 4, 128, 128, 128, 0, 0, None, B, 128, C, None) == 1   # null x
+    assert f(A, 4, 128, 120, 128, 0, 0, None, B, 128, C, None) == 2      # ldx < K
+    assert f(A, 4, 128, 132, 128, 0, 0, None, B, 128, C, None) == 4      # bf16 row not 16-B
+    assert f(ODD, 4, 128, 128, 128, 0, 0, None, B, 128, C, None) == 4    # base not 16-B
+    assert f(A, 4, 128, 128, 128, 0, 0, None, B, 136, C, None) == 4      # fp8 ld % 16
+    assert f(A, 4, 128, 128, 128, 0, 0, None, B, 128, None, None) == 1   # null scales
+
+
+def test_rmsnorm_quant_validation(lib):
+    f = lib.fp8q_rmsnorm_quant
+    assert f(A, B, 1e-6, -1, 128, 128, 0, B, 128, C, None, 0, None) == 2
+    assert f(A, B, 0.0, 4, 128, 128, 0, B, 128, C, None, 0, None) == 7     # eps <= 0
+    assert f(A, B, float("nan"), 4, 128, 128, 0, B, 128, C, None, 0, None) == 7
+    assert f(A, B, 1e-6, 4, 128, 128, 5, B, 128, C, None, 0, None) == 3    # layout
+    assert f(A, None, 1e-6, 4, 128, 128, 0, B, 128, C, None, 0, None) == 1  # null gamma
+    assert f(A, B, 1e-6, 4, 128, 128, 0, B, 128, C, A, 100, None) == 2     # ldy < K
+
+
+def test_quant_weight_block_validation(lib):
+    f = lib.fp8q_quant_weight_block
+    assert f(A, 256, 256, 256, 64, 64, 0, B, 256, C, None) == 3          # 64x64 blocks
+    assert f(A, 256, 256, 256, 1, 32, 0, B, 256, C, None) == 3           # MX block, f32
+    assert f(A, 256, 256, 256, 32, 32, 1, B, 256, C, None) == 3          # MX must be 1x32
+    assert f(A, 256, 256, 256, 128, 128, 0, B, 256, None, None) == 1
+    assert f(A, -2, 256, 256, 128, 128, 0, B, 256, C, None) == 2
+
+
+def test_gemm_validation(lib):
+    g = lib.fp8q_gemm_blockscale
+    assert g(A, 128, C, 0, B, 128, C, None, C, 256, 4, 256, 0, 0, None) == 2     # K == 0
+    assert g(A, 128, C, 0, B, 128, C, None, C, 256, 4, 256, 128, 9, None) == 3   # gran
+    assert g(A, 128, C, 0, B, 128, C, None, C, 256, 0, 256, 128, 0, None) == 0   # M == 0
+    assert g(A, 120, C, 0, B, 128, C, None, C, 256, 4, 256, 128, 0, None) == 2   # lda < K
+    assert g(A, 128, None, 0, B, 128, C, None, C, 256, 4, 256, 128, 0, None) == 1
+    assert g(A, 128, C, 0, B, 128, C, None, C, 252, 4, 256, 128, 0, None) == 2   # ldy < N
+    assert g(A, 128, C, 0, B, 128, C, None, C, 260, 4, 260, 128, 0, None) == 4   # ldy % 8
+    m = lib.fp8q_gemm_mxfp8
+    assert m(A, 128, C, B, 128, C, None, C, 256, -1, 256, 128, None) == 2
+    assert m(A, 128, None, B, 128, C, None, C, 256, 4, 256, 128, None) == 1
+
+
+def test_device_check_without_gpu(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: valid-looking fake pointers must never reach a launch")
+    f = lib.fp8q_quant_act_group
+    assert f(A, 4, 128, 128, 128, 0, 0, None, B, 128, C, None) == 5
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
+def test_quantizer_division_sequence_exhaustive(tmp_path):
+    src = os.path.join(ROOT, "tests", "host", "div_by_scale_exhaustive.c")
+    exe = str(tmp_path / "divchk")
+    subprocess.run(["gcc", "-O2", "-mfma", "-ffp-contract=off", "-fopenmp", "-o", exe, src, "-lm"], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=600)
+    print(r.stdout)
+    assert r.returncode == 0, r.stdout
+    assert "fatal=0" in r.stdout
