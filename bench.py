@@ -254,15 +254,15 @@ def cpu_baseline(name, wl, d, target_s):
             qa, sa = oq.quant_group(xs)
             og.gemm_blockscale(qa, sa, qw, sw)
 
+    # grow the row sample until one run takes about target_s (or covers M)
     rows = min(M, 4)
-    t0 = time.perf_counter()
-    run(rows)
-    t = time.perf_counter() - t0
-    if t < target_s and rows < M:
-        rows = int(min(M, max(rows, rows * target_s / max(t, 1e-3))))
+    while True:
         t0 = time.perf_counter()
         run(rows)
         t = time.perf_counter() - t0
+        if t >= 0.5 * target_s or rows >= M:
+            break
+        rows = int(min(M, max(2 * rows, rows * 0.8 * target_s / max(t, 1e-3))))
     tflops = 2.0 * rows * N * K / t / 1e12
     return {"value": tflops, "unit": "TFLOP/s", "cores": blas_threads or len(os.sched_getaffinity(0)),
             "kind": "oracle",

@@ -67,15 +67,19 @@ __device__ __forceinline__ uint2 encode8(const float t[8]) {
 
 // ------------------------------------------------------------ x / s in fp32
 
-// Correctly rounded fp32 quotient x / s for the quantizer's operand domain,
-// given r = RN(1/s): y = RN(x*r) is refined once with the exact residual
-// x - y*s (an FMA) -- Markstein's correction.  For every bf16 x with |x| <=
-// amax and s = RN(max(amax, 1e-10)/448), amax a bf16 value, this equals IEEE
-// x / s; that domain is finite and is checked exhaustively by a host-side test.
+// fp32 quotient x / s for the quantizer's operand domain, given r = RN(1/s):
+// y = RN(|x|*r) is refined once with the exact residual |x| - y*s (an FMA) --
+// Markstein's correction -- and the sign of x is put back last (the FMA
+// sequence alone would turn -0 into +0).  For every bf16 x with |x| <= amax
+// and s = RN(max(amax, 1e-10)/448), amax a bf16 value, the result equals the
+// IEEE quotient x / s wherever either is at least 2^-10, and both lie below
+// 2^-10 (so both encode to E4M3 zero of the sign of x) everywhere else; the
+// domain is finite and a host-side test enumerates all of it.
 __device__ __forceinline__ float div_by_scale(float x, float s, float r) {
-  float y = x * r;
-  float e = __builtin_fmaf(-y, s, x);
-  return __builtin_fmaf(e, r, y);
+  const float ax = fabsf(x);
+  const float y = ax * r;
+  const float e = __builtin_fmaf(-y, s, ax);
+  return copysignf(__builtin_fmaf(e, r, y), x);
 }
 
 // ------------------------------------------------------- cross-lane max / sum

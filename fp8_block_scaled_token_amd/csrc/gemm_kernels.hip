@@ -19,9 +19,13 @@
 // The contraction runs on v_mfma_*_16x16x128_f8f6f4: one instruction is
 // exactly one 128-wide K block of a 16x16 output tile, so P_b comes out of a
 // single MFMA and the block rescale is 4 VALU FMAs per lane.  Operand layout
-// (A and B alike): lane l supplies row (l % 16) of its operand and the 32
-// consecutive K bytes [32*(l/16), +32) of the block; the 16x16 fp32 result has
-// rows 4*(l/16) + r (r = 0..3) and column l % 16 in lane l.
+// (A and B alike), measured on the device: lane l supplies row (l % 16) of its
+// operand; its first 16 bytes are K [16*(l/16), +16) of the block and its last
+// 16 bytes are K [64 + 16*(l/16), +16).  The E8M0 scale of lane l applies to
+// row (l % 16) and the 32-wide K block number (l / 16) in natural K order,
+// i.e. K [32*(l/16), +32): the first (blocks 0, 1) or last (blocks 2, 3) 16
+// bytes of two lane groups.  The 16x16 fp32 result has rows 4*(l/16) + r
+// (r = 0..3) and column l % 16 in lane l.
 //
 // Two kernels:
 //  * gemm_lds_kernel (prefill): BM x BN workgroup tiles, 4 waves, A and W
@@ -215,9 +219,9 @@ __global__ __launch_bounds__(256, 2) void gemm_lds_kernel(GemmArgs p) {
 
   auto read_frag = [&](const uint8_t* base, int row) {
     Frag f;
-    const int c0 = (lane >> 4) * 2;
+    const int c0 = lane >> 4;          // 16-byte chunks c0 and c0 + 4 of the row
     f.u[0] = *reinterpret_cast<const uint4*>(base + row * 128 + ((c0 ^ (row & 7)) << 4));
-    f.u[1] = *reinterpret_cast<const uint4*>(base + row * 128 + (((c0 + 1) ^ (row & 7)) << 4));
+    f.u[1] = *reinterpret_cast<const uint4*>(base + row * 128 + (((c0 + 4) ^ (row & 7)) << 4));
     return f;
   };
 
@@ -305,7 +309,7 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs p) {
   const int lane = t & 63, wave = t >> 6;
   const int n0 = blockIdx.x * (16 * TN);
   const int m0 = blockIdx.y * (16 * TM);
-  const int kq = (lane >> 4) * 32;      // this lane's 32-byte slice of a K block
+  const int kq = (lane >> 4) * 16;      // this lane's chunks: K [kq, +16) and [64 + kq, +16)
 
   int arow[TM], wrow[TN];
 #pragma unroll
@@ -325,12 +329,12 @@ __global__ __launch_bounds__(256) void gemm_decode_kernel(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       fb[buf][j].u[0] = load_chunk(p.w, p.ldw, wrow[j], k, p.K);
-      fb[buf][j].u[1] = load_chunk(p.w, p.ldw, wrow[j], k + 16, p.K);
+      fb[buf][j].u[1] = load_chunk(p.w, p.ldw, wrow[j], k + 64, p.K);
     }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       fa[buf][i].u[0] = load_chunk(p.a, p.lda, arow[i], k, p.K);
-      fa[buf][i].u[1] = load_chunk(p.a, p.lda, arow[i], k + 16, p.K);
+      fa[buf][i].u[1] = load_chunk(p.a, p.lda, arow[i], k + 64, p.K);
     }
   };
 

@@ -4,9 +4,11 @@
  * The group quantizer needs t = RN32(x / s) for bf16 x with |x| <= amax and
  * s = RN32(max(amax, 1e-10) / 448), amax itself a bf16 value (the group
  * maximum of bf16 inputs).  The GPU kernels compute it without a per-element
- * division: r = RN32(1/s) once per group, y = RN32(x*r), e = fma(-y, s, x)
- * (exact residual), t = fma(e, r, y).  This program enumerates every (amax, x)
- * pair of that finite domain (x >= 0; both formulas are odd in x) and checks
+ * division: r = RN32(1/s) once per group, y = RN32(|x|*r), e = fma(-y, s, |x|)
+ * (exact residual), t = copysign(fma(e, r, y), x).  Both t and the IEEE
+ * quotient are odd in x (the explicit copysign also keeps -0), so it suffices
+ * to enumerate every (amax, x) pair of that finite domain with x >= 0; this
+ * program does so and checks
  * that the FMA sequence returns the bits of the IEEE quotient wherever it can
  * matter.  The FMA residual is exact only while x and y*s stay out of the
  * fp32 subnormal range, so the two may differ when x is tiny; every such pair must
@@ -48,9 +50,10 @@ int main(void) {
     for (uint32_t xb = 0; xb <= ab; ++xb) { /* all bf16 0 <= x <= amax */
       const float x = bf16_to_f32(xb);
       const float ref = x / s;
-      const float y = x * r;
-      const float e = fmaf(-y, s, x);
-      const float t = fmaf(e, r, y);
+      const float ax = fabsf(x);
+      const float y = ax * r;
+      const float e = fmaf(-y, s, ax);
+      const float t = copysignf(fmaf(e, r, y), x);
       ++pairs;
       if (bits(t) != bits(ref)) {
         ++differ;
@@ -60,6 +63,17 @@ int main(void) {
           printf("FATAL amax=%a x=%a ref=%a got=%a\n", amax, x, ref, t);
         }
       }
+    }
+  }
+  /* the negative half relies on oddness; check the one point where an FMA
+   * sequence without the explicit copysign breaks it: x = -0 */
+  {
+    const float s = 3.0f / fmax, r = 1.0f / s, x = -0.0f;
+    const float ax = fabsf(x), y = ax * r, e = fmaf(-y, s, ax);
+    const float t = copysignf(fmaf(e, r, y), x);
+    if (bits(t) != bits(x / s)) {
+      ++fatal;
+      printf("FATAL -0 gives %a\n", t);
     }
   }
   printf("pairs=%llu differ=%llu differ_with_normal_x=%llu fatal=%llu\n", pairs, differ,
