@@ -19,9 +19,15 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfp8q.so")
 
-SOURCES = ["api.cpp", "quant_kernels.hip", "gemm_kernels.hip"]
+SOURCES = ["api.cpp", "quant_kernels.hip", "gemm_kernels.hip", "gemm_fast.hip"]
 
 ARCH = "gfx950"
+
+# per-source device code generation options
+EXTRA_FLAGS = {
+    # MFMA results feed VALU rescale FMAs: keep them in VGPRs, not AGPRs
+    "gemm_fast.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def hipcc() -> str:
@@ -49,6 +55,7 @@ def _compile(src: str, save_temps: bool) -> str:
     cmd = [hipcc()] + compile_flags()
     if src.endswith(".cpp"):
         cmd += ["-x", "hip"]
+    cmd += EXTRA_FLAGS.get(src, [])
     if save_temps:
         cmd += ["-save-temps=obj"]
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]

@@ -51,7 +51,9 @@ fp8q_status check_matrix(const void* p, int64_t K, int64_t ld, int elem_bytes) {
     if (s_ != FP8Q_OK) return s_;      \
   } while (0)
 
-constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+// Launch-grid limits: rows (M, N) up to 2^26, K up to 2^30.
+constexpr int64_t kMaxRows = int64_t(1) << 26;
+constexpr int64_t kMaxK = int64_t(1) << 30;
 
 }  // namespace
 
@@ -61,7 +63,7 @@ const char* fp8q_status_string(fp8q_status_t s) {
   switch (s) {
     case FP8Q_OK: return "ok";
     case FP8Q_ERR_NULL: return "null pointer argument";
-    case FP8Q_ERR_SHAPE: return "invalid shape (negative extent, K <= 0, or ld < K)";
+    case FP8Q_ERR_SHAPE: return "invalid shape (negative extent, K <= 0, ld < K, or beyond the size limits)";
     case FP8Q_ERR_UNSUPPORTED: return "unsupported group/block/format/layout combination";
     case FP8Q_ERR_MISALIGNED: return "misaligned pointer or stride (rows must start on 16-byte boundaries)";
     case FP8Q_ERR_DEVICE: return "current HIP device is not gfx950 (or device query failed)";
@@ -77,7 +79,7 @@ fp8q_status_t fp8q_quant_act_group(const uint16_t* x, int64_t M, int64_t K, int6
                                    int32_t group_size, int32_t fmt, int32_t layout,
                                    const float* static_scale, uint8_t* q, int64_t ldq,
                                    void* scales, void* stream) {
-  if (M < 0 || K <= 0 || M > kMaxDim || K > kMaxDim) return FP8Q_ERR_SHAPE;
+  if (M < 0 || K <= 0 || M > kMaxRows || K > kMaxK) return FP8Q_ERR_SHAPE;
   if (static_scale == nullptr) {
     const bool g128 = group_size == 128 && fmt == FP8Q_SCALE_F32;
     const bool g32 = group_size == 32 && fmt == FP8Q_SCALE_UE8M0;
@@ -106,7 +108,7 @@ fp8q_status_t fp8q_quant_act_group(const uint16_t* x, int64_t M, int64_t K, int6
 fp8q_status_t fp8q_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, float eps, int64_t M,
                                  int64_t K, int64_t ldx, int32_t layout, uint8_t* q, int64_t ldq,
                                  float* scales, uint16_t* y_out, int64_t ldy, void* stream) {
-  if (M < 0 || K <= 0 || M > kMaxDim || K > kMaxDim) return FP8Q_ERR_SHAPE;
+  if (M < 0 || K <= 0 || M > kMaxRows || K > kMaxK) return FP8Q_ERR_SHAPE;
   if (layout != FP8Q_SCALES_ROW_MAJOR && layout != FP8Q_SCALES_COL_MAJOR) return FP8Q_ERR_UNSUPPORTED;
   if (!(eps > 0.0f) || !std::isfinite(eps)) return FP8Q_ERR_VALUE;
   if (M == 0) return FP8Q_OK;
@@ -125,7 +127,7 @@ fp8q_status_t fp8q_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, float
 fp8q_status_t fp8q_quant_weight_block(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
                                       int32_t block_n, int32_t block_k, int32_t fmt, uint8_t* q,
                                       int64_t ldq, void* scale_inv, void* stream) {
-  if (N < 0 || K <= 0 || N > kMaxDim || K > kMaxDim) return FP8Q_ERR_SHAPE;
+  if (N < 0 || K <= 0 || N > kMaxRows || K > kMaxK) return FP8Q_ERR_SHAPE;
   enum { BLOCK, MX, TENSOR } kind;
   if (block_n == 128 && block_k == 128 && fmt == FP8Q_SCALE_F32) kind = BLOCK;
   else if (block_n == 1 && block_k == 32 && fmt == FP8Q_SCALE_UE8M0) kind = MX;
@@ -150,7 +152,8 @@ fp8q_status_t fp8q_gemm_blockscale(const uint8_t* a, int64_t lda, const float* a
                                    const float* w_scale_inv, const uint16_t* bias, uint16_t* y,
                                    int64_t ldy, int64_t M, int64_t N, int64_t K, int32_t gran,
                                    void* stream) {
-  if (M < 0 || N < 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8Q_ERR_SHAPE;
+  if (M < 0 || N < 0 || K <= 0 || M > kMaxRows || N > kMaxRows || K > kMaxK) return FP8Q_ERR_SHAPE;
+  if ((M / 128 + 1) * (N / 128 + 1) >= (int64_t(1) << 24)) return FP8Q_ERR_SHAPE;   // tile grid
   if (gran != FP8Q_GRAN_BLOCK128 && gran != FP8Q_GRAN_PER_TENSOR) return FP8Q_ERR_UNSUPPORTED;
   if (a_layout != FP8Q_SCALES_ROW_MAJOR && a_layout != FP8Q_SCALES_COL_MAJOR) return FP8Q_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) return FP8Q_OK;
@@ -172,7 +175,8 @@ fp8q_status_t fp8q_gemm_mxfp8(const uint8_t* a, int64_t lda, const uint8_t* a_sc
                               const uint8_t* w, int64_t ldw, const uint8_t* w_scales,
                               const uint16_t* bias, uint16_t* y, int64_t ldy, int64_t M,
                               int64_t N, int64_t K, void* stream) {
-  if (M < 0 || N < 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8Q_ERR_SHAPE;
+  if (M < 0 || N < 0 || K <= 0 || M > kMaxRows || N > kMaxRows || K > kMaxK) return FP8Q_ERR_SHAPE;
+  if ((M / 128 + 1) * (N / 128 + 1) >= (int64_t(1) << 24)) return FP8Q_ERR_SHAPE;   // tile grid
   if (M == 0 || N == 0) return FP8Q_OK;
   FP8Q_TRY(check_matrix(a, K, lda, 1));
   FP8Q_TRY(check_matrix(w, K, ldw, 1));

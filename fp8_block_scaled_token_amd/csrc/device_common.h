@@ -39,8 +39,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return u >> 16;
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 pair (v_cvt_pk_bf16_f32: round to nearest even).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  const bf16x2 b = __builtin_convertvector((f32x2){lo, hi}, bf16x2);
+  return __builtin_bit_cast(uint32_t, b);
 }
 
 // ------------------------------------------------------------------ E4M3 encode
@@ -68,48 +73,53 @@ __device__ __forceinline__ uint2 encode8(const float t[8]) {
 // ------------------------------------------------------------ x / s in fp32
 
 // fp32 quotient x / s for the quantizer's operand domain, given r = RN(1/s):
-// y = RN(|x|*r) is refined once with the exact residual |x| - y*s (an FMA) --
-// Markstein's correction -- and the sign of x is put back last (the FMA
-// sequence alone would turn -0 into +0).  For every bf16 x with |x| <= amax
-// and s = RN(max(amax, 1e-10)/448), amax a bf16 value, the result equals the
-// IEEE quotient x / s wherever either is at least 2^-10, and both lie below
-// 2^-10 (so both encode to E4M3 zero of the sign of x) everywhere else; the
-// domain is finite and a host-side test enumerates all of it.
+// y = RN(x*r) is refined once with the exact negated residual y*s - x (one
+// FMA) -- Markstein's correction.  Computing the residual as y*s - x (rather
+// than x - y*s) keeps the sign of a zero x, so the sequence is odd in x.  For
+// every bf16 x with |x| <= amax and s = RN(max(amax, 1e-10)/448), amax a bf16
+// value, the result equals the IEEE quotient x / s wherever either is at
+// least 2^-10, and both lie below 2^-10 (so both encode to the E4M3 zero of
+// the sign of x) everywhere else; a host-side test enumerates that finite
+// domain.
 __device__ __forceinline__ float div_by_scale(float x, float s, float r) {
-  const float ax = fabsf(x);
-  const float y = ax * r;
-  const float e = __builtin_fmaf(-y, s, ax);
-  return copysignf(__builtin_fmaf(e, r, y), x);
+  const float y = x * r;
+  const float e = __builtin_fmaf(y, s, -x);
+  return __builtin_fmaf(-e, r, y);
 }
 
 // ------------------------------------------------------- cross-lane max / sum
 
 template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
 }
+
+// Cross-lane maxima of NON-NEGATIVE, non-NaN fp32 values: on such values the
+// order of the bit patterns as unsigned integers is the numeric order, so the
+// DPP steps are integer maxima (no NaN canonicalisation needed).
 
 // Max over each aligned group of 4 lanes (quad), result in every lane.
 __device__ __forceinline__ float max_quad(float v) {
-  v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
-  v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
-  return v;
+  uint32_t u = __float_as_uint(v);
+  u = max(u, dpp_u<0xB1>(u));     // quad_perm [1,0,3,2]
+  u = max(u, dpp_u<0x4E>(u));     // quad_perm [2,3,0,1]
+  return __uint_as_float(u);
 }
 
 // Max over each aligned row of 16 lanes, result in every lane.
 __device__ __forceinline__ float max_row16(float v) {
-  v = max_quad(v);
-  v = fmaxf(v, dpp_f<0x141>(v));  // row_half_mirror: lanes 0-3 <-> 4-7
-  v = fmaxf(v, dpp_f<0x140>(v));  // row_mirror: lanes 0-7 <-> 8-15
-  return v;
+  uint32_t u = __float_as_uint(max_quad(v));
+  u = max(u, dpp_u<0x141>(u));    // row_half_mirror: lanes 0-3 <-> 4-7
+  u = max(u, dpp_u<0x140>(u));    // row_mirror: lanes 0-7 <-> 8-15
+  return __uint_as_float(u);
 }
 
 // Max over the whole 64-lane wave (every lane gets the result).
 __device__ __forceinline__ float max_wave(float v) {
-  v = max_row16(v);
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+  uint32_t u = __float_as_uint(max_row16(v));
+  u = max(u, (uint32_t)__shfl_xor((int)u, 16));
+  u = max(u, (uint32_t)__shfl_xor((int)u, 32));
+  return __uint_as_float(u);
 }
 
 __device__ __forceinline__ double sum_wave_f64(double v) {

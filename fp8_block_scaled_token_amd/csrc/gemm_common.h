@@ -1,0 +1,115 @@
+// Shared pieces of the scaled FP8 GEMM kernels (gfx950): argument block,
+// MFMA wrappers, tile ordering and the bf16 epilogue store.
+//
+// Operand layout of v_mfma_*_16x16x128_f8f6f4 (A and B alike), measured on
+// the device: lane l supplies row (l % 16) of its operand; its first 16 bytes
+// are K [16*(l/16), +16) of the 128-wide block and its last 16 bytes are
+// K [64 + 16*(l/16), +16).  The E8M0 scale of lane l applies to row (l % 16)
+// and the 32-wide K block number (l / 16) in natural K order, i.e. to
+// K [32*(l/16), +32).  The 16x16 fp32 result has rows 4*(l/16) + r (r = 0..3)
+// and column l % 16 in lane l.
+#pragma once
+
+#include <type_traits>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace fp8q {
+
+enum { MODE_BLOCK = 0, MODE_TENSOR = 1, MODE_MX = 2 };
+
+struct GemmArgs {
+  const uint8_t* a;
+  int64_t lda;
+  const void* sa;       // float* (BLOCK/TENSOR) or uint8_t* (MX)
+  int sa_col_major;
+  const uint8_t* w;
+  int64_t ldw;
+  const void* sw;       // float* (BLOCK/TENSOR) or uint8_t* (MX)
+  const uint16_t* bias;
+  uint16_t* y;
+  int64_t ldy;
+  int M, N, K;
+  int KB;               // number of 128-wide K blocks
+  int KB32;             // number of 32-wide K blocks (MX scale columns)
+  int NB;               // number of 128-row weight blocks
+  int tiles_m, tiles_n;
+};
+
+union Frag {
+  v8i v;
+  uint4 u[2];
+};
+
+// Keep the first `valid` bytes of a 16-byte chunk (0 < valid < 16).
+__device__ __forceinline__ uint4 keep_bytes(uint4 c, int valid) {
+  uint32_t d[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int nb = valid - 4 * i;
+    if (nb <= 0) d[i] = 0u;
+    else if (nb < 4) d[i] &= (1u << (8 * nb)) - 1u;
+  }
+  return make_uint4(d[0], d[1], d[2], d[3]);
+}
+
+// 16 bytes of row `row` starting at column k (k % 16 == 0); bytes >= K are 0.
+// Never touches memory past roundup(K, 16) <= ld.
+__device__ __forceinline__ uint4 load_chunk(const uint8_t* base, int64_t ld, int64_t row, int k, int K) {
+  const int valid = K - k;
+  if (valid >= 16) return ld16(base + row * ld + k);
+  if (valid <= 0) return make_uint4(0, 0, 0, 0);
+  return keep_bytes(ld16(base + row * ld + k), valid);
+}
+
+__device__ __forceinline__ v4f mfma_plain(const v8i& a, const v8i& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ v4f mfma_mx(const v8i& a, const v8i& b, const v4f& c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
+// MX scale byte of (row, 32-block kb32) or the neutral 127 past the last block.
+__device__ __forceinline__ int mx_byte(const uint8_t* s, int64_t row, int kb32, int KB32) {
+  return kb32 < KB32 ? (int)s[row * KB32 + kb32] : 127;
+}
+
+// Workgroup id -> (tile_m, tile_n).  Hardware hands consecutive workgroup ids
+// to the 8 XCDs in turn; renumber so that each XCD receives a contiguous run,
+// then walk tiles in groups of GROUP_M tile rows so neighbours share A and W.
+__device__ __forceinline__ void tile_of(int pid, int tiles_m, int tiles_n, int& tm, int& tn) {
+  constexpr int GROUP_M = 8;
+  const int total = tiles_m * tiles_n;
+  const int xcd = pid & 7, idx = pid >> 3;
+  const int per = total >> 3, rem = total & 7;
+  pid = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + idx;
+  const int width = GROUP_M * tiles_n;
+  const int group = pid / width;
+  const int first_m = group * GROUP_M;
+  const int gsize = min(tiles_m - first_m, GROUP_M);
+  const int in_group = pid - group * width;
+  tm = first_m + in_group % gsize;
+  tn = in_group / gsize;
+}
+
+__device__ __forceinline__ void store_tile_bf16(const GemmArgs& p, const v4f& acc, int row0, int col,
+                                                float mul, float bias) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = row0 + r;
+    if (row < p.M && col < p.N) {
+      float v = acc[r];
+      if (mul != 1.0f) v = v * mul;
+      v = v + bias;
+      p.y[(int64_t)row * p.ldy + col] = (uint16_t)f32_to_bf16_bits(v);
+    }
+  }
+}
+
+// Fast prefill path (gemm_fast.hip): shapes it accepts, and its launcher.
+bool gemm_fast_eligible(const GemmArgs& p);
+hipError_t launch_gemm_fast(GemmArgs p, int mode, hipStream_t stream);
+
+}  // namespace fp8q

@@ -19,28 +19,16 @@
 // elements [seg0 + 512c + 8l, +8): every load instruction of the wave reads one
 // contiguous kilobyte, and the 16 lanes of a DPP row hold exactly one
 // 128-element group (4 lanes hold one 32-element MX block), so group maxima
-// are DPP reductions with no LDS traffic.  Quantization is HBM-bound: the
-// kernels keep all CH loads of a lane in flight before using any of them.
+// are DPP reductions.  The wave's 4*CH group scales are then computed once,
+// lane j handling group j (two IEEE divisions per wave instead of per lane
+// and chunk), and handed back with lane permutes; the same lanes store the
+// scales, so row-major scale writes are one coalesced store.  Segments that
+// lie wholly inside the row take an unmasked path; only a row's last segment
+// masks.  Quantization is HBM-bound: every lane issues all CH loads first.
 #include "device_common.h"
 #include "launch.h"
 
 namespace fp8q {
-
-// --------------------------------------------------------------------------
-// Group-128 dynamic quantizer (fp32 scales)
-
-__device__ __forceinline__ void quant_chunk_g128(const uint4& raw, float amax_row16,
-                                                 uint2& out, float& s_out) {
-  float v[8];
-  unpack8(raw, v);
-  const float s = fmaxf(amax_row16, kAmaxFloor) / kFp8Max;   // IEEE division
-  const float r = 1.0f / s;                                   // IEEE division
-  float t[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) t[e] = clamp448(div_by_scale(v[e], s, r));
-  out = encode8(t);
-  s_out = s;
-}
 
 __device__ __forceinline__ float absmax8(const uint4& raw) {
   float v[8];
@@ -51,40 +39,96 @@ __device__ __forceinline__ float absmax8(const uint4& raw) {
   return m;
 }
 
+// Group scales of a wave segment.  amax[c] holds, in every lane of 16-lane
+// row g, the max of group 4c + g.  Lane j < 4*CH receives group j and computes
+// s = fp32(max(amax, 1e-10) / 448) and r = fp32(1 / s) with IEEE division;
+// s_mine is that value (lane j), s[c] / r[c] the scale of this lane's own
+// group in chunk c.
+template <int CH>
+__device__ __forceinline__ void group_scales(const float (&amax)[CH], float (&s)[CH],
+                                             float (&r)[CH], float& s_mine) {
+  static_assert(4 * CH <= 64, "one lane per group");
+  const int lane = threadIdx.x & 63;
+  float g = 0.0f;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const float v = __shfl(amax[c], (lane & 3) << 4);
+    if ((lane >> 2) == c) g = v;
+  }
+  const float sg = fmaxf(g, kAmaxFloor) / kFp8Max;   // IEEE division
+  const float rg = 1.0f / sg;                         // IEEE division
+  s_mine = sg;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    s[c] = __shfl(sg, 4 * c + (lane >> 4));
+    r[c] = __shfl(rg, 4 * c + (lane >> 4));
+  }
+}
+
+__device__ __forceinline__ uint2 quant8(const uint4& raw, float s, float r) {
+  float v[8], t[8];
+  unpack8(raw, v);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) t[e] = clamp448(div_by_scale(v[e], s, r));
+  return encode8(t);
+}
+
+// Store the wave's group scales: lane j < 4*CH holds group first_group + j.
+template <int CH>
+__device__ __forceinline__ void store_group_scales(float* scales, float s_mine, int64_t first_group,
+                                                   int64_t G, int64_t M, int64_t row, int col_major) {
+  const int lane = threadIdx.x & 63;
+  const int64_t g = first_group + lane;
+  if (lane < 4 * CH && g < G) {
+    if (col_major) scales[g * M + row] = s_mine;
+    else scales[row * G + g] = s_mine;
+  }
+}
+
+// --------------------------------------------------------------------------
+// Group-128 dynamic quantizer (fp32 scales)
+
 template <int CH>
 __global__ __launch_bounds__(256) void quant_group128_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
-    uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ scales, int col_major,
-    int64_t segs_per_row) {
+    uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ scales, int col_major) {
   const int lane = threadIdx.x & 63;
-  const int64_t wave = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;
-  const int64_t row = wave / segs_per_row;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= M) return;
-  const int64_t seg0 = (wave - row * segs_per_row) * (512 * CH);
+  const int64_t seg0 = (int64_t)blockIdx.y * (512 * CH);
   const uint16_t* xr = x + row * ldx;
   uint8_t* qr = q + row * ldq;
-  const int64_t G = (K + 127) >> 7;
+  const bool full = seg0 + 512 * CH <= K;
 
   uint4 raw[CH];
+  if (full) {
+    const uint16_t* xs = xr + seg0 + 8 * lane;
 #pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    const int64_t k0 = seg0 + 512 * c + 8 * lane;
-    raw[c] = (k0 < K) ? load8_bf16_masked(xr, k0, K) : make_uint4(0, 0, 0, 0);
-  }
+    for (int c = 0; c < CH; ++c) raw[c] = ld16(xs + 512 * c);
+  } else {
 #pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    const int64_t k0 = seg0 + 512 * c + 8 * lane;
-    const float amax = max_row16(absmax8(raw[c]));
-    uint2 o;
-    float s;
-    quant_chunk_g128(raw[c], amax, o, s);
-    if (k0 < K) store8_masked(qr, k0, K, o);
-    const int64_t g = (seg0 + 512 * c) / 128 + (lane >> 4);
-    if ((lane & 15) == 0 && g < G) {
-      if (col_major) scales[g * M + row] = s;
-      else scales[row * G + g] = s;
+    for (int c = 0; c < CH; ++c) {
+      const int64_t k0 = seg0 + 512 * c + 8 * lane;
+      raw[c] = (k0 < K) ? load8_bf16_masked(xr, k0, K) : make_uint4(0, 0, 0, 0);
     }
   }
+  float amax[CH], s[CH], r[CH], s_mine;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) amax[c] = max_row16(absmax8(raw[c]));
+  group_scales<CH>(amax, s, r, s_mine);
+  if (full) {
+    uint8_t* qs = qr + seg0 + 8 * lane;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) st8(qs + 512 * c, quant8(raw[c], s[c], r[c]));
+  } else {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int64_t k0 = seg0 + 512 * c + 8 * lane;
+      const uint2 o = quant8(raw[c], s[c], r[c]);
+      if (k0 < K) store8_masked(qr, k0, K, o);
+    }
+  }
+  store_group_scales<CH>(scales, s_mine, seg0 / 128, (K + 127) >> 7, M, row, col_major);
 }
 
 // --------------------------------------------------------------------------
@@ -100,39 +144,49 @@ __device__ __forceinline__ uint32_t ue8m0_byte(float amax) {
   return biased - 8u + (man > 0x600000u ? 1u : 0u);
 }
 
+// x * 2^-e is exact and |x| <= amax <= 448 * 2^e, so no clamp is needed.
+__device__ __forceinline__ uint2 quant8_mx(const uint4& raw, uint32_t byte) {
+  // 2^-e = 2^(127 - byte) as an fp32 bit pattern (byte <= 253 for bf16 input)
+  const float inv = __uint_as_float((254u - byte) << 23);
+  float v[8], t[8];
+  unpack8(raw, v);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) t[e] = v[e] * inv;
+  return encode8(t);
+}
+
 template <int CH>
 __global__ __launch_bounds__(256) void quant_group32mx_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
-    uint8_t* __restrict__ q, int64_t ldq, uint8_t* __restrict__ scales, int col_major,
-    int64_t segs_per_row) {
+    uint8_t* __restrict__ q, int64_t ldq, uint8_t* __restrict__ scales, int col_major) {
   const int lane = threadIdx.x & 63;
-  const int64_t wave = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;
-  const int64_t row = wave / segs_per_row;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= M) return;
-  const int64_t seg0 = (wave - row * segs_per_row) * (512 * CH);
+  const int64_t seg0 = (int64_t)blockIdx.y * (512 * CH);
   const uint16_t* xr = x + row * ldx;
   uint8_t* qr = q + row * ldq;
   const int64_t G = (K + 31) >> 5;
+  const bool full = seg0 + 512 * CH <= K;
 
   uint4 raw[CH];
+  if (full) {
+    const uint16_t* xs = xr + seg0 + 8 * lane;
 #pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    const int64_t k0 = seg0 + 512 * c + 8 * lane;
-    raw[c] = (k0 < K) ? load8_bf16_masked(xr, k0, K) : make_uint4(0, 0, 0, 0);
+    for (int c = 0; c < CH; ++c) raw[c] = ld16(xs + 512 * c);
+  } else {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int64_t k0 = seg0 + 512 * c + 8 * lane;
+      raw[c] = (k0 < K) ? load8_bf16_masked(xr, k0, K) : make_uint4(0, 0, 0, 0);
+    }
   }
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int64_t k0 = seg0 + 512 * c + 8 * lane;
-    const float amax = max_quad(absmax8(raw[c]));
-    const uint32_t byte = ue8m0_byte(amax);
-    // 2^-e = 2^(127 - byte) as an fp32 bit pattern (byte <= 253 for bf16 input)
-    const float inv = __uint_as_float((254u - byte) << 23);
-    float v[8], t[8];
-    unpack8(raw[c], v);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) t[e] = clamp448(v[e] * inv);   // exact scaling
-    const uint2 o = encode8(t);
-    if (k0 < K) store8_masked(qr, k0, K, o);
+    const uint32_t byte = ue8m0_byte(max_quad(absmax8(raw[c])));
+    const uint2 o = quant8_mx(raw[c], byte);
+    if (full) st8(qr + k0, o);
+    else if (k0 < K) store8_masked(qr, k0, K, o);
     const int64_t g = (seg0 + 512 * c) / 32 + (lane >> 2);
     if ((lane & 3) == 0 && g < G) {
       if (col_major) scales[g * M + row] = (uint8_t)byte;
@@ -142,26 +196,25 @@ __global__ __launch_bounds__(256) void quant_group32mx_kernel(
 }
 
 // --------------------------------------------------------------------------
-// Static per-tensor quantizer
+// Static per-tensor quantizer (any positive scale: IEEE division per element)
 
 template <int CH>
 __global__ __launch_bounds__(256) void quant_static_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
-    const float* __restrict__ scale, uint8_t* __restrict__ q, int64_t ldq,
-    int64_t segs_per_row) {
+    const float* __restrict__ scale, uint8_t* __restrict__ q, int64_t ldq) {
   const int lane = threadIdx.x & 63;
-  const int64_t wave = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;
-  const int64_t row = wave / segs_per_row;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= M) return;
-  const int64_t seg0 = (wave - row * segs_per_row) * (512 * CH);
+  const int64_t seg0 = (int64_t)blockIdx.y * (512 * CH);
   const uint16_t* xr = x + row * ldx;
   uint8_t* qr = q + row * ldq;
   const float s = *scale;
+  const bool full = seg0 + 512 * CH <= K;
   uint4 raw[CH];
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int64_t k0 = seg0 + 512 * c + 8 * lane;
-    raw[c] = (k0 < K) ? load8_bf16_masked(xr, k0, K) : make_uint4(0, 0, 0, 0);
+    raw[c] = full ? ld16(xr + k0) : (k0 < K) ? load8_bf16_masked(xr, k0, K) : make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
@@ -170,12 +223,16 @@ __global__ __launch_bounds__(256) void quant_static_kernel(
     unpack8(raw[c], v);
 #pragma unroll
     for (int e = 0; e < 8; ++e) t[e] = clamp448(v[e] / s);   // IEEE division
-    if (k0 < K) store8_masked(qr, k0, K, encode8(t));
+    const uint2 o = encode8(t);
+    if (full) st8(qr + k0, o);
+    else if (k0 < K) store8_masked(qr, k0, K, o);
   }
 }
 
 // --------------------------------------------------------------------------
-// RMSNorm fused with the group-128 quantizer: one wave per row.
+// RMSNorm fused with the group-128 quantizer: one wave per row.  With
+// ONE_PASS the whole row (K <= 512*CH) stays in registers between the sum of
+// squares and the quantization; otherwise the row is read twice.
 
 template <int CH, bool ONE_PASS>
 __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(
@@ -187,19 +244,29 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(
   if (row >= M) return;
   const uint16_t* xr = x + row * ldx;
   uint8_t* qr = q + row * ldq;
+  uint16_t* yr = y_out != nullptr ? y_out + row * ldy : nullptr;
   const int64_t G = (K + 127) >> 7;
   constexpr int64_t SEG = 512 * CH;
   const int64_t nseg = ONE_PASS ? 1 : (K + SEG - 1) / SEG;
 
-  // pass 1: sum of squares in fp64 (bf16 squares are exact in fp64)
+  auto load_seg = [&](uint4 (&raw)[CH], int64_t seg0) {
+    if (seg0 + SEG <= K) {
+#pragma unroll
+      for (int c = 0; c < CH; ++c) raw[c] = ld16(xr + seg0 + 512 * c + 8 * lane);
+    } else {
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const int64_t k0 = seg0 + 512 * c + 8 * lane;
+        raw[c] = (k0 < K) ? load8_bf16_masked(xr, k0, K) : make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+
+  // pass 1: sum of squares in fp64 (squares of bf16 values are exact)
   uint4 raw[CH];
   double ss = 0.0;
   for (int64_t sg = 0; sg < nseg; ++sg) {
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int64_t k0 = sg * SEG + 512 * c + 8 * lane;
-      raw[c] = (k0 < K) ? load8_bf16_masked(xr, k0, K) : make_uint4(0, 0, 0, 0);
-    }
+    load_seg(raw, sg * SEG);
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       float v[8];
@@ -212,44 +279,42 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(
     }
   }
   ss = sum_wave_f64(ss);
-  const float r = (float)(1.0 / sqrt(ss / (double)K + (double)eps));
+  const float rn = (float)(1.0 / sqrt(ss / (double)K + (double)eps));
 
-  // pass 2: normalize, round to bf16, quantize per 128-group
+  // pass 2: y = bf16((x * r) * g), then group quantization of y
   for (int64_t sg = 0; sg < nseg; ++sg) {
-    if (!ONE_PASS) {
-#pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        const int64_t k0 = sg * SEG + 512 * c + 8 * lane;
-        raw[c] = (k0 < K) ? load8_bf16_masked(xr, k0, K) : make_uint4(0, 0, 0, 0);
-      }
-    }
+    const int64_t seg0 = sg * SEG;
+    const bool full = seg0 + SEG <= K;
+    if (!ONE_PASS) load_seg(raw, seg0);
+    float amax[CH];
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const int64_t k0 = sg * SEG + 512 * c + 8 * lane;
-      const uint4 gr = (k0 < K) ? load8_bf16_masked(gamma, k0, K) : make_uint4(0, 0, 0, 0);
+      const int64_t k0 = seg0 + 512 * c + 8 * lane;
+      const uint4 gr = full ? ld16(gamma + k0)
+                            : (k0 < K) ? load8_bf16_masked(gamma, k0, K) : make_uint4(0, 0, 0, 0);
       float v[8], g[8];
       unpack8(raw[c], v);
       unpack8(gr, g);
       uint32_t yb[4];
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const float y0 = (v[e] * r) * g[e];
-        const float y1 = (v[e + 1] * r) * g[e + 1];
-        yb[e >> 1] = pack_bf16x2(y0, y1);
+      for (int e = 0; e < 8; e += 2) yb[e >> 1] = pack_bf16x2((v[e] * rn) * g[e], (v[e + 1] * rn) * g[e + 1]);
+      raw[c] = make_uint4(yb[0], yb[1], yb[2], yb[3]);      // raw now holds bf16 y
+      if (yr != nullptr) {
+        if (full) *reinterpret_cast<uint4*>(yr + k0) = raw[c];
+        else if (k0 < K) store8_bf16_masked(yr, k0, K, raw[c]);
       }
-      const uint4 ybits = make_uint4(yb[0], yb[1], yb[2], yb[3]);
-      if (y_out != nullptr && k0 < K) store8_bf16_masked(y_out + row * ldy, k0, K, ybits);
-      const float amax = max_row16(absmax8(ybits));
-      uint2 o;
-      float s;
-      quant_chunk_g128(ybits, amax, o, s);
-      if (k0 < K) store8_masked(qr, k0, K, o);
-      const int64_t gi = (sg * SEG + 512 * c) / 128 + (lane >> 4);
-      if ((lane & 15) == 0 && gi < G) {
-        if (col_major) scales[gi * M + row] = s;
-        else scales[row * G + gi] = s;
-      }
+      amax[c] = max_row16(absmax8(raw[c]));
     }
+    float s[CH], r[CH], s_mine;
+    group_scales<CH>(amax, s, r, s_mine);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int64_t k0 = seg0 + 512 * c + 8 * lane;
+      const uint2 o = quant8(raw[c], s[c], r[c]);
+      if (full) st8(qr + k0, o);
+      else if (k0 < K) store8_masked(qr, k0, K, o);
+    }
+    store_group_scales<CH>(scales, s_mine, seg0 / 128, G, M, row, col_major);
   }
 }
 
@@ -297,13 +362,7 @@ __global__ __launch_bounds__(256) void weight_block_kernel(
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int64_t n = bn * 128 + (t >> 4) + 16 * i;
-    if (n < N && k0 < K) {
-      float v[8], tt[8];
-      unpack8(raw[i], v);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) tt[e] = clamp448(div_by_scale(v[e], s, r));
-      store8_masked(q + n * ldq, k0, K, encode8(tt));
-    }
+    if (n < N && k0 < K) store8_masked(q + n * ldq, k0, K, quant8(raw[i], s, r));
   }
   if (MODE == 0 && t == 0) scale_out[bn * KB + bk] = s;
 }
@@ -323,43 +382,43 @@ static inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Row quantizers: segments of 512*CH elements per wave; CH is chosen so that
 // short rows do not leave most lanes idle.
+static inline int row_chunks(int64_t K) { return K <= 512 ? 1 : (K <= 1024 ? 2 : 4); }
+
 hipError_t launch_quant_group128(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                  uint8_t* q, int64_t ldq, float* scales, int col_major,
                                  hipStream_t stream) {
-  const int ch = K <= 512 ? 1 : (K <= 1024 ? 2 : 4);
+  const int ch = row_chunks(K);
   const int64_t segs = ceil_div(K, 512 * ch);
-  const int64_t waves = M * segs;
-  const dim3 grid((unsigned)ceil_div(waves, 4)), block(256);
+  const dim3 grid((unsigned)ceil_div(M, 4), (unsigned)segs), block(256);
   if (ch == 1)
-    hipLaunchKernelGGL(quant_group128_kernel<1>, grid, block, 0, stream, x, M, K, ldx, q, ldq, scales, col_major, segs);
+    hipLaunchKernelGGL(quant_group128_kernel<1>, grid, block, 0, stream, x, M, K, ldx, q, ldq, scales, col_major);
   else if (ch == 2)
-    hipLaunchKernelGGL(quant_group128_kernel<2>, grid, block, 0, stream, x, M, K, ldx, q, ldq, scales, col_major, segs);
+    hipLaunchKernelGGL(quant_group128_kernel<2>, grid, block, 0, stream, x, M, K, ldx, q, ldq, scales, col_major);
   else
-    hipLaunchKernelGGL(quant_group128_kernel<4>, grid, block, 0, stream, x, M, K, ldx, q, ldq, scales, col_major, segs);
+    hipLaunchKernelGGL(quant_group128_kernel<4>, grid, block, 0, stream, x, M, K, ldx, q, ldq, scales, col_major);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_group32mx(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                   uint8_t* q, int64_t ldq, uint8_t* scales, int col_major,
                                   hipStream_t stream) {
-  const int ch = K <= 512 ? 1 : (K <= 1024 ? 2 : 4);
+  const int ch = row_chunks(K);
   const int64_t segs = ceil_div(K, 512 * ch);
-  const int64_t waves = M * segs;
-  const dim3 grid((unsigned)ceil_div(waves, 4)), block(256);
+  const dim3 grid((unsigned)ceil_div(M, 4), (unsigned)segs), block(256);
   if (ch == 1)
-    hipLaunchKernelGGL(quant_group32mx_kernel<1>, grid, block, 0, stream, x, M, K, ldx, q, ldq, scales, col_major, segs);
+    hipLaunchKernelGGL(quant_group32mx_kernel<1>, grid, block, 0, stream, x, M, K, ldx, q, ldq, scales, col_major);
   else if (ch == 2)
-    hipLaunchKernelGGL(quant_group32mx_kernel<2>, grid, block, 0, stream, x, M, K, ldx, q, ldq, scales, col_major, segs);
+    hipLaunchKernelGGL(quant_group32mx_kernel<2>, grid, block, 0, stream, x, M, K, ldx, q, ldq, scales, col_major);
   else
-    hipLaunchKernelGGL(quant_group32mx_kernel<4>, grid, block, 0, stream, x, M, K, ldx, q, ldq, scales, col_major, segs);
+    hipLaunchKernelGGL(quant_group32mx_kernel<4>, grid, block, 0, stream, x, M, K, ldx, q, ldq, scales, col_major);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_static(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                const float* scale, uint8_t* q, int64_t ldq, hipStream_t stream) {
   const int64_t segs = ceil_div(K, 512 * 4);
-  const dim3 grid((unsigned)ceil_div(M * segs, 4)), block(256);
-  hipLaunchKernelGGL(quant_static_kernel<4>, grid, block, 0, stream, x, M, K, ldx, scale, q, ldq, segs);
+  const dim3 grid((unsigned)ceil_div(M, 4), (unsigned)segs), block(256);
+  hipLaunchKernelGGL(quant_static_kernel<4>, grid, block, 0, stream, x, M, K, ldx, scale, q, ldq);
   return hipGetLastError();
 }
 

@@ -55,7 +55,8 @@ extern "C" {
 typedef enum {
   FP8Q_OK = 0,
   FP8Q_ERR_NULL = 1,         /* a required pointer is NULL                      */
-  FP8Q_ERR_SHAPE = 2,        /* negative extent, K <= 0, or ld < row length     */
+  FP8Q_ERR_SHAPE = 2,        /* negative extent, K <= 0, ld < row length, or an
+                                extent beyond the limits (rows 2^26, K 2^30) */
   FP8Q_ERR_UNSUPPORTED = 3,  /* group/block/format/layout combination not offered */
   FP8Q_ERR_MISALIGNED = 4,   /* pointer or stride breaks the alignment rule     */
   FP8Q_ERR_DEVICE = 5,       /* current device is not gfx950, or HIP query failed */

@@ -4,11 +4,10 @@
  * The group quantizer needs t = RN32(x / s) for bf16 x with |x| <= amax and
  * s = RN32(max(amax, 1e-10) / 448), amax itself a bf16 value (the group
  * maximum of bf16 inputs).  The GPU kernels compute it without a per-element
- * division: r = RN32(1/s) once per group, y = RN32(|x|*r), e = fma(-y, s, |x|)
- * (exact residual), t = copysign(fma(e, r, y), x).  Both t and the IEEE
- * quotient are odd in x (the explicit copysign also keeps -0), so it suffices
- * to enumerate every (amax, x) pair of that finite domain with x >= 0; this
- * program does so and checks
+ * division: r = RN32(1/s) once per group, y = RN32(x*r), e = fma(y, s, -x)
+ * (the exact negated residual), t = fma(-e, r, y).  This program enumerates
+ * every (amax, x) pair of that finite domain, both signs of x (and -0), and
+ * checks
  * that the FMA sequence returns the bits of the IEEE quotient wherever it can
  * matter.  The FMA residual is exact only while x and y*s stay out of the
  * fp32 subnormal range, so the two may differ when x is tiny; every such pair must
@@ -17,6 +16,7 @@
  * had a normal x) and fails if any differing pair reaches 2^-10.
  *
  * Build: gcc -O2 -mfma -ffp-contract=off -fopenmp; exit status 0 = pass.
+ * (x86-64 only: the negations are pinned with an empty asm barrier.)
  */
 #include <math.h>
 #include <stdint.h>
@@ -28,6 +28,13 @@ static float bf16_to_f32(uint32_t b) {
   float f;
   memcpy(&f, &u, 4);
   return f;
+}
+
+/* Hide a value from the optimizer: gcc otherwise rewrites fma(-fma(a, b, -c), ...)
+ * as fma(fma(-a, b, c), ...), which differs in the sign of a zero result. */
+static inline float opaque(float v) {
+  __asm__("" : "+x"(v));
+  return v;
 }
 
 static uint32_t bits(float f) {
@@ -47,33 +54,24 @@ int main(void) {
     const float a = amax > floor_ ? amax : floor_;
     const float s = a / fmax;
     const float r = 1.0f / s;
-    for (uint32_t xb = 0; xb <= ab; ++xb) { /* all bf16 0 <= x <= amax */
-      const float x = bf16_to_f32(xb);
-      const float ref = x / s;
-      const float ax = fabsf(x);
-      const float y = ax * r;
-      const float e = fmaf(-y, s, ax);
-      const float t = copysignf(fmaf(e, r, y), x);
-      ++pairs;
-      if (bits(t) != bits(ref)) {
-        ++differ;
-        if (x >= 0x1p-126f) ++differ_normal_x;
-        if (fabsf(ref) >= tiny || fabsf(t) >= tiny) {
-          ++fatal;
-          printf("FATAL amax=%a x=%a ref=%a got=%a\n", amax, x, ref, t);
+    for (uint32_t xb = 0; xb <= ab; ++xb) { /* all bf16 |x| <= amax, both signs */
+      for (uint32_t sign = 0; sign < 2; ++sign) {
+        const float x = bf16_to_f32(xb | (sign << 15));
+        const float ref = x / s;
+        const float y = x * r;
+        const float e = opaque(fmaf(y, s, opaque(-x)));
+        const float t = fmaf(opaque(-e), r, y);
+        ++pairs;
+        if (bits(t) != bits(ref)) {
+          ++differ;
+          if (fabsf(x) >= 0x1p-126f) ++differ_normal_x;
+          /* must encode alike: both below 2^-10 (E4M3 zero) with x's sign */
+          if (fabsf(ref) >= tiny || fabsf(t) >= tiny || signbit(t) != signbit(x)) {
+            ++fatal;
+            printf("FATAL amax=%a x=%a ref=%a got=%a\n", amax, x, ref, t);
+          }
         }
       }
-    }
-  }
-  /* the negative half relies on oddness; check the one point where an FMA
-   * sequence without the explicit copysign breaks it: x = -0 */
-  {
-    const float s = 3.0f / fmax, r = 1.0f / s, x = -0.0f;
-    const float ax = fabsf(x), y = ax * r, e = fmaf(-y, s, ax);
-    const float t = copysignf(fmaf(e, r, y), x);
-    if (bits(t) != bits(x / s)) {
-      ++fatal;
-      printf("FATAL -0 gives %a\n", t);
     }
   }
   printf("pairs=%llu differ=%llu differ_with_normal_x=%llu fatal=%llu\n", pairs, differ,
