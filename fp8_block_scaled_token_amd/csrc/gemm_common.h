@@ -109,7 +109,7 @@ __device__ __forceinline__ void store_tile_bf16(const GemmArgs& p, const v4f& ac
 }
 
 // Fast prefill path (gemm_fast.hip): shapes it accepts, and its launcher.
-bool gemm_fast_eligible(const GemmArgs& p);
+bool gemm_fast_eligible(const GemmArgs& p, int mode);
 hipError_t launch_gemm_fast(GemmArgs p, int mode, hipStream_t stream);
 
 }  // namespace fp8q

@@ -26,9 +26,7 @@ namespace fp8q {
 
 namespace {
 
-constexpr int FBM = 256, FBN = 128;           // workgroup tile
-constexpr int A_BYTES = FBM * 128;            // one K block of A (128 bytes per row)
-constexpr int W_BYTES = FBN * 128;
+constexpr int FBN = 128;                      // workgroup tile width (one weight-scale block)
 
 // Byte offset of 16-byte chunk c (0..7) of tile row r in a swizzled LDS tile.
 __device__ __forceinline__ int swz(int r, int c) { return (r << 7) | ((c ^ (r & 7)) << 4); }
@@ -50,22 +48,23 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// Direct-to-LDS loads: lane i's 16 (or 4) bytes land at wave_base + 16*i (4*i).
+// Direct-to-LDS loads: lane i's 16 (or 4) bytes land at LDS address
+// lds + 16*i (4*i); `lds` must be wave-uniform.
 // Written as inline assembly on purpose: the compiler cannot tell which LDS
 // stage a direct-to-LDS load fills, and would otherwise make every LDS read
 // wait for all of them.  These loads are therefore invisible to the
 // compiler's vmcnt bookkeeping; the kernel waits for them explicitly
 // (wait_vmcnt) and issues no other vector-memory loads inside its K loop.
-__device__ __forceinline__ void dma16(const i32x4& r, const void* wave_base, int voffset) {
+__device__ __forceinline__ void dma16(const i32x4& r, uint32_t lds, int voffset) {
   asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
-               : "v"(voffset), "s"(r), "s"(__builtin_amdgcn_readfirstlane(lds_addr(wave_base)))
+               : "v"(voffset), "s"(r), "s"(lds)
                : "memory", "m0");
 }
-__device__ __forceinline__ void dma4(const i32x4& r, const void* wave_base, int voffset) {
+__device__ __forceinline__ void dma4(const i32x4& r, uint32_t lds, int voffset) {
   asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds"
                :
-               : "v"(voffset), "s"(r), "s"(__builtin_amdgcn_readfirstlane(lds_addr(wave_base)))
+               : "v"(voffset), "s"(r), "s"(lds)
                : "memory", "m0");
 }
 
@@ -77,28 +76,34 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 }  // namespace
 
-// NW waves per workgroup (4 or 8) in a WM x (NW/WM) grid over the 256 x 128
-// tile.  LDS (three stages) limits the kernel to one workgroup per CU.
-template <int MODE, int NW>
+// BM x 128 workgroup tile, NW waves in a WM x (NW/WM) grid, NS LDS stages
+// (each stage one LDS object: A tile, W tile, scale words).
+template <int MODE, int BM, int NW, int NS>
 __global__ __launch_bounds__(NW * 64) void gemm_fast_kernel(GemmArgs p) {
-  constexpr int WM = NW == 8 ? 4 : 2, WN = NW / WM;
-  constexpr int WTM = FBM / WM, WTN = FBN / WN;        // wave tile
+  constexpr int BN = FBN;
+  constexpr int WM = (NW == 8 && BM == 256) ? 4 : 2, WN = NW / WM;
+  constexpr int WTM = BM / WM, WTN = BN / WN;          // wave tile
   constexpr int TM = WTM / 16, TN = WTN / 16;
-  constexpr int A_PER = (A_BYTES / 1024) / NW;         // 1 KB DMA instructions per wave
-  constexpr int W_PER = (W_BYTES / 1024) / NW;
-  constexpr int RA = FBM / NW, RW = FBN / NW;          // scale rows per wave
+  constexpr int ABYTES = BM * 128, WBYTES = BN * 128;  // one K block of A / W
+  constexpr int A_PER = (ABYTES / 1024) / NW;          // 1 KB DMA instructions per wave
+  constexpr int W_PER = (WBYTES / 1024) / NW;
+  constexpr int RA = BM / NW, RW = BN / NW;            // scale rows per wave
   constexpr int S_WORDS_NW = 128 * NW;                 // A scales, then W scales / copies
-  constexpr int STAGE_BYTES = A_BYTES + W_BYTES + S_WORDS_NW * 4;
+  constexpr int STAGE_BYTES = ABYTES + WBYTES + S_WORDS_NW * 4;
+  static_assert(A_PER >= 1 && W_PER >= 1 && RA <= 64 && RW <= 64, "tile too small for NW waves");
   static_assert(WTN <= 128 && 128 % WTN == 0, "one weight-scale block per wave");
-  // one LDS object per stage: A tile, W tile, scale words
-  __shared__ __attribute__((aligned(1024))) uint8_t st0[STAGE_BYTES], st1[STAGE_BYTES], st2[STAGE_BYTES];
+  static_assert(NS >= 2 && NS <= 4, "2..4 stages");
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[STAGE_BYTES], st1[STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t st2[NS > 2 ? STAGE_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t st3[NS > 3 ? STAGE_BYTES : 16];
 
   const int t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave / WN, wn = wave % WN;
   int tm, tn;
   tile_of(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
-  const int m0 = tm * FBM, n0 = tn * FBN;
+  const int m0 = tm * BM, n0 = tn * BN;
 
   const i32x4 rA = rsrc(p.a, (int64_t)p.M * p.lda);
   const i32x4 rW = rsrc(p.w, (int64_t)p.N * p.ldw);
@@ -124,30 +129,32 @@ __global__ __launch_bounds__(NW * 64) void gemm_fast_kernel(GemmArgs p) {
   auto stage = [&](auto S) -> uint8_t* {
     if constexpr (decltype(S)::value == 0) return st0;
     else if constexpr (decltype(S)::value == 1) return st1;
-    else return st2;
+    else if constexpr (decltype(S)::value == 2) return st2;
+    else return st3;
   };
-  auto stage_s = [&](auto S) -> uint32_t* { return reinterpret_cast<uint32_t*>(stage(S) + A_BYTES + W_BYTES); };
+  auto stage_s = [&](auto S) -> uint32_t* { return reinterpret_cast<uint32_t*>(stage(S) + ABYTES + WBYTES); };
 
   // DMA instructions per wave per stage (the vmcnt bookkeeping relies on it)
   constexpr int NLOAD = A_PER + W_PER + (MODE == MODE_TENSOR ? 0 : 2);
 
   auto issue = [&](auto S, int kb) {
-    uint8_t* a = stage(S) + wave * A_PER * 1024;
-    uint8_t* w = stage(S) + A_BYTES + wave * W_PER * 1024;
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(stage(S)));
+    const uint32_t a = base + wave * A_PER * 1024;
+    const uint32_t w = base + ABYTES + wave * W_PER * 1024;
+    const uint32_t sc = base + ABYTES + WBYTES + wave * 256;
     const int kofs = kb * 128;
 #pragma unroll
     for (int i = 0; i < A_PER; ++i) dma16(rA, a + i * 1024, offA + i * lda8 + kofs);
 #pragma unroll
     for (int i = 0; i < W_PER; ++i) dma16(rW, w + i * 1024, offW + i * ldw8 + kofs);
-    uint32_t* s = stage_s(S);
     if constexpr (MODE == MODE_BLOCK) {
       const int e = p.sa_col_major ? kb * p.M + srow : srow * p.KB + kb;
-      dma4(rSA, s + wave * 64, e * 4);
+      dma4(rSA, sc, e * 4);
       // the tile's weight-block scale, same address in every lane
-      dma4(rSW, s + 64 * NW + wave * 64, (wblk * p.KB + kb) * 4);
+      dma4(rSW, sc + 256 * NW, (wblk * p.KB + kb) * 4);
     } else if constexpr (MODE == MODE_MX) {
-      dma4(rSA, s + wave * 64, srow * p.KB32 + kb * 4);
-      dma4(rSW, s + 64 * NW + wave * 64, swrow * p.KB32 + kb * 4);
+      dma4(rSA, sc, srow * p.KB32 + kb * 4);
+      dma4(rSW, sc + 256 * NW, swrow * p.KB32 + kb * 4);
     }
   };
   // word index of A-scale row r / W-scale row c within a stage's scale words
@@ -170,7 +177,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_fast_kernel(GemmArgs p) {
 
   auto compute = [&](auto S) {
     const uint8_t* a = stage(S);
-    const uint8_t* w = stage(S) + A_BYTES;
+    const uint8_t* w = stage(S) + ABYTES;
     const uint32_t* s = stage_s(S);
     Frag fb[TN];
 #pragma unroll
@@ -214,26 +221,45 @@ __global__ __launch_bounds__(NW * 64) void gemm_fast_kernel(GemmArgs p) {
     }
   };
 
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  using S2 = std::integral_constant<int, 2>;
-
-  auto step = [&](auto S, auto S_next2, int kb) {
-    // stage S holds block kb; block kb+1 may still be in flight
-    if (kb + 1 < p.KB) wait_vmcnt<NLOAD>();
-    else wait_vmcnt<0>();
+  // step kb: stage S = kb % NS holds block kb.  Blocks kb+1 .. kb+NS-2 may
+  // still be in flight; block kb+NS-1 is issued into the stage freed by kb-1.
+  auto step = [&](auto S, auto S_issue, int kb) {
+    const int ahead = min(p.KB - 1 - kb, NS - 2);     // blocks issued after kb
+    if constexpr (NS == 2) {
+      wait_vmcnt<0>();
+    } else if constexpr (NS == 3) {
+      if (ahead >= 1) wait_vmcnt<NLOAD>(); else wait_vmcnt<0>();
+    } else {
+      if (ahead >= 2) wait_vmcnt<2 * NLOAD>(); else if (ahead == 1) wait_vmcnt<NLOAD>(); else wait_vmcnt<0>();
+    }
     // plain s_barrier: a __syncthreads() fence would wait for every load in flight
     __builtin_amdgcn_s_barrier();
-    if (kb + 2 < p.KB) issue(S_next2, kb + 2);
+    if (kb + NS - 1 < p.KB) issue(S_issue, kb + NS - 1);
     compute(S);
   };
 
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
+
   issue(S0{}, 0);
-  if (p.KB > 1) issue(S1{}, 1);
-  for (int kb = 0; kb < p.KB; kb += 3) {
-    step(S0{}, S2{}, kb);
-    if (kb + 1 < p.KB) step(S1{}, S0{}, kb + 1);
-    if (kb + 2 < p.KB) step(S2{}, S1{}, kb + 2);
+  if (NS > 2 && p.KB > 1) issue(S1{}, 1);
+  if (NS > 3 && p.KB > 2) issue(S2{}, 2);
+  for (int kb = 0; kb < p.KB; kb += NS) {
+    if constexpr (NS == 2) {
+      step(S0{}, S1{}, kb);
+      if (kb + 1 < p.KB) step(S1{}, S0{}, kb + 1);
+    } else if constexpr (NS == 3) {
+      step(S0{}, S2{}, kb);
+      if (kb + 1 < p.KB) step(S1{}, S0{}, kb + 1);
+      if (kb + 2 < p.KB) step(S2{}, S1{}, kb + 2);
+    } else {
+      step(S0{}, S3{}, kb);
+      if (kb + 1 < p.KB) step(S1{}, S0{}, kb + 1);
+      if (kb + 2 < p.KB) step(S2{}, S1{}, kb + 2);
+      if (kb + 3 < p.KB) step(S3{}, S2{}, kb + 3);
+    }
   }
 
   float mul = 1.0f;
@@ -249,41 +275,46 @@ __global__ __launch_bounds__(NW * 64) void gemm_fast_kernel(GemmArgs p) {
   }
 }
 
-// Waves per workgroup: FP8Q_GEMM_WAVES=4|8 overrides (tuning only).
-static int gemm_fast_waves(int mode) {
+// Tile configuration: 0 = 256x128 tile, 8 waves, 3 stages (one workgroup
+// per CU); 1 = 128x128 tile, 4 waves, 2 stages (two workgroups per CU, whose
+// independent barriers overlap).  Measured on MI355X: 1 is faster for the
+// block and per-tensor modes, 0 for MX.  FP8Q_GEMM_CFG overrides (tuning).
+static int gemm_fast_cfg(int mode) {
   static const int forced = [] {
-    const char* e = getenv("FP8Q_GEMM_WAVES");
-    return e ? atoi(e) : 0;
+    const char* e = getenv("FP8Q_GEMM_CFG");
+    return e ? atoi(e) : -1;
   }();
-  if (forced == 4 || forced == 8) return forced;
-  (void)mode;
-  return 8;
+  if (forced == 0 || forced == 1) return forced;
+  return mode == MODE_MX ? 0 : 1;
 }
 
-bool gemm_fast_eligible(const GemmArgs& p) {
-  const int64_t a_bytes = (int64_t)p.M * p.lda + 256 * p.lda;     // + rows past M of the last tile
-  const int64_t w_bytes = (int64_t)p.N * p.ldw + 128 * p.ldw;
+static int cfg_bm(int cfg) { return cfg == 1 ? 128 : 256; }
+
+bool gemm_fast_eligible(const GemmArgs& p, int mode) {
+  const int bm = cfg_bm(gemm_fast_cfg(mode));
+  const int64_t a_bytes = (int64_t)p.M * p.lda + bm * p.lda;     // + rows past M of the last tile
+  const int64_t w_bytes = (int64_t)p.N * p.ldw + FBN * p.ldw;
   const int64_t lim = (int64_t(1) << 31) - 1;
   return p.M > 64 && p.K % 128 == 0 && a_bytes < lim && w_bytes < lim &&
-         (int64_t)p.M * p.KB * 4 + 1024 < lim && (int64_t)(p.M + 256) * p.KB32 < lim &&
-         (int64_t)(p.N + 128) * p.KB32 < lim;
+         (int64_t)(p.M + bm) * p.KB * 4 < lim && (int64_t)(p.M + bm) * p.KB32 < lim &&
+         (int64_t)(p.N + FBN) * p.KB32 < lim;
+}
+
+template <int MODE>
+static void launch_cfg(const GemmArgs& p, int cfg, hipStream_t stream) {
+  const dim3 grid(p.tiles_m * p.tiles_n);
+  if (cfg == 1) hipLaunchKernelGGL((gemm_fast_kernel<MODE, 128, 4, 2>), grid, dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL((gemm_fast_kernel<MODE, 256, 8, 3>), grid, dim3(512), 0, stream, p);
 }
 
 hipError_t launch_gemm_fast(GemmArgs p, int mode, hipStream_t stream) {
-  p.tiles_m = (p.M + FBM - 1) / FBM;
+  const int cfg = gemm_fast_cfg(mode);
+  const int bm = cfg_bm(cfg);
+  p.tiles_m = (p.M + bm - 1) / bm;
   p.tiles_n = (p.N + FBN - 1) / FBN;
-  const dim3 grid(p.tiles_m * p.tiles_n);
-  const int nw = gemm_fast_waves(mode);
-  if (mode == MODE_BLOCK) {
-    if (nw == 8) hipLaunchKernelGGL((gemm_fast_kernel<MODE_BLOCK, 8>), grid, dim3(512), 0, stream, p);
-    else hipLaunchKernelGGL((gemm_fast_kernel<MODE_BLOCK, 4>), grid, dim3(256), 0, stream, p);
-  } else if (mode == MODE_TENSOR) {
-    if (nw == 8) hipLaunchKernelGGL((gemm_fast_kernel<MODE_TENSOR, 8>), grid, dim3(512), 0, stream, p);
-    else hipLaunchKernelGGL((gemm_fast_kernel<MODE_TENSOR, 4>), grid, dim3(256), 0, stream, p);
-  } else {
-    if (nw == 8) hipLaunchKernelGGL((gemm_fast_kernel<MODE_MX, 8>), grid, dim3(512), 0, stream, p);
-    else hipLaunchKernelGGL((gemm_fast_kernel<MODE_MX, 4>), grid, dim3(256), 0, stream, p);
-  }
+  if (mode == MODE_BLOCK) launch_cfg<MODE_BLOCK>(p, cfg, stream);
+  else if (mode == MODE_TENSOR) launch_cfg<MODE_TENSOR>(p, cfg, stream);
+  else launch_cfg<MODE_MX>(p, cfg, stream);
   return hipGetLastError();
 }
 

@@ -356,7 +356,7 @@ static hipError_t launch_mode(GemmArgs p, hipStream_t stream) {
 #undef FP8Q_DEC
     return hipGetLastError();
   }
-  if (gemm_fast_eligible(p)) return launch_gemm_fast(p, MODE, stream);
+  if (gemm_fast_eligible(p, MODE)) return launch_gemm_fast(p, MODE, stream);
   constexpr int BM = 128, BN = 128;
   p.tiles_m = cdiv(p.M, BM);
   p.tiles_n = cdiv(p.N, BN);
