@@ -76,22 +76,30 @@ __device__ __forceinline__ int mx_byte(const uint8_t* s, int64_t row, int kb32, 
   return kb32 < KB32 ? (int)s[row * KB32 + kb32] : 127;
 }
 
-// Workgroup id -> (tile_m, tile_n).  Hardware hands consecutive workgroup ids
-// to the 8 XCDs in turn; renumber so that each XCD receives a contiguous run,
-// then walk tiles in groups of GROUP_M tile rows so neighbours share A and W.
-__device__ __forceinline__ void tile_of(int pid, int tiles_m, int tiles_n, int& tm, int& tn) {
-  constexpr int GROUP_M = 8;
-  const int total = tiles_m * tiles_n;
+// Hardware hands consecutive workgroup ids to the 8 XCDs in turn.  Renumber
+// ids 0..total-1 so that each XCD receives a contiguous run (a bijection).
+__device__ __forceinline__ int xcd_contiguous(int pid, int total) {
   const int xcd = pid & 7, idx = pid >> 3;
   const int per = total >> 3, rem = total & 7;
-  pid = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + idx;
+  return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + idx;
+}
+
+// Tile index -> (tile_m, tile_n), walking groups of GROUP_M tile rows so that
+// consecutive indices share A rows and W rows.
+__device__ __forceinline__ void group_walk(int idx, int tiles_m, int tiles_n, int& tm, int& tn) {
+  constexpr int GROUP_M = 8;
   const int width = GROUP_M * tiles_n;
-  const int group = pid / width;
+  const int group = idx / width;
   const int first_m = group * GROUP_M;
   const int gsize = min(tiles_m - first_m, GROUP_M);
-  const int in_group = pid - group * width;
+  const int in_group = idx - group * width;
   tm = first_m + in_group % gsize;
   tn = in_group / gsize;
+}
+
+// Workgroup id -> (tile_m, tile_n): neighbouring tiles meet in one XCD's L2.
+__device__ __forceinline__ void tile_of(int pid, int tiles_m, int tiles_n, int& tm, int& tn) {
+  group_walk(xcd_contiguous(pid, tiles_m * tiles_n), tiles_m, tiles_n, tm, tn);
 }
 
 __device__ __forceinline__ void store_tile_bf16(const GemmArgs& p, const v4f& acc, int row0, int col,

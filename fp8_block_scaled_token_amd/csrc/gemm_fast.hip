@@ -3,30 +3,37 @@
 //
 // Same arithmetic as the generic kernels (block rescale per 128-wide K block,
 // per-tensor, or MX scales inside the MFMA; see gemm_kernels.hip), organised
-// for throughput:
-//  * 256 x 128 workgroup tile, 4 waves in a 2 x 2 grid, 128 x 64 per wave
-//    (8 x 4 MFMA tiles of 16 x 16): each K block a wave reads 12 operand
-//    fragments from LDS for 32 MFMAs.
+// for throughput on CDNA4:
+//  * Large workgroup tiles.  One K block of a BM x BN tile moves
+//    (BM + BN) * 128 bytes from L2 through the CU's vector cache into LDS;
+//    at the fp8 MFMA rate a 128 x 128 tile would need that path's whole
+//    bandwidth, a 256 x 256 tile needs half of it.  The big configuration
+//    is 256 x 256 with 8 waves (2 x 4, 128 x 64 per wave: 8 x 4 MFMA tiles),
+//    one workgroup per CU; the small one is 128 x 128 with 4 waves, two
+//    workgroups per CU, for shapes with few tiles.
 //  * Operands move global -> LDS with buffer_load ... lds (no VGPR staging).
 //    Such a load writes 16 bytes per lane to consecutive LDS addresses, so the
 //    XOR row swizzle of the LDS tile is produced by choosing, per lane, which
 //    16-byte chunk of global memory to fetch.  Rows past M or N fall outside
 //    the buffer descriptor and read as zero.
-//  * Three LDS stages: K block kb+2 streams in while kb is multiplied; one
-//    barrier per K block.
-//  * Workgroup ids are renumbered XCD-aware and walked in groups of tile rows
-//    (tile_of), so tiles sharing A rows or W rows meet in the same L2.
+//  * Two LDS stages, one barrier per K block; the loop body is a single basic
+//    block so the scheduler can interleave the block-mode rescale FMAs of one
+//    16-row tile with the MFMAs of the next.
+//  * Tail balancing: when the last round of tiles would leave at least half
+//    of the CUs idle, those tiles are split into two half-height tiles, which
+//    fill the machine and take half as long.
+//  * Workgroup ids are renumbered XCD-aware and tiles walked in groups of
+//    tile rows, so tiles sharing A rows or W rows meet in the same L2.
 // Preconditions (checked by the launcher): K % 128 == 0, every operand and
 // scale array smaller than 2^31 bytes, M > 64.
 #include <cstdlib>
+#include <utility>
 
 #include "gemm_common.h"
 
 namespace fp8q {
 
 namespace {
-
-constexpr int FBN = 128;                      // workgroup tile width (one weight-scale block)
 
 // Byte offset of 16-byte chunk c (0..7) of tile row r in a swizzled LDS tile.
 __device__ __forceinline__ int swz(int r, int c) { return (r << 7) | ((c ^ (r & 7)) << 4); }
@@ -53,19 +60,32 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // Written as inline assembly on purpose: the compiler cannot tell which LDS
 // stage a direct-to-LDS load fills, and would otherwise make every LDS read
 // wait for all of them.  These loads are therefore invisible to the
-// compiler's vmcnt bookkeeping; the kernel waits for them explicitly
-// (wait_vmcnt) and issues no other vector-memory loads inside its K loop.
-__device__ __forceinline__ void dma16(const i32x4& r, uint32_t lds, int voffset) {
+// compiler's vmcnt bookkeeping; the kernel waits for them explicitly and
+// issues no other vector-memory loads inside its K loop.
+__device__ __forceinline__ void dma16(const i32x4& r, uint32_t lds, uint32_t voffset) {
   asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
                : "v"(voffset), "s"(r), "s"(lds)
                : "memory", "m0");
 }
-__device__ __forceinline__ void dma4(const i32x4& r, uint32_t lds, int voffset) {
+__device__ __forceinline__ void dma4(const i32x4& r, uint32_t lds, uint32_t voffset) {
   asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds"
                :
                : "v"(voffset), "s"(r), "s"(lds)
                : "memory", "m0");
+}
+
+// Added to a load offset that must not read memory: every descriptor covers
+// fewer than 2^31 bytes, so the load falls out of range and writes zeros.
+constexpr uint32_t OOB = 0x80000000u;
+
+template <int... I, typename F>
+__device__ __forceinline__ void static_for_impl(std::integer_sequence<int, I...>, F&& f) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(std::make_integer_sequence<int, N>{}, f);
 }
 
 template <int N>
@@ -74,36 +94,54 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
+// Wait until at most N of this wave's global loads are in flight and all of
+// its LDS reads have returned, then a workgroup barrier.  One asm statement
+// with a memory clobber, so no LDS access moves across it.  (A
+// __syncthreads() fence would wait for every global load.)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+
 }  // namespace
 
-// BM x 128 workgroup tile, NW waves in a WM x (NW/WM) grid, NS LDS stages
-// (each stage one LDS object: A tile, W tile, scale words).
-template <int MODE, int BM, int NW, int NS>
-__global__ __launch_bounds__(NW * 64) void gemm_fast_kernel(GemmArgs p) {
-  constexpr int BN = FBN;
-  constexpr int WM = (NW == 8 && BM == 256) ? 4 : 2, WN = NW / WM;
-  constexpr int WTM = BM / WM, WTN = BN / WN;          // wave tile
-  constexpr int TM = WTM / 16, TN = WTN / 16;
-  constexpr int ABYTES = BM * 128, WBYTES = BN * 128;  // one K block of A / W
-  constexpr int A_PER = (ABYTES / 1024) / NW;          // 1 KB DMA instructions per wave
-  constexpr int W_PER = (WBYTES / 1024) / NW;
-  constexpr int RA = BM / NW, RW = BN / NW;            // scale rows per wave
-  constexpr int S_WORDS_NW = 128 * NW;                 // A scales, then W scales / copies
-  constexpr int STAGE_BYTES = ABYTES + WBYTES + S_WORDS_NW * 4;
-  static_assert(A_PER >= 1 && W_PER >= 1 && RA <= 64 && RW <= 64, "tile too small for NW waves");
+// Geometry of one fast-kernel configuration: BM x BN workgroup tile, WM x WN
+// waves.  Stage layout in LDS (2 stages): A tile [BM][128] and W tile
+// [BN][128], both swizzled; then 64 A-scale words per wave, then 64 W-scale
+// words per wave.
+template <int MODE_, int BM_, int BN_, int WM_, int WN_>
+struct FastTile {
+  static constexpr int MODE = MODE_, BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int NW = WM * WN;
+  static constexpr int WTN = BN / WN, TN = WTN / 16;
+  static constexpr int ABYTES = BM * 128, WBYTES = BN * 128;
+  static constexpr int A_PER = ABYTES / 1024 / NW;  // 1 KB loads per wave per stage
+  static constexpr int W_PER = WBYTES / 1024 / NW;
+  static constexpr int SA_OFF = ABYTES + WBYTES;
+  static constexpr int SW_OFF = SA_OFF + NW * 256;
+  static constexpr int STAGE = SW_OFF + NW * 256;
+  static constexpr int NS = 2;
+  static_assert(BM == 32 * NW && BN == 32 * NW, "each wave fetches the scales of 32 rows");
+  static_assert(A_PER * NW * 1024 == ABYTES && W_PER * NW * 1024 == WBYTES, "whole 1 KB loads");
   static_assert(WTN <= 128 && 128 % WTN == 0, "one weight-scale block per wave");
-  static_assert(NS >= 2 && NS <= 4, "2..4 stages");
-  __shared__ __attribute__((aligned(1024))) uint8_t st0[STAGE_BYTES], st1[STAGE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t st2[NS > 2 ? STAGE_BYTES : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t st3[NS > 3 ? STAGE_BYTES : 16];
+  static_assert(STAGE % 1024 == 0, "stages stay 1 KB aligned");
+};
 
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+// One tile: rows [m0, m0 + RM) x columns [n0, n0 + BN), RM = BM (full) or
+// BM / 2 (HALF).
+template <class T, bool HALF>
+__device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int m0, int n0) {
+  constexpr int MODE = T::MODE, BN = T::BN, WN = T::WN;
+  constexpr int RM = HALF ? T::BM / 2 : T::BM;
+  constexpr int WTM = RM / T::WM, TM = WTM / 16, WTN = T::WTN, TN = T::TN;
+  constexpr int A_PER = T::A_PER, W_PER = T::W_PER, STAGE = T::STAGE;
+  constexpr int ABYTES = T::ABYTES, SA_OFF = T::SA_OFF, SW_OFF = T::SW_OFF;
+  static_assert(TM >= 1, "wave tile at least 16 rows");
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WN, wn = wave % WN;
-  int tm, tn;
-  tile_of(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
 
   const i32x4 rA = rsrc(p.a, (int64_t)p.M * p.lda);
   const i32x4 rW = rsrc(p.w, (int64_t)p.N * p.ldw);
@@ -112,54 +150,54 @@ __global__ __launch_bounds__(NW * 64) void gemm_fast_kernel(GemmArgs p) {
   const i32x4 rSW =
       rsrc(p.sw, MODE == MODE_MX ? (int64_t)p.N * p.KB32 : (MODE == MODE_BLOCK ? (int64_t)p.NB * p.KB * 4 : 4));
 
-  // DMA source offsets.  DMA instruction i of wave w fills LDS kilobyte
-  // A_PER*w + i, i.e. tile rows 8*(A_PER*w + i) + lane/8 with lane % 8 the
-  // physical chunk; the logical chunk to fetch is (lane % 8) ^ (row % 8) =
-  // (lane % 8) ^ (lane / 8).
+  // Load i of wave w fills LDS kilobyte (A_PER*w + i) of the A tile, i.e.
+  // tile rows 8*(A_PER*w + i) + lane/8 with lane % 8 the physical chunk; the
+  // logical chunk to fetch is (lane % 8) ^ (row % 8) = (lane % 8) ^ (lane / 8).
+  // A half tile needs only its first RM rows: the other loads are kept (for
+  // the vmcnt count) but read nothing.
   const int lrow = lane >> 3, lchunk = (lane & 7) ^ (lane >> 3);
   const int offA = (m0 + 8 * A_PER * wave + lrow) * (int)p.lda + lchunk * 16;
   const int offW = (n0 + 8 * W_PER * wave + lrow) * (int)p.ldw + lchunk * 16;
   const int lda8 = 8 * (int)p.lda, ldw8 = 8 * (int)p.ldw;
-  // scale rows: lane l of wave w fetches A row RA*w + l % RA (word 64w + l),
-  // and (MX) W row RW*w + l % RW (word 64*NW + 64w + l)
-  const int srow = m0 + RA * wave + (lane % RA);
-  const int swrow = n0 + RW * wave + (lane % RW);
-  const int wblk = n0 / 128;
+  // scales: lane l of wave w fetches A row 32w + l % 32 (and, MX, W row
+  // 32w + l % 32) into scale word 64w + l; block mode: W block n0/128 + l % NBLK
+  constexpr int NBLK = BN / 128 > 0 ? BN / 128 : 1;
+  const int srow = m0 + 32 * wave + (lane & 31);
+  const int swrow = n0 + 32 * wave + (lane & 31);
+  const int sa_row = p.sa_col_major ? srow : srow * p.KB;   // block-mode A scale (row, kb)
+  const int sa_kstride = p.sa_col_major ? p.M : 1;
+  const int wblk = n0 / 128 + lane % NBLK;
+  const uint32_t smem_base = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 
-  auto stage = [&](auto S) -> uint8_t* {
-    if constexpr (decltype(S)::value == 0) return st0;
-    else if constexpr (decltype(S)::value == 1) return st1;
-    else if constexpr (decltype(S)::value == 2) return st2;
-    else return st3;
-  };
-  auto stage_s = [&](auto S) -> uint32_t* { return reinterpret_cast<uint32_t*>(stage(S) + ABYTES + WBYTES); };
-
-  // DMA instructions per wave per stage (the vmcnt bookkeeping relies on it)
-  constexpr int NLOAD = A_PER + W_PER + (MODE == MODE_TENSOR ? 0 : 2);
-
-  auto issue = [&](auto S, int kb) {
-    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(stage(S)));
+  // Fill stage `st` with K block kb.  Past the last block the loads are kept
+  // (so every step issues the same number) but read nothing and write zeros
+  // into the free stage.
+  auto issue = [&](int st, int kb) {
+    const bool valid = kb < p.KB;
+    const uint32_t oob = valid ? 0u : OOB;
+    const uint32_t base = smem_base + st * STAGE;
     const uint32_t a = base + wave * A_PER * 1024;
     const uint32_t w = base + ABYTES + wave * W_PER * 1024;
-    const uint32_t sc = base + ABYTES + WBYTES + wave * 256;
-    const int kofs = kb * 128;
+    const int kofs = valid ? kb * 128 : 0;
 #pragma unroll
-    for (int i = 0; i < A_PER; ++i) dma16(rA, a + i * 1024, offA + i * lda8 + kofs);
+    for (int i = 0; i < A_PER; ++i) {
+      const bool live = !HALF || (A_PER * wave + i) * 8 < RM;
+      dma16(rA, a + i * 1024, (uint32_t)(offA + i * lda8 + kofs) + (live ? oob : OOB));
+    }
 #pragma unroll
-    for (int i = 0; i < W_PER; ++i) dma16(rW, w + i * 1024, offW + i * ldw8 + kofs);
+    for (int i = 0; i < W_PER; ++i) dma16(rW, w + i * 1024, (uint32_t)(offW + i * ldw8 + kofs) + oob);
+    const int kbv = valid ? kb : 0;
+    const uint32_t sa_lds = base + SA_OFF + wave * 256, sw_lds = base + SW_OFF + wave * 256;
     if constexpr (MODE == MODE_BLOCK) {
-      const int e = p.sa_col_major ? kb * p.M + srow : srow * p.KB + kb;
-      dma4(rSA, sc, e * 4);
-      // the tile's weight-block scale, same address in every lane
-      dma4(rSW, sc + 256 * NW, (wblk * p.KB + kb) * 4);
+      dma4(rSA, sa_lds, (uint32_t)((sa_row + kbv * sa_kstride) * 4) + oob);
+      dma4(rSW, sw_lds, (uint32_t)((wblk * p.KB + kbv) * 4) + oob);
     } else if constexpr (MODE == MODE_MX) {
-      dma4(rSA, sc, srow * p.KB32 + kb * 4);
-      dma4(rSW, sc + 256 * NW, swrow * p.KB32 + kb * 4);
+      dma4(rSA, sa_lds, (uint32_t)(srow * p.KB32 + kbv * 4) + oob);
+      dma4(rSW, sw_lds, (uint32_t)(swrow * p.KB32 + kbv * 4) + oob);
     }
   };
-  // word index of A-scale row r / W-scale row c within a stage's scale words
-  auto sa_word = [](int r) { return 64 * (r / RA) + (r % RA); };
-  auto sw_word = [](int c) { return 64 * NW + 64 * (c / RW) + (c % RW); };
+  // scale word of tile row r / tile column c
+  auto s_word = [](int r) { return 64 * (r >> 5) + (r & 31); };
 
   v4f acc[TM][TN];
 #pragma unroll
@@ -175,34 +213,66 @@ __global__ __launch_bounds__(NW * 64) void gemm_fast_kernel(GemmArgs p) {
     return f;
   };
 
-  auto compute = [&](auto S) {
-    const uint8_t* a = stage(S);
-    const uint8_t* w = stage(S) + ABYTES;
-    const uint32_t* s = stage_s(S);
+  // Block mode rescale, software-pipelined: the MFMAs of 16-row tile i give
+  // P (fp32 partial products of this K block); P is folded into the
+  // accumulators (acc += P * s_a * s_w) while the MFMAs of tile i + 1 run.
+  // The last tile's P is folded at the start of the next K block (or before
+  // the epilogue).
+  v4f Pq[TN];
+  float scq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < TN; ++j) Pq[j] = v4f{0.f, 0.f, 0.f, 0.f};
+  auto fold = [&](auto I) {
+    constexpr int i = decltype(I)::value;
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(Pq[j][r], scq[r], acc[i][j][r]);
+  };
+
+  const int arow = wm * WTM + (lane & 15);           // fragment row of 16-row tile 0
+  const int brow = wn * WTN + (lane & 15);
+  auto compute = [&](int st) {
+    const uint8_t* a = smem + st * STAGE;
+    const uint8_t* w = a + ABYTES;
+    const uint32_t* sa = reinterpret_cast<const uint32_t*>(a + SA_OFF);
+    const uint32_t* sw = reinterpret_cast<const uint32_t*>(a + SW_OFF);
     Frag fb[TN];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) fb[j] = read_frag(w, wn * WTN + 16 * j + (lane & 15));
+    for (int j = 0; j < TN; ++j) fb[j] = read_frag(w, brow + 16 * j);
     if constexpr (MODE == MODE_BLOCK) {
-      const float swv = __uint_as_float(s[64 * NW + wave * 64]);
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const Frag fa = read_frag(a, wm * WTM + 16 * i + (lane & 15));
-        // rows 4*(lane/16) + r of this 16-row tile are consecutive scale words
-        const int r0 = wm * WTM + 16 * i + 4 * (lane >> 4);
-        const uint4 sx4 = *reinterpret_cast<const uint4*>(s + sa_word(r0));
-        const float sc[4] = {__uint_as_float(sx4.x) * swv, __uint_as_float(sx4.y) * swv,
-                             __uint_as_float(sx4.z) * swv, __uint_as_float(sx4.w) * swv};
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const v4f P = mfma_plain(fa.v, fb[j].v, v4f{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(P[r], sc[r], acc[i][j][r]);
+      const float swv = __uint_as_float(sw[wave * 64 + (wn * WTN) / 128]);
+      // rows 4*(lane/16) + r of a 16-row tile are consecutive scale words
+      const int srow0 = wm * WTM + 4 * (lane >> 4);
+      Frag fa = read_frag(a, arow);
+      uint4 sx4 = *reinterpret_cast<const uint4*>(sa + s_word(srow0));
+      static_for<TM>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        Frag fn;
+        uint4 sxn;
+        if constexpr (i + 1 < TM) {
+          fn = read_frag(a, arow + 16 * (i + 1));
+          sxn = *reinterpret_cast<const uint4*>(sa + s_word(srow0 + 16 * (i + 1)));
         }
-      }
+        v4f Pn[TN];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) Pn[j] = mfma_plain(fa.v, fb[j].v, v4f{0.f, 0.f, 0.f, 0.f});
+        fold(std::integral_constant<int, (i == 0 ? TM - 1 : i - 1)>{});
+#pragma unroll
+        for (int j = 0; j < TN; ++j) Pq[j] = Pn[j];
+        scq[0] = __uint_as_float(sx4.x) * swv;
+        scq[1] = __uint_as_float(sx4.y) * swv;
+        scq[2] = __uint_as_float(sx4.z) * swv;
+        scq[3] = __uint_as_float(sx4.w) * swv;
+        if constexpr (i + 1 < TM) {
+          fa = fn;
+          sx4 = sxn;
+        }
+      });
     } else if constexpr (MODE == MODE_TENSOR) {
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        const Frag fa = read_frag(a, wm * WTM + 16 * i + (lane & 15));
+        const Frag fa = read_frag(a, arow + 16 * i);
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = mfma_plain(fa.v, fb[j].v, acc[i][j]);
       }
@@ -210,57 +280,33 @@ __global__ __launch_bounds__(NW * 64) void gemm_fast_kernel(GemmArgs p) {
       const int sh = 8 * (lane >> 4);
       int swb[TN];
 #pragma unroll
-      for (int j = 0; j < TN; ++j) swb[j] = (s[sw_word(wn * WTN + 16 * j + (lane & 15))] >> sh) & 0xFF;
+      for (int j = 0; j < TN; ++j) swb[j] = (sw[s_word(brow + 16 * j)] >> sh) & 0xFF;
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        const Frag fa = read_frag(a, wm * WTM + 16 * i + (lane & 15));
-        const int sab = (s[sa_word(wm * WTM + 16 * i + (lane & 15))] >> sh) & 0xFF;
+        const Frag fa = read_frag(a, arow + 16 * i);
+        const int sab = (sa[s_word(arow + 16 * i)] >> sh) & 0xFF;
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = mfma_mx(fa.v, fb[j].v, acc[i][j], sab, swb[j]);
       }
     }
   };
 
-  // step kb: stage S = kb % NS holds block kb.  Blocks kb+1 .. kb+NS-2 may
-  // still be in flight; block kb+NS-1 is issued into the stage freed by kb-1.
-  auto step = [&](auto S, auto S_issue, int kb) {
-    const int ahead = min(p.KB - 1 - kb, NS - 2);     // blocks issued after kb
-    if constexpr (NS == 2) {
-      wait_vmcnt<0>();
-    } else if constexpr (NS == 3) {
-      if (ahead >= 1) wait_vmcnt<NLOAD>(); else wait_vmcnt<0>();
-    } else {
-      if (ahead >= 2) wait_vmcnt<2 * NLOAD>(); else if (ahead == 1) wait_vmcnt<NLOAD>(); else wait_vmcnt<0>();
-    }
-    // plain s_barrier: a __syncthreads() fence would wait for every load in flight
-    __builtin_amdgcn_s_barrier();
-    if (kb + NS - 1 < p.KB) issue(S_issue, kb + NS - 1);
-    compute(S);
-  };
-
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  using S2 = std::integral_constant<int, 2>;
-  using S3 = std::integral_constant<int, 3>;
-
-  issue(S0{}, 0);
-  if (NS > 2 && p.KB > 1) issue(S1{}, 1);
-  if (NS > 3 && p.KB > 2) issue(S2{}, 2);
-  for (int kb = 0; kb < p.KB; kb += NS) {
-    if constexpr (NS == 2) {
-      step(S0{}, S1{}, kb);
-      if (kb + 1 < p.KB) step(S1{}, S0{}, kb + 1);
-    } else if constexpr (NS == 3) {
-      step(S0{}, S2{}, kb);
-      if (kb + 1 < p.KB) step(S1{}, S0{}, kb + 1);
-      if (kb + 2 < p.KB) step(S2{}, S1{}, kb + 2);
-    } else {
-      step(S0{}, S3{}, kb);
-      if (kb + 1 < p.KB) step(S1{}, S0{}, kb + 1);
-      if (kb + 2 < p.KB) step(S2{}, S1{}, kb + 2);
-      if (kb + 3 < p.KB) step(S3{}, S2{}, kb + 3);
-    }
+  // Main loop, one K block per iteration: wait for this wave's loads of
+  // block kb, barrier (every wave's part of block kb has landed and no wave
+  // still reads the stage of block kb-1), refill that stage with block kb+1,
+  // multiply block kb.
+  static_assert(T::NS == 2, "the wait count below assumes two stages");
+  issue(0, 0);
+  int cs = 0;
+  for (int kb = 0; kb < p.KB; ++kb) {
+    wait_vmcnt_barrier<0>();
+    issue(cs ^ 1, kb + 1);
+    compute(cs);
+    cs ^= 1;
   }
+  // the predicated-off loads still write LDS: let them land before exit
+  wait_vmcnt<0>();
+  if constexpr (MODE == MODE_BLOCK) fold(std::integral_constant<int, TM - 1>{});
 
   float mul = 1.0f;
   if (MODE == MODE_TENSOR)
@@ -275,46 +321,121 @@ __global__ __launch_bounds__(NW * 64) void gemm_fast_kernel(GemmArgs p) {
   }
 }
 
-// Tile configuration: 0 = 256x128 tile, 8 waves, 3 stages (one workgroup
-// per CU); 1 = 128x128 tile, 4 waves, 2 stages (two workgroups per CU, whose
-// independent barriers overlap).  Measured on MI355X: 1 is faster for the
-// block and per-tensor modes, 0 for MX.  FP8Q_GEMM_CFG overrides (tuning).
-static int gemm_fast_cfg(int mode) {
-  static const int forced = [] {
-    const char* e = getenv("FP8Q_GEMM_CFG");
-    return e ? atoi(e) : -1;
-  }();
-  if (forced == 0 || forced == 1) return forced;
-  return mode == MODE_MX ? 0 : 1;
+// Workgroups [0, full) take whole tiles (in XCD-contiguous group order);
+// the remaining tiles of that order are split into two half-height tiles,
+// one per workgroup.
+template <class T>
+__global__ __launch_bounds__(T::NW * 64) void gemm_fast_kernel(GemmArgs p, int full) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[T::NS * T::STAGE];
+  const int total = p.tiles_m * p.tiles_n;
+  const int b = blockIdx.x;
+  int tm, tn;
+  if (b < full) {
+    group_walk(xcd_contiguous(b, full), p.tiles_m, p.tiles_n, tm, tn);
+    fast_tile<T, false>(p, smem, tm * T::BM, tn * T::BN);
+  } else {
+    const int h = xcd_contiguous(b - full, 2 * (total - full));
+    group_walk(full + (h >> 1), p.tiles_m, p.tiles_n, tm, tn);
+    fast_tile<T, true>(p, smem, tm * T::BM + (h & 1) * (T::BM / 2), tn * T::BN);
+  }
 }
 
-static int cfg_bm(int cfg) { return cfg == 1 ? 128 : 256; }
+namespace {
 
-bool gemm_fast_eligible(const GemmArgs& p, int mode) {
-  const int bm = cfg_bm(gemm_fast_cfg(mode));
-  const int64_t a_bytes = (int64_t)p.M * p.lda + bm * p.lda;     // + rows past M of the last tile
-  const int64_t w_bytes = (int64_t)p.N * p.ldw + FBN * p.ldw;
-  const int64_t lim = (int64_t(1) << 31) - 1;
-  return p.M > 64 && p.K % 128 == 0 && a_bytes < lim && w_bytes < lim &&
-         (int64_t)(p.M + bm) * p.KB * 4 < lim && (int64_t)(p.M + bm) * p.KB32 < lim &&
-         (int64_t)(p.N + FBN) * p.KB32 < lim;
+// Configuration 0: 256 x 256 tiles, 8 waves, one workgroup per CU.
+// Configuration 1: 128 x 128 tiles, 4 waves, two workgroups per CU.
+// Tuning and test overrides, read at every call: FP8Q_GEMM_CFG=0/1 forces a
+// configuration, FP8Q_GEMM_SPLIT=0 disables the half-tile tail balancing,
+// FP8Q_GEMM_SLOTS=n plans for n CUs instead of the device's count.
+int env_int(const char* name, int dflt) {
+  const char* e = getenv(name);
+  return e ? atoi(e) : dflt;
+}
+
+int cu_count() {
+  const int forced = env_int("FP8Q_GEMM_SLOTS", 0);
+  if (forced > 0) return forced;
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+
+struct Plan {
+  int cfg;       // 0 = 256 x 256, 1 = 128 x 128
+  int tiles_m, tiles_n;
+  int full;      // workgroups that take whole tiles
+  int grid;
+};
+
+// Tiles of one configuration and how many of them to split: when the last
+// round would occupy at most half of the workgroup slots, split it.
+Plan plan_cfg(const GemmArgs& p, int cfg, int slots, bool split) {
+  const int bm = cfg == 0 ? 256 : 128, bn = bm;
+  Plan pl;
+  pl.cfg = cfg;
+  pl.tiles_m = (p.M + bm - 1) / bm;
+  pl.tiles_n = (p.N + bn - 1) / bn;
+  const int total = pl.tiles_m * pl.tiles_n;
+  const int rem = total % slots;
+  const int tail = (split && total > slots && rem > 0 && 2 * rem <= slots) ? rem : 0;
+  pl.full = total - tail;
+  pl.grid = total + tail;
+  return pl;
+}
+
+// Estimated time in units of one 256 x 256 tile on one CU; the 128 x 128
+// configuration runs two tiles per CU at a lower MFMA efficiency.
+double plan_cost(const Plan& pl, int cus) {
+  const int slots = pl.cfg == 0 ? cus : 2 * cus;
+  const int total = pl.tiles_m * pl.tiles_n;
+  const int tail = total - pl.full;
+  const double rounds = (pl.full + slots - 1) / slots + (tail > 0 ? 0.5 : 0.0);
+  const double per_round = pl.cfg == 0 ? 1.0 : 0.5 / 0.8;
+  return rounds * per_round;
+}
+
+Plan choose_plan(const GemmArgs& p) {
+  const int forced = env_int("FP8Q_GEMM_CFG", -1);
+  const bool split = env_int("FP8Q_GEMM_SPLIT", 1) != 0;
+  const int cus = cu_count();
+  const Plan big = plan_cfg(p, 0, cus, split), small = plan_cfg(p, 1, 2 * cus, split);
+  if (forced == 0) return big;
+  if (forced == 1) return small;
+  return plan_cost(big, cus) <= plan_cost(small, cus) ? big : small;
 }
 
 template <int MODE>
-static void launch_cfg(const GemmArgs& p, int cfg, hipStream_t stream) {
-  const dim3 grid(p.tiles_m * p.tiles_n);
-  if (cfg == 1) hipLaunchKernelGGL((gemm_fast_kernel<MODE, 128, 4, 2>), grid, dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL((gemm_fast_kernel<MODE, 256, 8, 3>), grid, dim3(512), 0, stream, p);
+void launch_plan(GemmArgs p, const Plan& pl, hipStream_t stream) {
+  p.tiles_m = pl.tiles_m;
+  p.tiles_n = pl.tiles_n;
+  if (pl.cfg == 0) {
+    using T = FastTile<MODE, 256, 256, 2, 4>;
+    hipLaunchKernelGGL(gemm_fast_kernel<T>, dim3(pl.grid), dim3(T::NW * 64), 0, stream, p, pl.full);
+  } else {
+    using T = FastTile<MODE, 128, 128, 2, 2>;
+    hipLaunchKernelGGL(gemm_fast_kernel<T>, dim3(pl.grid), dim3(T::NW * 64), 0, stream, p, pl.full);
+  }
+}
+
+}  // namespace
+
+bool gemm_fast_eligible(const GemmArgs& p, int /*mode*/) {
+  const int bm = 256, bn = 256;  // the larger configuration bounds both
+  const int64_t a_bytes = (int64_t)p.M * p.lda + bm * p.lda;     // + rows past M of the last tile
+  const int64_t w_bytes = (int64_t)p.N * p.ldw + bn * p.ldw;
+  const int64_t lim = (int64_t(1) << 31) - 1;
+  return p.M > 64 && p.K % 128 == 0 && a_bytes < lim && w_bytes < lim &&
+         (int64_t)(p.M + bm) * p.KB * 4 < lim && (int64_t)(p.M + bm) * p.KB32 < lim &&
+         (int64_t)(p.N + bn) * p.KB32 < lim && (int64_t)(p.NB + 2) * p.KB * 4 < lim;
 }
 
 hipError_t launch_gemm_fast(GemmArgs p, int mode, hipStream_t stream) {
-  const int cfg = gemm_fast_cfg(mode);
-  const int bm = cfg_bm(cfg);
-  p.tiles_m = (p.M + bm - 1) / bm;
-  p.tiles_n = (p.N + FBN - 1) / FBN;
-  if (mode == MODE_BLOCK) launch_cfg<MODE_BLOCK>(p, cfg, stream);
-  else if (mode == MODE_TENSOR) launch_cfg<MODE_TENSOR>(p, cfg, stream);
-  else launch_cfg<MODE_MX>(p, cfg, stream);
+  const Plan pl = choose_plan(p);
+  if (mode == MODE_BLOCK) launch_plan<MODE_BLOCK>(p, pl, stream);
+  else if (mode == MODE_TENSOR) launch_plan<MODE_TENSOR>(p, pl, stream);
+  else launch_plan<MODE_MX>(p, pl, stream);
   return hipGetLastError();
 }
 
