@@ -122,20 +122,23 @@ def main() -> int:
         elif name == "pertensor":
             s["s"] = sx_static
         else:
-            s["s"] = torch.empty(M, KB, dtype=torch.float32, device="cuda")
+            s["s"] = torch.empty(KB, M, dtype=torch.float32, device="cuda")
         s["y"] = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
         sets.append(s)
     del xg
 
+    # activation group scales travel column-major ([K/128, M]): a K block's
+    # scales for consecutive rows are contiguous, one cache line per 32 rows
+    # for the GEMM (the row-major form costs a line per row)
     def quant(s):
         if wl.norm:
-            fq.fp8q_rmsnorm_quant(s["x"], gamma, d["eps"], fq.ROW_MAJOR, s["q"], s["s"])
+            fq.fp8q_rmsnorm_quant(s["x"], gamma, d["eps"], fq.COL_MAJOR, s["q"], s["s"])
         elif name == "mx":
             fq.fp8q_quant_act_group(s["x"], 32, fq.SCALE_UE8M0, fq.ROW_MAJOR, None, s["q"], s["s"])
         elif name == "pertensor":
             fq.fp8q_quant_act_group(s["x"], 128, fq.SCALE_F32, fq.ROW_MAJOR, sx_static, s["q"], None)
         else:
-            fq.fp8q_quant_act_group(s["x"], 128, fq.SCALE_F32, fq.ROW_MAJOR, None, s["q"], s["s"])
+            fq.fp8q_quant_act_group(s["x"], 128, fq.SCALE_F32, fq.COL_MAJOR, None, s["q"], s["s"])
 
     def gemm(s):
         if name == "mx":
@@ -143,7 +146,7 @@ def main() -> int:
         elif name == "pertensor":
             fq.fp8q_gemm_blockscale(s["q"], s["s"], fq.ROW_MAJOR, qw, sw, None, s["y"], fq.GRAN_PER_TENSOR)
         else:
-            fq.fp8q_gemm_blockscale(s["q"], s["s"], fq.ROW_MAJOR, qw, sw, None, s["y"], fq.GRAN_BLOCK128)
+            fq.fp8q_gemm_blockscale(s["q"], s["s"], fq.COL_MAJOR, qw, sw, None, s["y"], fq.GRAN_BLOCK128)
 
     for i in range(args.warmup):
         s = sets[i % nsets]

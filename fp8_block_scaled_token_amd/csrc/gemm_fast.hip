@@ -31,6 +31,12 @@
 
 #include "gemm_common.h"
 
+// K blocks between an L2 prefetch touch and the operand loads it serves
+// (0 disables the touches).
+#ifndef FP8Q_PREFETCH_DISTANCE
+#define FP8Q_PREFETCH_DISTANCE 3
+#endif
+
 namespace fp8q {
 
 namespace {
@@ -110,9 +116,12 @@ __device__ __forceinline__ void wait_vmcnt_barrier() {
 // waves.  Stage layout in LDS (2 stages): A tile [BM][128] and W tile
 // [BN][128], both swizzled; then 64 A-scale words per wave, then 64 W-scale
 // words per wave.
-template <int MODE_, int BM_, int BN_, int WM_, int WN_>
+template <int MODE_, int BM_, int BN_, int WM_, int WN_, int NTN_>
 struct FastTile {
   static constexpr int MODE = MODE_, BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  // tile columns of one XCD's concurrently running group of tiles (the XCD's
+  // workgroup slots divided by the group height of group_walk)
+  static constexpr int NTN = NTN_;
   static constexpr int NW = WM * WN;
   static constexpr int WTN = BN / WN, TN = WTN / 16;
   static constexpr int ABYTES = BM * 128, WBYTES = BN * 128;
@@ -122,6 +131,8 @@ struct FastTile {
   static constexpr int SW_OFF = SA_OFF + NW * 256;
   static constexpr int STAGE = SW_OFF + NW * 256;
   static constexpr int NS = 2;
+  static constexpr int PF_OFF = NS * STAGE;            // 256 bytes per wave: prefetch sink
+  static constexpr int LDS_BYTES = PF_OFF + NW * 256;
   static_assert(BM == 32 * NW && BN == 32 * NW, "each wave fetches the scales of 32 rows");
   static_assert(A_PER * NW * 1024 == ABYTES && W_PER * NW * 1024 == WBYTES, "whole 1 KB loads");
   static_assert(WTN <= 128 && 128 % WTN == 0, "one weight-scale block per wave");
@@ -131,7 +142,7 @@ struct FastTile {
 // One tile: rows [m0, m0 + RM) x columns [n0, n0 + BN), RM = BM (full) or
 // BM / 2 (HALF).
 template <class T, bool HALF>
-__device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int m0, int n0) {
+__device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int m0, int n0, int gm, int gn) {
   constexpr int MODE = T::MODE, BN = T::BN, WN = T::WN;
   constexpr int RM = HALF ? T::BM / 2 : T::BM;
   constexpr int WTM = RM / T::WM, TM = WTM / 16, WTN = T::WTN, TN = T::TN;
@@ -196,6 +207,26 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
       dma4(rSW, sw_lds, (uint32_t)(swrow * p.KB32 + kbv * 4) + oob);
     }
   };
+  // L2 prefetch.  Tiles running together on one XCD share operand rows: the
+  // NTN tiles of a tile row read the same A rows, the 8 tiles of a tile
+  // column (group_walk's group height) the same W rows.  Every workgroup
+  // touches one line (the 128 bytes of a K block) of its share of those rows,
+  // PFD K blocks ahead, so that the operand loads find them in L2.  The
+  // touches go to a per-wave LDS sink; they are issued after the operand
+  // loads of a step and may stay in flight until the next step's wait.
+  constexpr int PFD = FP8Q_PREFETCH_DISTANCE;
+  constexpr int PA = RM / T::NTN / T::NW, PW = BN / 8 / T::NW;   // rows per wave
+  static_assert(PA >= 1 && PA <= 64 && PW >= 1 && PW <= 64, "prefetch slice");
+  const uint32_t pfa = (uint32_t)(m0 + gn * (RM / T::NTN) + wave * PA + lane) * (uint32_t)p.lda;
+  const uint32_t pfw = (uint32_t)(n0 + gm * (BN / 8) + wave * PW + lane) * (uint32_t)p.ldw;
+  const uint32_t pf_lds = smem_base + T::PF_OFF + wave * 256;
+  auto prefetch = [&](int kb) {
+    const bool valid = PFD > 0 && kb < p.KB;
+    const uint32_t kofs = valid ? (uint32_t)kb * 128u : 0u;
+    dma4(rA, pf_lds, (valid && lane < PA) ? pfa + kofs : OOB);
+    dma4(rW, pf_lds, (valid && lane < PW) ? pfw + kofs : OOB);
+  };
+
   // scale word of tile row r / tile column c
   auto s_word = [](int r) { return 64 * (r >> 5) + (r & 31); };
 
@@ -270,24 +301,24 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
         }
       });
     } else if constexpr (MODE == MODE_TENSOR) {
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
+      static_for<TM>([&](auto I) {
+        constexpr int i = decltype(I)::value;
         const Frag fa = read_frag(a, arow + 16 * i);
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = mfma_plain(fa.v, fb[j].v, acc[i][j]);
-      }
+      });
     } else {
       const int sh = 8 * (lane >> 4);
       int swb[TN];
 #pragma unroll
       for (int j = 0; j < TN; ++j) swb[j] = (sw[s_word(brow + 16 * j)] >> sh) & 0xFF;
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
+      static_for<TM>([&](auto I) {
+        constexpr int i = decltype(I)::value;
         const Frag fa = read_frag(a, arow + 16 * i);
         const int sab = (sa[s_word(arow + 16 * i)] >> sh) & 0xFF;
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = mfma_mx(fa.v, fb[j].v, acc[i][j], sab, swb[j]);
-      }
+      });
     }
   };
 
@@ -295,12 +326,15 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
   // block kb, barrier (every wave's part of block kb has landed and no wave
   // still reads the stage of block kb-1), refill that stage with block kb+1,
   // multiply block kb.
+  // The two prefetch touches issued after a step's loads may stay in flight.
   static_assert(T::NS == 2, "the wait count below assumes two stages");
   issue(0, 0);
+  prefetch(PFD - 1);
   int cs = 0;
   for (int kb = 0; kb < p.KB; ++kb) {
-    wait_vmcnt_barrier<0>();
+    wait_vmcnt_barrier<2>();
     issue(cs ^ 1, kb + 1);
+    prefetch(kb + PFD);
     compute(cs);
     cs ^= 1;
   }
@@ -326,17 +360,17 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
 // one per workgroup.
 template <class T>
 __global__ __launch_bounds__(T::NW * 64) void gemm_fast_kernel(GemmArgs p, int full) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[T::NS * T::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES];
   const int total = p.tiles_m * p.tiles_n;
   const int b = blockIdx.x;
   int tm, tn;
   if (b < full) {
     group_walk(xcd_contiguous(b, full), p.tiles_m, p.tiles_n, tm, tn);
-    fast_tile<T, false>(p, smem, tm * T::BM, tn * T::BN);
+    fast_tile<T, false>(p, smem, tm * T::BM, tn * T::BN, tm % 8, tn % T::NTN);
   } else {
     const int h = xcd_contiguous(b - full, 2 * (total - full));
     group_walk(full + (h >> 1), p.tiles_m, p.tiles_n, tm, tn);
-    fast_tile<T, true>(p, smem, tm * T::BM + (h & 1) * (T::BM / 2), tn * T::BN);
+    fast_tile<T, true>(p, smem, tm * T::BM + (h & 1) * (T::BM / 2), tn * T::BN, tm % 8, tn % T::NTN);
   }
 }
 
@@ -411,10 +445,10 @@ void launch_plan(GemmArgs p, const Plan& pl, hipStream_t stream) {
   p.tiles_m = pl.tiles_m;
   p.tiles_n = pl.tiles_n;
   if (pl.cfg == 0) {
-    using T = FastTile<MODE, 256, 256, 2, 4>;
+    using T = FastTile<MODE, 256, 256, 2, 4, 4>;
     hipLaunchKernelGGL(gemm_fast_kernel<T>, dim3(pl.grid), dim3(T::NW * 64), 0, stream, p, pl.full);
   } else {
-    using T = FastTile<MODE, 128, 128, 2, 2>;
+    using T = FastTile<MODE, 128, 128, 2, 2, 8>;
     hipLaunchKernelGGL(gemm_fast_kernel<T>, dim3(pl.grid), dim3(T::NW * 64), 0, stream, p, pl.full);
   }
 }

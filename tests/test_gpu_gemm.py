@@ -176,11 +176,12 @@ def _full_size(name, rows_sample):
     log(f"full size {name}: M={wl.M} N={wl.N} K={wl.K}")
     xd, wd = d["x"].cuda(), d["w"].cuda()
     qw, sw = m.quant_weight_block(wd)
+    # the bench's launch configuration: column-major activation scales
     if wl.norm:
-        qa, sa = m.rmsnorm_quant(xd, d["gamma"].cuda(), d["eps"])
+        qa, sa = m.rmsnorm_quant(xd, d["gamma"].cuda(), d["eps"], layout=m.COL_MAJOR)
     else:
-        qa, sa = m.quant_act_group(xd)
-    y = m.gemm_blockscale(qa, sa, qw, sw)
+        qa, sa = m.quant_act_group(xd, layout=m.COL_MAJOR)
+    y = m.gemm_blockscale(qa, sa, qw, sw, a_layout=m.COL_MAJOR)
     torch.cuda.synchronize()
     rows = rows_sample(wl.M)
     xh = bf16_host(d["x"][rows])
