@@ -55,7 +55,27 @@ fp8q_status check_matrix(const void* p, int64_t K, int64_t ld, int elem_bytes) {
 constexpr int64_t kMaxRows = int64_t(1) << 26;
 constexpr int64_t kMaxK = int64_t(1) << 30;
 
+std::atomic<int> g_cu_count[kMaxDevices];
+
 }  // namespace
+
+namespace fp8q {
+
+// Compute units of the current device (cached per device; 256 if unknown).
+int device_cu_count() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < kMaxDevices) {
+    const int c = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (dev < kMaxDevices) g_cu_count[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+}  // namespace fp8q
 
 extern "C" {
 

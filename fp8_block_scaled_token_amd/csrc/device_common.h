@@ -128,6 +128,18 @@ __device__ __forceinline__ double sum_wave_f64(double v) {
   return v;
 }
 
+// ------------------------------------------------------------- work mapping
+
+// Hardware hands consecutive workgroup ids to the 8 XCDs in turn.  Renumber
+// ids 0..total-1 so that each XCD receives a contiguous run (a bijection):
+// neighbouring work items then share that XCD's L2, and partial cache lines
+// written by neighbours (column-major scales) are completed in one L2.
+__device__ __forceinline__ int xcd_contiguous(int pid, int total) {
+  const int xcd = pid & 7, idx = pid >> 3;
+  const int per = total >> 3, rem = total & 7;
+  return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + idx;
+}
+
 // ------------------------------------------------------------- memory access
 
 __device__ __forceinline__ uint4 ld16(const void* p) {

@@ -76,14 +76,6 @@ __device__ __forceinline__ int mx_byte(const uint8_t* s, int64_t row, int kb32, 
   return kb32 < KB32 ? (int)s[row * KB32 + kb32] : 127;
 }
 
-// Hardware hands consecutive workgroup ids to the 8 XCDs in turn.  Renumber
-// ids 0..total-1 so that each XCD receives a contiguous run (a bijection).
-__device__ __forceinline__ int xcd_contiguous(int pid, int total) {
-  const int xcd = pid & 7, idx = pid >> 3;
-  const int per = total >> 3, rem = total & 7;
-  return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + idx;
-}
-
 // Tile index -> (tile_m, tile_n), walking groups of GROUP_M tile rows so that
 // consecutive indices share A rows and W rows.
 __device__ __forceinline__ void group_walk(int idx, int tiles_m, int tiles_n, int& tm, int& tn) {

@@ -30,6 +30,7 @@
 #include <utility>
 
 #include "gemm_common.h"
+#include "launch.h"
 
 // K blocks between an L2 prefetch touch and the operand loads it serves
 // (0 disables the touches).
@@ -388,12 +389,7 @@ int env_int(const char* name, int dflt) {
 
 int cu_count() {
   const int forced = env_int("FP8Q_GEMM_SLOTS", 0);
-  if (forced > 0) return forced;
-  int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-    return 256;
-  return n;
+  return forced > 0 ? forced : device_cu_count();
 }
 
 struct Plan {

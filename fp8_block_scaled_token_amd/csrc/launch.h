@@ -6,6 +6,9 @@
 
 namespace fp8q {
 
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
 hipError_t launch_quant_group128(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                  uint8_t* q, int64_t ldq, float* scales, int col_major,
                                  hipStream_t stream);

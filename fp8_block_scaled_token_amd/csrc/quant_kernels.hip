@@ -88,14 +88,23 @@ __device__ __forceinline__ void store_group_scales(float* scales, float s_mine, 
 // --------------------------------------------------------------------------
 // Group-128 dynamic quantizer (fp32 scales)
 
+// Workgroup b (after XCD-contiguous renumbering) owns rows 4*(b / segs) + wave
+// of segment b % segs: each XCD handles a contiguous band of rows.
+__device__ __forceinline__ void row_block(int segs, int64_t& row, int64_t& seg) {
+  const int b = xcd_contiguous(blockIdx.x, gridDim.x);
+  row = (int64_t)(b / segs) * 4 + (threadIdx.x >> 6);
+  seg = b % segs;
+}
+
 template <int CH>
 __global__ __launch_bounds__(256) void quant_group128_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
-    uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ scales, int col_major) {
+    uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ scales, int col_major, int segs) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  int64_t row, seg;
+  row_block(segs, row, seg);
   if (row >= M) return;
-  const int64_t seg0 = (int64_t)blockIdx.y * (512 * CH);
+  const int64_t seg0 = seg * (512 * CH);
   const uint16_t* xr = x + row * ldx;
   uint8_t* qr = q + row * ldq;
   const bool full = seg0 + 512 * CH <= K;
@@ -158,11 +167,12 @@ __device__ __forceinline__ uint2 quant8_mx(const uint4& raw, uint32_t byte) {
 template <int CH>
 __global__ __launch_bounds__(256) void quant_group32mx_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
-    uint8_t* __restrict__ q, int64_t ldq, uint8_t* __restrict__ scales, int col_major) {
+    uint8_t* __restrict__ q, int64_t ldq, uint8_t* __restrict__ scales, int col_major, int segs) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  int64_t row, seg;
+  row_block(segs, row, seg);
   if (row >= M) return;
-  const int64_t seg0 = (int64_t)blockIdx.y * (512 * CH);
+  const int64_t seg0 = seg * (512 * CH);
   const uint16_t* xr = x + row * ldx;
   uint8_t* qr = q + row * ldq;
   const int64_t G = (K + 31) >> 5;
@@ -201,11 +211,12 @@ __global__ __launch_bounds__(256) void quant_group32mx_kernel(
 template <int CH>
 __global__ __launch_bounds__(256) void quant_static_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
-    const float* __restrict__ scale, uint8_t* __restrict__ q, int64_t ldq) {
+    const float* __restrict__ scale, uint8_t* __restrict__ q, int64_t ldq, int segs) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  int64_t row, seg;
+  row_block(segs, row, seg);
   if (row >= M) return;
-  const int64_t seg0 = (int64_t)blockIdx.y * (512 * CH);
+  const int64_t seg0 = seg * (512 * CH);
   const uint16_t* xr = x + row * ldx;
   uint8_t* qr = q + row * ldq;
   const float s = *scale;
@@ -230,91 +241,155 @@ __global__ __launch_bounds__(256) void quant_static_kernel(
 }
 
 // --------------------------------------------------------------------------
-// RMSNorm fused with the group-128 quantizer: one wave per row.  With
-// ONE_PASS the whole row (K <= 512*CH) stays in registers between the sum of
-// squares and the quantization; otherwise the row is read twice.
+// RMSNorm fused with the group-128 quantizer.  A 4-wave workgroup handles a
+// row at a time; wave w covers the segment of 512*CH elements starting at
+// (4i + w) * 512*CH in pass i.  The per-wave fp64 partial sums of squares
+// meet in LDS and are added in wave order (deterministic).
+//
+// rmsnorm_quant_rows_kernel (K <= 4 * 512*CH): the workgroup owns a run of
+// consecutive rows (runs in XCD-contiguous order) and keeps a row in
+// registers from the sum of squares to the quantization; the next row's
+// loads are issued before the current row is computed, so HBM traffic
+// overlaps the arithmetic.  gamma is loaded once.
+// rmsnorm_quant_kernel (longer rows): one row per workgroup, read twice.
 
-template <int CH, bool ONE_PASS>
-__global__ __launch_bounds__(256) void rmsnorm_quant_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma, float eps,
-    int64_t M, int64_t K, int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
-    float* __restrict__ scales, int col_major, uint16_t* __restrict__ y_out, int64_t ldy) {
+struct RmsArgs {
+  const uint16_t* x;
+  const uint16_t* gamma;
+  float eps;
+  int64_t M, K, ldx;
+  uint8_t* q;
+  int64_t ldq;
+  float* scales;
+  int col_major;
+  uint16_t* y_out;
+  int64_t ldy;
+};
+
+template <int CH>
+__device__ __forceinline__ void load_row_seg(uint4 (&raw)[CH], const uint16_t* xr, int64_t seg0, int64_t K) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;
-  if (row >= M) return;
-  const uint16_t* xr = x + row * ldx;
-  uint8_t* qr = q + row * ldq;
-  uint16_t* yr = y_out != nullptr ? y_out + row * ldy : nullptr;
-  const int64_t G = (K + 127) >> 7;
-  constexpr int64_t SEG = 512 * CH;
-  const int64_t nseg = ONE_PASS ? 1 : (K + SEG - 1) / SEG;
-
-  auto load_seg = [&](uint4 (&raw)[CH], int64_t seg0) {
-    if (seg0 + SEG <= K) {
+  if (seg0 + 512 * CH <= K) {
 #pragma unroll
-      for (int c = 0; c < CH; ++c) raw[c] = ld16(xr + seg0 + 512 * c + 8 * lane);
-    } else {
-#pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        const int64_t k0 = seg0 + 512 * c + 8 * lane;
-        raw[c] = (k0 < K) ? load8_bf16_masked(xr, k0, K) : make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-
-  // pass 1: sum of squares in fp64 (squares of bf16 values are exact)
-  uint4 raw[CH];
-  double ss = 0.0;
-  for (int64_t sg = 0; sg < nseg; ++sg) {
-    load_seg(raw, sg * SEG);
+    for (int c = 0; c < CH; ++c) raw[c] = ld16(xr + seg0 + 512 * c + 8 * lane);
+  } else {
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      float v[8];
-      unpack8(raw[c], v);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const double d = (double)v[e];
-        ss = __builtin_fma(d, d, ss);
-      }
+      const int64_t k0 = seg0 + 512 * c + 8 * lane;
+      raw[c] = (k0 < K) ? load8_bf16_masked(xr, k0, K) : make_uint4(0, 0, 0, 0);
     }
   }
-  ss = sum_wave_f64(ss);
-  const float rn = (float)(1.0 / sqrt(ss / (double)K + (double)eps));
+}
 
-  // pass 2: y = bf16((x * r) * g), then group quantization of y
-  for (int64_t sg = 0; sg < nseg; ++sg) {
-    const int64_t seg0 = sg * SEG;
-    const bool full = seg0 + SEG <= K;
-    if (!ONE_PASS) load_seg(raw, seg0);
-    float amax[CH];
+// fp64 sum of squares of a segment (squares of bf16 values are exact)
+template <int CH>
+__device__ __forceinline__ double sumsq_seg(const uint4 (&raw)[CH], double ss) {
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int64_t k0 = seg0 + 512 * c + 8 * lane;
-      const uint4 gr = full ? ld16(gamma + k0)
-                            : (k0 < K) ? load8_bf16_masked(gamma, k0, K) : make_uint4(0, 0, 0, 0);
-      float v[8], g[8];
-      unpack8(raw[c], v);
-      unpack8(gr, g);
-      uint32_t yb[4];
+  for (int c = 0; c < CH; ++c) {
+    float v[8];
+    unpack8(raw[c], v);
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) yb[e >> 1] = pack_bf16x2((v[e] * rn) * g[e], (v[e + 1] * rn) * g[e + 1]);
-      raw[c] = make_uint4(yb[0], yb[1], yb[2], yb[3]);      // raw now holds bf16 y
-      if (yr != nullptr) {
-        if (full) *reinterpret_cast<uint4*>(yr + k0) = raw[c];
-        else if (k0 < K) store8_bf16_masked(yr, k0, K, raw[c]);
-      }
-      amax[c] = max_row16(absmax8(raw[c]));
+    for (int e = 0; e < 8; ++e) {
+      const double d = (double)v[e];
+      ss = __builtin_fma(d, d, ss);
     }
-    float s[CH], r[CH], s_mine;
-    group_scales<CH>(amax, s, r, s_mine);
+  }
+  return ss;
+}
+
+// r = fp32(1 / sqrt(sum / K + eps)) from the wave partials; `part` holds one
+// slot per wave, written here, and the caller's barrier discipline keeps a
+// slot set from being overwritten while another wave still reads it.
+__device__ __forceinline__ float rms_inv(double ss, double* part, int64_t K, float eps) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  ss = sum_wave_f64(ss);
+  if (lane == 0) part[wave] = ss;
+  __syncthreads();
+  ss = ((part[0] + part[1]) + part[2]) + part[3];
+  return (float)(1.0 / sqrt(ss / (double)K + (double)eps));
+}
+
+// y = bf16((x * r) * g) for one segment, then its group quantization.
+template <int CH>
+__device__ __forceinline__ void norm_quant_seg(const RmsArgs& a, uint4 (&raw)[CH], const uint4 (&gr)[CH],
+                                               float rn, int64_t row, int64_t seg0) {
+  const int lane = threadIdx.x & 63;
+  const int64_t K = a.K;
+  const bool full = seg0 + 512 * CH <= K;
+  uint8_t* qr = a.q + row * a.ldq;
+  uint16_t* yr = a.y_out != nullptr ? a.y_out + row * a.ldy : nullptr;
+  float amax[CH];
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int64_t k0 = seg0 + 512 * c + 8 * lane;
-      const uint2 o = quant8(raw[c], s[c], r[c]);
-      if (full) st8(qr + k0, o);
-      else if (k0 < K) store8_masked(qr, k0, K, o);
+  for (int c = 0; c < CH; ++c) {
+    const int64_t k0 = seg0 + 512 * c + 8 * lane;
+    float v[8], g[8];
+    unpack8(raw[c], v);
+    unpack8(gr[c], g);
+    uint32_t yb[4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) yb[e >> 1] = pack_bf16x2((v[e] * rn) * g[e], (v[e + 1] * rn) * g[e + 1]);
+    raw[c] = make_uint4(yb[0], yb[1], yb[2], yb[3]);      // raw now holds bf16 y
+    if (yr != nullptr) {
+      if (full) *reinterpret_cast<uint4*>(yr + k0) = raw[c];
+      else if (k0 < K) store8_bf16_masked(yr, k0, K, raw[c]);
     }
-    store_group_scales<CH>(scales, s_mine, seg0 / 128, G, M, row, col_major);
+    amax[c] = max_row16(absmax8(raw[c]));
+  }
+  float s[CH], r[CH], s_mine;
+  group_scales<CH>(amax, s, r, s_mine);
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int64_t k0 = seg0 + 512 * c + 8 * lane;
+    const uint2 o = quant8(raw[c], s[c], r[c]);
+    if (full) st8(qr + k0, o);
+    else if (k0 < K) store8_masked(qr, k0, K, o);
+  }
+  store_group_scales<CH>(a.scales, s_mine, seg0 / 128, (K + 127) >> 7, a.M, row, a.col_major);
+}
+
+template <int CH>
+__global__ __launch_bounds__(256) void rmsnorm_quant_rows_kernel(RmsArgs a, int rows_per_wg) {
+  __shared__ double part[2][4];
+  const int wave = threadIdx.x >> 6;
+  const int64_t r0 = (int64_t)xcd_contiguous(blockIdx.x, gridDim.x) * rows_per_wg;
+  const int64_t r1 = r0 + rows_per_wg < a.M ? r0 + rows_per_wg : a.M;
+  if (r0 >= a.M) return;                       // whole workgroup
+  const int64_t seg0 = (int64_t)wave * (512 * CH);
+  uint4 gr[CH], cur[CH], nxt[CH];
+  load_row_seg<CH>(gr, a.gamma, seg0, a.K);
+  load_row_seg<CH>(cur, a.x + r0 * a.ldx, seg0, a.K);
+  for (int64_t row = r0; row < r1; ++row) {
+    if (row + 1 < r1) load_row_seg<CH>(nxt, a.x + (row + 1) * a.ldx, seg0, a.K);
+    // the two slot sets alternate; the barrier inside rms_inv of row i+1
+    // orders every read of set (i & 1) before the writes of row i+2
+    const float rn = rms_inv(sumsq_seg<CH>(cur, 0.0), part[(row - r0) & 1], a.K, a.eps);
+    if (seg0 < a.K) norm_quant_seg<CH>(a, cur, gr, rn, row, seg0);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) cur[c] = nxt[c];
+  }
+}
+
+template <int CH>
+__global__ __launch_bounds__(256) void rmsnorm_quant_kernel(RmsArgs a) {
+  __shared__ double part[4];
+  const int wave = threadIdx.x >> 6;
+  const int64_t row = xcd_contiguous(blockIdx.x, gridDim.x);
+  const uint16_t* xr = a.x + row * a.ldx;
+  constexpr int64_t SEG = 512 * CH;
+  const int64_t npass = (a.K + 4 * SEG - 1) / (4 * SEG);
+  uint4 raw[CH], gr[CH];
+  double ss = 0.0;
+  for (int64_t it = 0; it < npass; ++it) {
+    load_row_seg<CH>(raw, xr, (4 * it + wave) * SEG, a.K);
+    ss = sumsq_seg<CH>(raw, ss);
+  }
+  const float rn = rms_inv(ss, part, a.K, a.eps);
+  for (int64_t it = 0; it < npass; ++it) {
+    const int64_t seg0 = (4 * it + wave) * SEG;
+    if (seg0 >= a.K) break;
+    load_row_seg<CH>(raw, xr, seg0, a.K);
+    load_row_seg<CH>(gr, a.gamma, seg0, a.K);
+    norm_quant_seg<CH>(a, raw, gr, rn, row, seg0);
   }
 }
 
@@ -384,18 +459,23 @@ static inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // short rows do not leave most lanes idle.
 static inline int row_chunks(int64_t K) { return K <= 512 ? 1 : (K <= 1024 ? 2 : 4); }
 
+// 1-D grid of ceil(M/4) * segs workgroups; the kernels index it with int.
+static inline bool row_grid_fits(int64_t M, int64_t segs) { return ceil_div(M, 4) * segs <= 0x7FFFFFFF; }
+static inline dim3 row_grid(int64_t M, int64_t segs) { return dim3((unsigned)(ceil_div(M, 4) * segs)); }
+
 hipError_t launch_quant_group128(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                  uint8_t* q, int64_t ldq, float* scales, int col_major,
                                  hipStream_t stream) {
   const int ch = row_chunks(K);
-  const int64_t segs = ceil_div(K, 512 * ch);
-  const dim3 grid((unsigned)ceil_div(M, 4), (unsigned)segs), block(256);
+  const int segs = (int)ceil_div(K, 512 * ch);
+  if (!row_grid_fits(M, segs)) return hipErrorInvalidConfiguration;
+  const dim3 grid = row_grid(M, segs), block(256);
   if (ch == 1)
-    hipLaunchKernelGGL(quant_group128_kernel<1>, grid, block, 0, stream, x, M, K, ldx, q, ldq, scales, col_major);
+    hipLaunchKernelGGL(quant_group128_kernel<1>, grid, block, 0, stream, x, M, K, ldx, q, ldq, scales, col_major, segs);
   else if (ch == 2)
-    hipLaunchKernelGGL(quant_group128_kernel<2>, grid, block, 0, stream, x, M, K, ldx, q, ldq, scales, col_major);
+    hipLaunchKernelGGL(quant_group128_kernel<2>, grid, block, 0, stream, x, M, K, ldx, q, ldq, scales, col_major, segs);
   else
-    hipLaunchKernelGGL(quant_group128_kernel<4>, grid, block, 0, stream, x, M, K, ldx, q, ldq, scales, col_major);
+    hipLaunchKernelGGL(quant_group128_kernel<4>, grid, block, 0, stream, x, M, K, ldx, q, ldq, scales, col_major, segs);
   return hipGetLastError();
 }
 
@@ -403,38 +483,48 @@ hipError_t launch_quant_group32mx(const uint16_t* x, int64_t M, int64_t K, int64
                                   uint8_t* q, int64_t ldq, uint8_t* scales, int col_major,
                                   hipStream_t stream) {
   const int ch = row_chunks(K);
-  const int64_t segs = ceil_div(K, 512 * ch);
-  const dim3 grid((unsigned)ceil_div(M, 4), (unsigned)segs), block(256);
+  const int segs = (int)ceil_div(K, 512 * ch);
+  if (!row_grid_fits(M, segs)) return hipErrorInvalidConfiguration;
+  const dim3 grid = row_grid(M, segs), block(256);
   if (ch == 1)
-    hipLaunchKernelGGL(quant_group32mx_kernel<1>, grid, block, 0, stream, x, M, K, ldx, q, ldq, scales, col_major);
+    hipLaunchKernelGGL(quant_group32mx_kernel<1>, grid, block, 0, stream, x, M, K, ldx, q, ldq, scales, col_major, segs);
   else if (ch == 2)
-    hipLaunchKernelGGL(quant_group32mx_kernel<2>, grid, block, 0, stream, x, M, K, ldx, q, ldq, scales, col_major);
+    hipLaunchKernelGGL(quant_group32mx_kernel<2>, grid, block, 0, stream, x, M, K, ldx, q, ldq, scales, col_major, segs);
   else
-    hipLaunchKernelGGL(quant_group32mx_kernel<4>, grid, block, 0, stream, x, M, K, ldx, q, ldq, scales, col_major);
+    hipLaunchKernelGGL(quant_group32mx_kernel<4>, grid, block, 0, stream, x, M, K, ldx, q, ldq, scales, col_major, segs);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_static(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                const float* scale, uint8_t* q, int64_t ldq, hipStream_t stream) {
-  const int64_t segs = ceil_div(K, 512 * 4);
-  const dim3 grid((unsigned)ceil_div(M, 4), (unsigned)segs), block(256);
-  hipLaunchKernelGGL(quant_static_kernel<4>, grid, block, 0, stream, x, M, K, ldx, scale, q, ldq);
+  const int segs = (int)ceil_div(K, 512 * 4);
+  if (!row_grid_fits(M, segs)) return hipErrorInvalidConfiguration;
+  const dim3 grid = row_grid(M, segs), block(256);
+  hipLaunchKernelGGL(quant_static_kernel<4>, grid, block, 0, stream, x, M, K, ldx, scale, q, ldq, segs);
   return hipGetLastError();
 }
 
 hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, float eps, int64_t M,
                                 int64_t K, int64_t ldx, uint8_t* q, int64_t ldq, float* scales,
                                 int col_major, uint16_t* y_out, int64_t ldy, hipStream_t stream) {
-  const dim3 grid((unsigned)ceil_div(M, 4)), block(256);
-#define FP8Q_RMS(CH, ONE) \
-  hipLaunchKernelGGL((rmsnorm_quant_kernel<CH, ONE>), grid, block, 0, stream, x, gamma, eps, M, K, ldx, q, ldq, scales, col_major, y_out, ldy)
-  if (K <= 512) FP8Q_RMS(1, true);
-  else if (K <= 1024) FP8Q_RMS(2, true);
-  else if (K <= 2048) FP8Q_RMS(4, true);
-  else if (K <= 4096) FP8Q_RMS(8, true);
-  else if (K <= 6144) FP8Q_RMS(12, true);
-  else if (K <= 8192) FP8Q_RMS(16, true);
-  else FP8Q_RMS(8, false);
+  const RmsArgs a{x, gamma, eps, M, K, ldx, q, ldq, scales, col_major, y_out, ldy};
+  const dim3 block(256);
+  if (K > 4 * 512 * 8) {   // long rows: one workgroup per row, two reads
+    hipLaunchKernelGGL(rmsnorm_quant_kernel<4>, dim3((unsigned)M), block, 0, stream, a);
+    return hipGetLastError();
+  }
+  // four workgroups per CU, each a run of consecutive rows (measured best
+  // against two per CU and against one workgroup per row)
+  const int64_t wgs = (int64_t)device_cu_count() * 4;
+  const int rows = (int)ceil_div(M, wgs);
+  const dim3 grid((unsigned)ceil_div(M, rows));
+#define FP8Q_RMS(CH) hipLaunchKernelGGL((rmsnorm_quant_rows_kernel<CH>), grid, block, 0, stream, a, rows)
+  if (K <= 2048) FP8Q_RMS(1);
+  else if (K <= 4096) FP8Q_RMS(2);
+  else if (K <= 6144) FP8Q_RMS(3);
+  else if (K <= 8192) FP8Q_RMS(4);
+  else if (K <= 12288) FP8Q_RMS(6);
+  else FP8Q_RMS(8);
 #undef FP8Q_RMS
   return hipGetLastError();
 }

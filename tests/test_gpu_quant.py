@@ -141,7 +141,10 @@ def _rms_expected(xh, gh, eps, y_gpu_bits):
     return ref, amb
 
 
-@pytest.mark.parametrize("M,K", [(16, 512), (5, 520), (64, 6144), (3, 7168), (4, 9000), (2, 1001)])
+# several rows per workgroup with a short last run (2500 rows at K 6144 and
+# 1030 rows at K 16384), and rows longer than the one-read limit (17000)
+@pytest.mark.parametrize("M,K", [(16, 512), (5, 520), (64, 6144), (3, 7168), (4, 9000), (2, 1001),
+                                 (2500, 6144), (1030, 16384), (3, 17000)])
 @pytest.mark.parametrize("layout", [0, 1])
 def test_rmsnorm_quant_parity(M, K, layout):
     log(f"rmsnorm_quant M={M} K={K} layout={layout}")
@@ -177,18 +180,23 @@ def test_rmsnorm_quant_parity(M, K, layout):
         assert any(match), f"row {i}"
 
 
-def test_rmsnorm_quant_full_size_sampled_rows():
+@pytest.mark.parametrize("layout", [0, 1])
+def test_rmsnorm_quant_full_size_sampled_rows(layout):
+    # layout 1 is the bench's launch configuration
     wl = workloads.WORKLOADS["prefill_norm"]
-    log(f"rmsnorm_quant full size [{wl.M},{wl.K}]")
+    log(f"rmsnorm_quant full size [{wl.M},{wl.K}] layout={layout}")
     m = fq()
     d = wl.make("cpu")
-    q, s = m.rmsnorm_quant(d["x"].cuda(), d["gamma"].cuda(), d["eps"])
+    q, s = m.rmsnorm_quant(d["x"].cuda(), d["gamma"].cuda(), d["eps"], layout=layout)
     torch.cuda.synchronize()
+    sg = s.cpu().numpy()
+    if layout:
+        sg = sg.T
     rows = np.unique(np.concatenate([[0, wl.M - 1], np.random.default_rng(1).integers(0, wl.M, 30)]))
     ref = oq.rmsnorm_quant(bf16_host(d["x"][rows]), bf16_host(d["gamma"]), d["eps"])
     ok = ~ref["ambiguous"]
     np.testing.assert_array_equal(q.cpu().numpy()[rows][ok], ref["q"][ok])
-    np.testing.assert_array_equal(s.cpu().numpy()[rows][ok], ref["s"][ok])
+    np.testing.assert_array_equal(sg[rows][ok], ref["s"][ok])
 
 
 @pytest.mark.parametrize("N,K", [(256, 512), (300, 200), (128, 1001), (1024, 7168)])
