@@ -4,26 +4,36 @@
 // Same arithmetic as the generic kernels (block rescale per 128-wide K block,
 // per-tensor, or MX scales inside the MFMA; see gemm_kernels.hip), organised
 // for throughput on CDNA4:
+//  * Transposed MFMA tiles.  Each 16x16x128 MFMA takes a weight fragment as
+//    its first operand and an activation fragment as its second, so a lane
+//    holds four consecutive output COLUMNS of one output ROW.  In block mode
+//    the four partial products of a lane then share one activation scale:
+//    the per-K-block rescale is 4 FMAs per MFMA plus one scale product per
+//    16 rows, which fits the VALU issue slots that an fp8 MFMA leaves free
+//    (about 4 per MFMA on one SIMD, measured), and the epilogue writes
+//    8-byte runs of bf16.
 //  * Large workgroup tiles.  One K block of a BM x BN tile moves
 //    (BM + BN) * 128 bytes from L2 through the CU's vector cache into LDS;
-//    at the fp8 MFMA rate a 128 x 128 tile would need that path's whole
-//    bandwidth, a 256 x 256 tile needs half of it.  The big configuration
-//    is 256 x 256 with 8 waves (2 x 4, 128 x 64 per wave: 8 x 4 MFMA tiles),
-//    one workgroup per CU; the small one is 128 x 128 with 4 waves, two
-//    workgroups per CU, for shapes with few tiles.
+//    the big configuration is 256 x 256 with 8 waves (2 x 4, 128 rows x 64
+//    columns per wave), one workgroup per CU; the small one is 128 x 128 with
+//    4 waves, two workgroups per CU, for shapes with few tiles.
 //  * Operands move global -> LDS with buffer_load ... lds (no VGPR staging).
 //    Such a load writes 16 bytes per lane to consecutive LDS addresses, so the
 //    XOR row swizzle of the LDS tile is produced by choosing, per lane, which
-//    16-byte chunk of global memory to fetch.  Rows past M or N fall outside
-//    the buffer descriptor and read as zero.
-//  * Two LDS stages, one barrier per K block; the loop body is a single basic
-//    block so the scheduler can interleave the block-mode rescale FMAs of one
-//    16-row tile with the MFMAs of the next.
+//    16-byte chunk of global memory to fetch.  The per-lane offsets are fixed
+//    for the whole K loop and the K position travels in the scalar offset,
+//    so issuing a K block costs no vector instructions.  Rows past M or N are
+//    given an offset outside the buffer descriptor and read as zero.
+//  * Two LDS stages, one barrier per K block; the K loop body is a single
+//    basic block so the scheduler can interleave the block-mode rescale FMAs
+//    of one 16-row tile with the MFMAs of the next.
 //  * Tail balancing: when the last round of tiles would leave at least half
 //    of the CUs idle, those tiles are split into two half-height tiles, which
 //    fill the machine and take half as long.
 //  * Workgroup ids are renumbered XCD-aware and tiles walked in groups of
-//    tile rows, so tiles sharing A rows or W rows meet in the same L2.
+//    tile rows, so tiles sharing A rows or W rows meet in the same L2, and
+//    every workgroup touches its share of the operand lines a few K blocks
+//    ahead so that the LDS loads find them in L2.
 // Preconditions (checked by the launcher): K % 128 == 0, every operand and
 // scale array smaller than 2^31 bytes, M > 64.
 #include <cstdlib>
@@ -47,7 +57,7 @@ __device__ __forceinline__ int swz(int r, int c) { return (r << 7) | ((c ^ (r & 
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-// Raw buffer descriptor (stride 0): reads at byte offsets >= `bytes` return 0.
+// Raw buffer descriptor (stride 0): lanes whose offset is >= `bytes` read 0.
 __device__ __forceinline__ i32x4 rsrc(const void* base, int64_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
   i32x4 r;
@@ -62,28 +72,32 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// Direct-to-LDS loads: lane i's 16 (or 4) bytes land at LDS address
-// lds + 16*i (4*i); `lds` must be wave-uniform.
+// Direct-to-LDS loads: lane i's 16 (or 4) bytes from base + voffset + soffset
+// land at LDS address lds + 16*i (4*i); `lds` and `soffset` are wave-uniform.
 // Written as inline assembly on purpose: the compiler cannot tell which LDS
 // stage a direct-to-LDS load fills, and would otherwise make every LDS read
 // wait for all of them.  These loads are therefore invisible to the
 // compiler's vmcnt bookkeeping; the kernel waits for them explicitly and
 // issues no other vector-memory loads inside its K loop.
-__device__ __forceinline__ void dma16(const i32x4& r, uint32_t lds, uint32_t voffset) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+// Every caller keeps voffset + soffset below the descriptor's size for a lane
+// whose voffset is below it, so the loads stay inside their arrays whether or
+// not the range check includes the scalar offset.
+__device__ __forceinline__ void dma16(const i32x4& r, uint32_t lds, uint32_t voffset, uint32_t soffset) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
                :
-               : "v"(voffset), "s"(r), "s"(lds)
+               : "v"(voffset), "s"(r), "s"(lds), "s"(soffset)
                : "memory", "m0");
 }
-__device__ __forceinline__ void dma4(const i32x4& r, uint32_t lds, uint32_t voffset) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds"
+__device__ __forceinline__ void dma4(const i32x4& r, uint32_t lds, uint32_t voffset, uint32_t soffset) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, %3 offen lds"
                :
-               : "v"(voffset), "s"(r), "s"(lds)
+               : "v"(voffset), "s"(r), "s"(lds), "s"(soffset)
                : "memory", "m0");
 }
 
-// Added to a load offset that must not read memory: every descriptor covers
-// fewer than 2^31 bytes, so the load falls out of range and writes zeros.
+// A lane offset that must not read memory: every descriptor covers fewer
+// than 2^31 bytes and every scalar offset is below 2^31, so the load falls
+// out of range (and the sum does not wrap) and writes zeros.
 constexpr uint32_t OOB = 0x80000000u;
 
 template <int... I, typename F>
@@ -115,8 +129,9 @@ __device__ __forceinline__ void wait_vmcnt_barrier() {
 
 // Geometry of one fast-kernel configuration: BM x BN workgroup tile, WM x WN
 // waves.  Stage layout in LDS (2 stages): A tile [BM][128] and W tile
-// [BN][128], both swizzled; then 64 A-scale words per wave, then 64 W-scale
-// words per wave.
+// [BN][128], both swizzled; then the scale words of the stage's K block: BM
+// activation-scale words, then BN weight-scale words (MX: one word = the four
+// 32-wide blocks of a row; block mode: only the first BN/128 words are used).
 template <int MODE_, int BM_, int BN_, int WM_, int WN_, int NTN_>
 struct FastTile {
   static constexpr int MODE = MODE_, BM = BM_, BN = BN_, WM = WM_, WN = WN_;
@@ -129,12 +144,14 @@ struct FastTile {
   static constexpr int A_PER = ABYTES / 1024 / NW;  // 1 KB loads per wave per stage
   static constexpr int W_PER = WBYTES / 1024 / NW;
   static constexpr int SA_OFF = ABYTES + WBYTES;
-  static constexpr int SW_OFF = SA_OFF + NW * 256;
-  static constexpr int STAGE = SW_OFF + NW * 256;
+  static constexpr int SW_OFF = SA_OFF + BM * 4;
+  static constexpr int STAGE = ((SW_OFF + BN * 4) + 1023) / 1024 * 1024;
   static constexpr int NS = 2;
   static constexpr int PF_OFF = NS * STAGE;            // 256 bytes per wave: prefetch sink
   static constexpr int LDS_BYTES = PF_OFF + NW * 256;
-  static_assert(BM == 32 * NW && BN == 32 * NW, "each wave fetches the scales of 32 rows");
+  // scale loads: one 64-word load per wave covers the BM + BN scale words
+  static constexpr int SCALE_LOADS = MODE == MODE_TENSOR ? 0 : 1;
+  static_assert(NW * 64 == BM + BN, "one scale word per lane");
   static_assert(A_PER * NW * 1024 == ABYTES && W_PER * NW * 1024 == WBYTES, "whole 1 KB loads");
   static_assert(WTN <= 128 && 128 % WTN == 0, "one weight-scale block per wave");
   static_assert(STAGE % 1024 == 0, "stages stay 1 KB aligned");
@@ -144,69 +161,104 @@ struct FastTile {
 // BM / 2 (HALF).
 template <class T, bool HALF>
 __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int m0, int n0, int gm, int gn) {
-  constexpr int MODE = T::MODE, BN = T::BN, WN = T::WN;
+  constexpr int MODE = T::MODE, BM = T::BM, BN = T::BN, WN = T::WN, NW = T::NW;
   constexpr int RM = HALF ? T::BM / 2 : T::BM;
   constexpr int WTM = RM / T::WM, TM = WTM / 16, WTN = T::WTN, TN = T::TN;
   constexpr int A_PER = T::A_PER, W_PER = T::W_PER, STAGE = T::STAGE;
   constexpr int ABYTES = T::ABYTES, SA_OFF = T::SA_OFF, SW_OFF = T::SW_OFF;
   static_assert(TM >= 1, "wave tile at least 16 rows");
 
-  const int lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63, l16 = lane & 15, lq = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WN, wn = wave % WN;
 
   const i32x4 rA = rsrc(p.a, (int64_t)p.M * p.lda);
   const i32x4 rW = rsrc(p.w, (int64_t)p.N * p.ldw);
-  const i32x4 rSA =
-      rsrc(p.sa, MODE == MODE_MX ? (int64_t)p.M * p.KB32 : (MODE == MODE_BLOCK ? (int64_t)p.M * p.KB * 4 : 4));
-  const i32x4 rSW =
-      rsrc(p.sw, MODE == MODE_MX ? (int64_t)p.N * p.KB32 : (MODE == MODE_BLOCK ? (int64_t)p.NB * p.KB * 4 : 4));
 
+  // ---- per-lane load offsets (fixed for the whole K loop)
   // Load i of wave w fills LDS kilobyte (A_PER*w + i) of the A tile, i.e.
   // tile rows 8*(A_PER*w + i) + lane/8 with lane % 8 the physical chunk; the
   // logical chunk to fetch is (lane % 8) ^ (row % 8) = (lane % 8) ^ (lane / 8).
   // A half tile needs only its first RM rows: the other loads are kept (for
   // the vmcnt count) but read nothing.
   const int lrow = lane >> 3, lchunk = (lane & 7) ^ (lane >> 3);
-  const int offA = (m0 + 8 * A_PER * wave + lrow) * (int)p.lda + lchunk * 16;
-  const int offW = (n0 + 8 * W_PER * wave + lrow) * (int)p.ldw + lchunk * 16;
-  const int lda8 = 8 * (int)p.lda, ldw8 = 8 * (int)p.ldw;
-  // scales: lane l of wave w fetches A row 32w + l % 32 (and, MX, W row
-  // 32w + l % 32) into scale word 64w + l; block mode: W block n0/128 + l % NBLK
-  constexpr int NBLK = BN / 128 > 0 ? BN / 128 : 1;
-  const int srow = m0 + 32 * wave + (lane & 31);
-  const int swrow = n0 + 32 * wave + (lane & 31);
-  const int sa_row = p.sa_col_major ? srow : srow * p.KB;   // block-mode A scale (row, kb)
-  const int sa_kstride = p.sa_col_major ? p.M : 1;
-  const int wblk = n0 / 128 + lane % NBLK;
+  uint32_t offA[A_PER], offW[W_PER];
+#pragma unroll
+  for (int i = 0; i < A_PER; ++i) {
+    const int r = 8 * (A_PER * wave + i) + lrow;
+    offA[i] = (r < RM) ? (uint32_t)((m0 + r) * (int)p.lda + lchunk * 16) : OOB;
+  }
+#pragma unroll
+  for (int i = 0; i < W_PER; ++i)
+    offW[i] = (uint32_t)((n0 + 8 * (W_PER * wave + i) + lrow) * (int)p.ldw + lchunk * 16);
+
+  // Scale words: lane l of wave w fetches word q = 64w + l of the stage's
+  // scale area.  Activation words are ordered [wm][row % 16][row tile] so a
+  // lane reads the TM scales of its rows as consecutive words; MX weight
+  // words likewise [wn][row % 16][row tile].  Block mode: weight word b is
+  // the scale of 128-column block n0/128 + b.
+  const bool wave_is_a = 64 * wave < BM;    // waves below BM/64 fetch activation scales
+  i32x4 rSA = rA, rSW = rW;
+  uint32_t offS = OOB;
+  uint32_t kstepS = 0;    // scalar offset advance per K block
+  if constexpr (MODE != MODE_TENSOR) {
+    const int q = 64 * wave + lane;
+    const bool is_a = q < BM;
+    if (MODE == MODE_BLOCK) {
+      rSA = rsrc(p.sa, (int64_t)p.M * p.KB * 4);
+      rSW = rsrc(p.sw, (int64_t)p.NB * p.KB * 4);
+    } else {
+      rSA = rsrc(p.sa, (int64_t)p.M * p.KB32);
+      rSW = rsrc(p.sw, (int64_t)p.N * p.KB32);
+    }
+    if (is_a) {
+      const int g = q / WTM, rem = q % WTM;               // q < RM only when g < WM
+      const int row = m0 + g * WTM + 16 * (rem % TM) + rem / TM;
+      const bool live = q < RM && row < p.M;
+      if (MODE == MODE_BLOCK)
+        offS = live ? (uint32_t)(p.sa_col_major ? row * 4 : row * p.KB * 4) : OOB;
+      else
+        offS = live ? (uint32_t)(row * p.KB32) : OOB;
+    } else {
+      const int qw = q - BM;
+      if (MODE == MODE_BLOCK) {
+        const int blk = n0 / 128 + qw;
+        offS = (qw < (BN + 127) / 128 && blk < p.NB) ? (uint32_t)(blk * p.KB * 4) : OOB;
+      } else {
+        const int g = qw / WTN, rem = qw % WTN;
+        const int row = n0 + g * WTN + 16 * (rem % TN) + rem / TN;
+        offS = row < p.N ? (uint32_t)(row * p.KB32) : OOB;
+      }
+    }
+    // the scalar offset of a K block: block-mode column-major activation
+    // scales advance by M words, every other scale array by one word (block)
+    // or four bytes (MX) per K block
+    kstepS = (MODE == MODE_BLOCK && p.sa_col_major && wave_is_a) ? (uint32_t)p.M * 4u : 4u;
+  }
+  const i32x4 rS = wave_is_a ? rSA : rSW;
   const uint32_t smem_base = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 
-  // Fill stage `st` with K block kb.  Past the last block the loads are kept
-  // (so every step issues the same number) but read nothing and write zeros
-  // into the free stage.
+  // Fill stage `st` with K block kb.  Past the last block the descriptors
+  // cover nothing: the loads are still issued (every step issues the same
+  // number) but read nothing and write zeros into the free stage.
+  const int KB = p.KB;
   auto issue = [&](int st, int kb) {
-    const bool valid = kb < p.KB;
-    const uint32_t oob = valid ? 0u : OOB;
+    const bool valid = kb < KB;
+    i32x4 ra = rA, rw = rW, rs = rS;
+    ra.z = valid ? ra.z : 0;
+    rw.z = valid ? rw.z : 0;
+    rs.z = valid ? rs.z : 0;
+    const int kbv = valid ? kb : 0;
     const uint32_t base = smem_base + st * STAGE;
     const uint32_t a = base + wave * A_PER * 1024;
     const uint32_t w = base + ABYTES + wave * W_PER * 1024;
-    const int kofs = valid ? kb * 128 : 0;
+    const uint32_t kofs = (uint32_t)kbv * 128u;
 #pragma unroll
-    for (int i = 0; i < A_PER; ++i) {
-      const bool live = !HALF || (A_PER * wave + i) * 8 < RM;
-      dma16(rA, a + i * 1024, (uint32_t)(offA + i * lda8 + kofs) + (live ? oob : OOB));
-    }
+    for (int i = 0; i < A_PER; ++i) dma16(ra, a + i * 1024, offA[i], kofs);
 #pragma unroll
-    for (int i = 0; i < W_PER; ++i) dma16(rW, w + i * 1024, (uint32_t)(offW + i * ldw8 + kofs) + oob);
-    const int kbv = valid ? kb : 0;
-    const uint32_t sa_lds = base + SA_OFF + wave * 256, sw_lds = base + SW_OFF + wave * 256;
-    if constexpr (MODE == MODE_BLOCK) {
-      dma4(rSA, sa_lds, (uint32_t)((sa_row + kbv * sa_kstride) * 4) + oob);
-      dma4(rSW, sw_lds, (uint32_t)((wblk * p.KB + kbv) * 4) + oob);
-    } else if constexpr (MODE == MODE_MX) {
-      dma4(rSA, sa_lds, (uint32_t)(srow * p.KB32 + kbv * 4) + oob);
-      dma4(rSW, sw_lds, (uint32_t)(swrow * p.KB32 + kbv * 4) + oob);
-    }
+    for (int i = 0; i < W_PER; ++i) dma16(rw, w + i * 1024, offW[i], kofs);
+    if constexpr (MODE != MODE_TENSOR)
+      dma4(rs, base + SA_OFF + wave * 256, offS, (uint32_t)kbv * kstepS);
   };
   // L2 prefetch.  Tiles running together on one XCD share operand rows: the
   // NTN tiles of a tile row read the same A rows, the 8 tiles of a tile
@@ -215,144 +267,205 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
   // PFD K blocks ahead, so that the operand loads find them in L2.  The
   // touches go to a per-wave LDS sink; they are issued after the operand
   // loads of a step and may stay in flight until the next step's wait.
+  // Past the last K block the descriptors cover nothing and the touches read
+  // nothing.
   constexpr int PFD = FP8Q_PREFETCH_DISTANCE;
-  constexpr int PA = RM / T::NTN / T::NW, PW = BN / 8 / T::NW;   // rows per wave
+  constexpr int PA = RM / T::NTN / NW, PW = BN / 8 / NW;   // rows per wave
   static_assert(PA >= 1 && PA <= 64 && PW >= 1 && PW <= 64, "prefetch slice");
-  const uint32_t pfa = (uint32_t)(m0 + gn * (RM / T::NTN) + wave * PA + lane) * (uint32_t)p.lda;
-  const uint32_t pfw = (uint32_t)(n0 + gm * (BN / 8) + wave * PW + lane) * (uint32_t)p.ldw;
+  const int pra = m0 + gn * (RM / T::NTN) + wave * PA + lane;
+  const int prw = n0 + gm * (BN / 8) + wave * PW + lane;
+  const uint32_t pfa = (PFD > 0 && lane < PA && pra < p.M) ? (uint32_t)pra * (uint32_t)p.lda : OOB;
+  const uint32_t pfw = (PFD > 0 && lane < PW && prw < p.N) ? (uint32_t)prw * (uint32_t)p.ldw : OOB;
   const uint32_t pf_lds = smem_base + T::PF_OFF + wave * 256;
   auto prefetch = [&](int kb) {
     const bool valid = PFD > 0 && kb < p.KB;
+    i32x4 ra = rA, rw = rW;
+    ra.z = valid ? ra.z : 0;
+    rw.z = valid ? rw.z : 0;
     const uint32_t kofs = valid ? (uint32_t)kb * 128u : 0u;
-    dma4(rA, pf_lds, (valid && lane < PA) ? pfa + kofs : OOB);
-    dma4(rW, pf_lds, (valid && lane < PW) ? pfw + kofs : OOB);
+    dma4(ra, pf_lds, pfa, kofs);
+    dma4(rw, pf_lds, pfw, kofs);
   };
 
-  // scale word of tile row r / tile column c
-  auto s_word = [](int r) { return 64 * (r >> 5) + (r & 31); };
-
+  // acc[i][j]: output rows m0 + wm*WTM + 16i + lane%16, columns
+  // n0 + wn*WTN + 16j + 4*(lane/16) + r (r = 0..3)
   v4f acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
+  // n consecutive scale words (n = 1, 2 or a multiple of 4) from LDS
+  auto read_words = [&](const uint32_t* src, uint32_t* dst, auto NN) {
+    constexpr int n = decltype(NN)::value;
+    if constexpr (n % 4 == 0) {
+#pragma unroll
+      for (int i = 0; i < n; i += 4) {
+        const uint4 s4 = *reinterpret_cast<const uint4*>(src + i);
+        dst[i] = s4.x; dst[i + 1] = s4.y; dst[i + 2] = s4.z; dst[i + 3] = s4.w;
+      }
+    } else if constexpr (n == 2) {
+      const uint2 s2 = *reinterpret_cast<const uint2*>(src);
+      dst[0] = s2.x; dst[1] = s2.y;
+    } else {
+      static_assert(n == 1, "scale word count");
+      dst[0] = src[0];
+    }
+  };
+
   auto read_frag = [&](const uint8_t* base, int row) {
     Frag f;
-    const int c0 = lane >> 4;
-    f.u[0] = *reinterpret_cast<const uint4*>(base + swz(row, c0));
-    f.u[1] = *reinterpret_cast<const uint4*>(base + swz(row, c0 + 4));
+    f.u[0] = *reinterpret_cast<const uint4*>(base + swz(row, lq));
+    f.u[1] = *reinterpret_cast<const uint4*>(base + swz(row, lq + 4));
     return f;
   };
 
   // Block mode rescale, software-pipelined: the MFMAs of 16-row tile i give
   // P (fp32 partial products of this K block); P is folded into the
-  // accumulators (acc += P * s_a * s_w) while the MFMAs of tile i + 1 run.
-  // The last tile's P is folded at the start of the next K block (or before
-  // the epilogue).
+  // accumulators (acc += P * s_a * s_w, one scale per lane) while the MFMAs
+  // of tile i + 1 run.  The last tile's P is folded during the first tile of
+  // the next K block (or before the epilogue).
   v4f Pq[TN];
-  float scq[4] = {0.f, 0.f, 0.f, 0.f};
+  float cq = 0.f;
 #pragma unroll
   for (int j = 0; j < TN; ++j) Pq[j] = v4f{0.f, 0.f, 0.f, 0.f};
-  auto fold = [&](auto I) {
+  auto fold_one = [&](auto I, int j) {
     constexpr int i = decltype(I)::value;
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(Pq[j][r], scq[r], acc[i][j][r]);
+    for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(Pq[j][r], cq, acc[i][j][r]);
   };
 
-  const int arow = wm * WTM + (lane & 15);           // fragment row of 16-row tile 0
-  const int brow = wn * WTN + (lane & 15);
-  auto compute = [&](int st) {
+  const int arow = wm * WTM + l16;            // fragment row of 16-row tile 0
+  const int brow = wn * WTN + l16;
+
+  // Operands carried from one K block to the next: the weight fragments, the
+  // first activation fragment and the scales of the block about to be
+  // multiplied are read from LDS while the previous block's last MFMAs run.
+  Frag fb[TN], fa;
+  uint32_t sav[TM] = {}, swb[TN] = {};    // activation / weight scale words
+  float swv = 0.f;                        // block mode: this wave's weight scale
+  auto load_regs = [&](int st) {
     const uint8_t* a = smem + st * STAGE;
     const uint8_t* w = a + ABYTES;
-    const uint32_t* sa = reinterpret_cast<const uint32_t*>(a + SA_OFF);
-    const uint32_t* sw = reinterpret_cast<const uint32_t*>(a + SW_OFF);
-    Frag fb[TN];
 #pragma unroll
     for (int j = 0; j < TN; ++j) fb[j] = read_frag(w, brow + 16 * j);
-    if constexpr (MODE == MODE_BLOCK) {
-      const float swv = __uint_as_float(sw[wave * 64 + (wn * WTN) / 128]);
-      // rows 4*(lane/16) + r of a 16-row tile are consecutive scale words
-      const int srow0 = wm * WTM + 4 * (lane >> 4);
-      Frag fa = read_frag(a, arow);
-      uint4 sx4 = *reinterpret_cast<const uint4*>(sa + s_word(srow0));
-      static_for<TM>([&](auto I) {
-        constexpr int i = decltype(I)::value;
-        Frag fn;
-        uint4 sxn;
-        if constexpr (i + 1 < TM) {
-          fn = read_frag(a, arow + 16 * (i + 1));
-          sxn = *reinterpret_cast<const uint4*>(sa + s_word(srow0 + 16 * (i + 1)));
-        }
-        v4f Pn[TN];
-#pragma unroll
-        for (int j = 0; j < TN; ++j) Pn[j] = mfma_plain(fa.v, fb[j].v, v4f{0.f, 0.f, 0.f, 0.f});
-        fold(std::integral_constant<int, (i == 0 ? TM - 1 : i - 1)>{});
-#pragma unroll
-        for (int j = 0; j < TN; ++j) Pq[j] = Pn[j];
-        scq[0] = __uint_as_float(sx4.x) * swv;
-        scq[1] = __uint_as_float(sx4.y) * swv;
-        scq[2] = __uint_as_float(sx4.z) * swv;
-        scq[3] = __uint_as_float(sx4.w) * swv;
-        if constexpr (i + 1 < TM) {
-          fa = fn;
-          sx4 = sxn;
-        }
-      });
-    } else if constexpr (MODE == MODE_TENSOR) {
-      static_for<TM>([&](auto I) {
-        constexpr int i = decltype(I)::value;
-        const Frag fa = read_frag(a, arow + 16 * i);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma_plain(fa.v, fb[j].v, acc[i][j]);
-      });
-    } else {
-      const int sh = 8 * (lane >> 4);
-      int swb[TN];
-#pragma unroll
-      for (int j = 0; j < TN; ++j) swb[j] = (sw[s_word(brow + 16 * j)] >> sh) & 0xFF;
-      static_for<TM>([&](auto I) {
-        constexpr int i = decltype(I)::value;
-        const Frag fa = read_frag(a, arow + 16 * i);
-        const int sab = (sa[s_word(arow + 16 * i)] >> sh) & 0xFF;
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma_mx(fa.v, fb[j].v, acc[i][j], sab, swb[j]);
-      });
-    }
+    fa = read_frag(a, arow);
+    if constexpr (MODE != MODE_TENSOR)
+      read_words(reinterpret_cast<const uint32_t*>(a + SA_OFF) + wm * WTM + l16 * TM, sav,
+                 std::integral_constant<int, TM>{});
+    if constexpr (MODE == MODE_BLOCK)
+      swv = __uint_as_float(reinterpret_cast<const uint32_t*>(a + SW_OFF)[(wn * WTN) / 128]);
+    if constexpr (MODE == MODE_MX)
+      read_words(reinterpret_cast<const uint32_t*>(a + SW_OFF) + wn * WTN + l16 * TN, swb,
+                 std::integral_constant<int, TN>{});
   };
 
-  // Main loop, one K block per iteration: wait for this wave's loads of
-  // block kb, barrier (every wave's part of block kb has landed and no wave
-  // still reads the stage of block kb-1), refill that stage with block kb+1,
-  // multiply block kb.
-  // The two prefetch touches issued after a step's loads may stay in flight.
+  // The MFMAs (and block-mode folds) of 16-row tile i of the block in stage
+  // st; fa holds its activation fragment and the next one is read meanwhile.
+  auto tile = [&](auto I, int st) {
+    constexpr int i = decltype(I)::value;
+    const uint8_t* a = smem + st * STAGE;
+    Frag fn;
+    if constexpr (i + 1 < TM) fn = read_frag(a, arow + 16 * (i + 1));
+    if constexpr (MODE == MODE_BLOCK) {
+      // fold column tile j of the previous 16-row tile (its MFMA was issued
+      // TN MFMAs ago), then reuse its registers for this tile's product
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        fold_one(std::integral_constant<int, (i == 0 ? TM - 1 : i - 1)>{}, j);
+        Pq[j] = mfma_plain(fb[j].v, fa.v, v4f{0.f, 0.f, 0.f, 0.f});
+        // keep this order of FMAs and MFMAs (only LDS reads and scalar
+        // instructions may move across): the scheduler would otherwise
+        // hoist folds next to the MFMAs whose results they read
+        __builtin_amdgcn_sched_barrier(0x0104);
+      }
+      cq = __uint_as_float(sav[i]) * swv;
+    } else if constexpr (MODE == MODE_TENSOR) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma_plain(fb[j].v, fa.v, acc[i][j]);
+    } else {
+      // scale byte of this lane's 32-wide K block (lane / 16) in each word
+      const int sh = 8 * lq;
+      const int sab = (int)((sav[i] >> sh) & 0xFF);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = mfma_mx(fb[j].v, fa.v, acc[i][j], (int)((swb[j] >> sh) & 0xFF), sab);
+    }
+    if constexpr (i + 1 < TM) fa = fn;
+  };
+
+  // Main loop.  Block kb sits in stage kb % 2 and block kb + 1 is being
+  // loaded into the other stage.  Once this wave has issued its last LDS
+  // read of block kb (the fragment of the last 16-row tile), it waits for its
+  // own loads of block kb + 1 and meets the other waves at the barrier: after
+  // it, block kb + 1 is complete in LDS and nobody reads stage kb % 2 any
+  // more, which is refilled with block kb + 2.  The last tile's MFMAs then
+  // overlap the reads of block kb + 1's first operands.  The two prefetch
+  // touches issued after a block's loads are the only loads issued after
+  // them, hence the wait for at most 2 loads in flight.
   static_assert(T::NS == 2, "the wait count below assumes two stages");
   issue(0, 0);
   prefetch(PFD - 1);
-  int cs = 0;
-  for (int kb = 0; kb < p.KB; ++kb) {
-    wait_vmcnt_barrier<2>();
-    issue(cs ^ 1, kb + 1);
-    prefetch(kb + PFD);
-    compute(cs);
-    cs ^= 1;
+  wait_vmcnt_barrier<2>();
+  issue(1, 1);
+  prefetch(PFD);
+  load_regs(0);
+  for (int kb = 0; kb < KB; ++kb) {
+    const int st = kb & 1;
+    static_for<TM>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      if constexpr (i == TM - 1) {
+        wait_vmcnt_barrier<2>();
+        issue(st, kb + 2);
+        prefetch(kb + 1 + PFD);
+      }
+      tile(I, st);
+    });
+    // keep the next block's reads behind the last tile's MFMAs, which still
+    // read the weight fragments being replaced
+    __builtin_amdgcn_sched_barrier(0);
+    load_regs(st ^ 1);
   }
-  // the predicated-off loads still write LDS: let them land before exit
+  // the prefetch touches still write the LDS sink: let them land before exit
   wait_vmcnt<0>();
-  if constexpr (MODE == MODE_BLOCK) fold(std::integral_constant<int, TM - 1>{});
+  if constexpr (MODE == MODE_BLOCK) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fold_one(std::integral_constant<int, TM - 1>{}, j);
+  }
 
+  // Epilogue: four consecutive bf16 columns per lane and tile.
   float mul = 1.0f;
   if (MODE == MODE_TENSOR)
     mul = static_cast<const float*>(p.sa)[0] * static_cast<const float*>(p.sw)[0];
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
-    const int col = n0 + wn * WTN + 16 * j + (lane & 15);
-    const float b = (p.bias != nullptr && col < p.N) ? __uint_as_float((uint32_t)p.bias[col] << 16) : 0.0f;
+    const int col = n0 + wn * WTN + 16 * j + 4 * lq;
+    float b[4] = {0.f, 0.f, 0.f, 0.f};
+    if (p.bias != nullptr) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
-      store_tile_bf16(p, acc[i][j], m0 + wm * WTM + 16 * i + 4 * (lane >> 4), col, mul, b);
+      for (int r = 0; r < 4; ++r)
+        if (col + r < p.N) b[r] = __uint_as_float((uint32_t)p.bias[col + r] << 16);
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int row = m0 + wm * WTM + 16 * i + l16;
+      if (row >= p.M) continue;
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        v[r] = acc[i][j][r];
+        if (MODE == MODE_TENSOR) v[r] = v[r] * mul;
+        v[r] = v[r] + b[r];
+      }
+      uint16_t* yr = p.y + (int64_t)row * p.ldy;
+      if (col + 4 <= p.N) {
+        *reinterpret_cast<uint2*>(yr + col) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (col + r < p.N) yr[col + r] = (uint16_t)f32_to_bf16_bits(v[r]);
+      }
+    }
   }
 }
 
