@@ -47,6 +47,10 @@
 #ifndef FP8Q_PREFETCH_DISTANCE
 #define FP8Q_PREFETCH_DISTANCE 3
 #endif
+// 16-row tiles between the LDS read of an activation fragment and its use.
+#ifndef FP8Q_A_LOOKAHEAD
+#define FP8Q_A_LOOKAHEAD 1
+#endif
 
 namespace fp8q {
 
@@ -238,27 +242,32 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
   const i32x4 rS = wave_is_a ? rSA : rSW;
   const uint32_t smem_base = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 
-  // Fill stage `st` with K block kb.  Past the last block the descriptors
-  // cover nothing: the loads are still issued (every step issues the same
-  // number) but read nothing and write zeros into the free stage.
+  // Loads of one K block, numbered l = 0 .. NLD-1 (A_PER activation loads,
+  // W_PER weight loads, then the scale load).  issue_load(l, st, kb) fills
+  // its part of stage `st` with K block kb.  Past the last block the
+  // descriptors cover nothing: the loads are still issued (every block
+  // issues the same number) but read nothing and write zeros into the free
+  // stage.
   const int KB = p.KB;
-  auto issue = [&](int st, int kb) {
+  constexpr int NLD = A_PER + W_PER + T::SCALE_LOADS;
+  auto issue_load = [&](auto L, int st, int kb) {
+    constexpr int l = decltype(L)::value;
     const bool valid = kb < KB;
-    i32x4 ra = rA, rw = rW, rs = rS;
-    ra.z = valid ? ra.z : 0;
-    rw.z = valid ? rw.z : 0;
-    rs.z = valid ? rs.z : 0;
     const int kbv = valid ? kb : 0;
     const uint32_t base = smem_base + st * STAGE;
-    const uint32_t a = base + wave * A_PER * 1024;
-    const uint32_t w = base + ABYTES + wave * W_PER * 1024;
-    const uint32_t kofs = (uint32_t)kbv * 128u;
-#pragma unroll
-    for (int i = 0; i < A_PER; ++i) dma16(ra, a + i * 1024, offA[i], kofs);
-#pragma unroll
-    for (int i = 0; i < W_PER; ++i) dma16(rw, w + i * 1024, offW[i], kofs);
-    if constexpr (MODE != MODE_TENSOR)
-      dma4(rs, base + SA_OFF + wave * 256, offS, (uint32_t)kbv * kstepS);
+    if constexpr (l < A_PER) {
+      i32x4 r = rA;
+      r.z = valid ? r.z : 0;
+      dma16(r, base + (wave * A_PER + l) * 1024, offA[l], (uint32_t)kbv * 128u);
+    } else if constexpr (l < A_PER + W_PER) {
+      i32x4 r = rW;
+      r.z = valid ? r.z : 0;
+      dma16(r, base + ABYTES + (wave * W_PER + l - A_PER) * 1024, offW[l - A_PER], (uint32_t)kbv * 128u);
+    } else {
+      i32x4 r = rS;
+      r.z = valid ? r.z : 0;
+      dma4(r, base + SA_OFF + wave * 256, offS, (uint32_t)kbv * kstepS);
+    }
   };
   // L2 prefetch.  Tiles running together on one XCD share operand rows: the
   // NTN tiles of a tile row read the same A rows, the 8 tiles of a tile
@@ -339,9 +348,13 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
   const int brow = wn * WTN + l16;
 
   // Operands carried from one K block to the next: the weight fragments, the
-  // first activation fragment and the scales of the block about to be
+  // first LA activation fragments and the scales of the block about to be
   // multiplied are read from LDS while the previous block's last MFMAs run.
-  Frag fb[TN], fa;
+  // Activation fragments live in a ring of LA + 1 registers sets: the one of
+  // 16-row tile i is read LA tiles before its MFMAs.
+  constexpr int LA = TM > FP8Q_A_LOOKAHEAD ? FP8Q_A_LOOKAHEAD : TM - 1 > 0 ? TM - 1 : 1;
+  static_assert(LA >= 1 && LA < TM, "activation fragment lookahead");
+  Frag fb[TN], fr[LA + 1];
   uint32_t sav[TM] = {}, swb[TN] = {};    // activation / weight scale words
   float swv = 0.f;                        // block mode: this wave's weight scale
   auto load_regs = [&](int st) {
@@ -349,7 +362,8 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
     const uint8_t* w = a + ABYTES;
 #pragma unroll
     for (int j = 0; j < TN; ++j) fb[j] = read_frag(w, brow + 16 * j);
-    fa = read_frag(a, arow);
+#pragma unroll
+    for (int i = 0; i < LA; ++i) fr[i] = read_frag(a, arow + 16 * i);
     if constexpr (MODE != MODE_TENSOR)
       read_words(reinterpret_cast<const uint32_t*>(a + SA_OFF) + wm * WTM + l16 * TM, sav,
                  std::integral_constant<int, TM>{});
@@ -361,12 +375,12 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
   };
 
   // The MFMAs (and block-mode folds) of 16-row tile i of the block in stage
-  // st; fa holds its activation fragment and the next one is read meanwhile.
+  // st; the activation fragment of tile i + LA is read meanwhile.
   auto tile = [&](auto I, int st) {
     constexpr int i = decltype(I)::value;
     const uint8_t* a = smem + st * STAGE;
-    Frag fn;
-    if constexpr (i + 1 < TM) fn = read_frag(a, arow + 16 * (i + 1));
+    if constexpr (i + LA < TM) fr[(i + LA) % (LA + 1)] = read_frag(a, arow + 16 * (i + LA));
+    const Frag& fa = fr[i % (LA + 1)];
     if constexpr (MODE == MODE_BLOCK) {
       // fold column tile j of the previous 16-row tile (its MFMA was issued
       // TN MFMAs ago), then reuse its registers for this tile's product
@@ -391,7 +405,6 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
       for (int j = 0; j < TN; ++j)
         acc[i][j] = mfma_mx(fb[j].v, fa.v, acc[i][j], (int)((swb[j] >> sh) & 0xFF), sab);
     }
-    if constexpr (i + 1 < TM) fa = fn;
   };
 
   // Main loop.  Block kb sits in stage kb % 2 and block kb + 1 is being
@@ -399,25 +412,44 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
   // read of block kb (the fragment of the last 16-row tile), it waits for its
   // own loads of block kb + 1 and meets the other waves at the barrier: after
   // it, block kb + 1 is complete in LDS and nobody reads stage kb % 2 any
-  // more, which is refilled with block kb + 2.  The last tile's MFMAs then
+  // more, which is refilled with block kb + 2.  The last LA tiles' MFMAs then
   // overlap the reads of block kb + 1's first operands.  The two prefetch
   // touches issued after a block's loads are the only loads issued after
-  // them, hence the wait for at most 2 loads in flight.
+  // them, hence the wait for at most 2 loads in flight.  (SLOTS - 1 < TM - LA:
+  // every slot of block kb + 1 is issued before that barrier.)
   static_assert(T::NS == 2, "the wait count below assumes two stages");
-  issue(0, 0);
-  prefetch(PFD - 1);
+  // The loads of a block are spread over SLOTS issue points: slot 0 right
+  // after the barrier that frees their stage, slot s >= 1 before 16-row tile
+  // s - 1 of the next block, so that the vector-memory queue never receives
+  // a whole block's loads at once (a full queue stalls the issuing wave and
+  // with it its MFMAs).  The prefetch touches follow the last slot.
+  constexpr int SLOTS = 1 + (TM - LA - 1 < 4 ? TM - LA - 1 : 4);
+  constexpr int PER = (NLD + SLOTS - 1) / SLOTS;
+  auto issue_slot = [&](auto S, int st, int kb) {
+    constexpr int sl = decltype(S)::value;
+    static_for<NLD>([&](auto L) {
+      if constexpr (decltype(L)::value / PER == sl) issue_load(L, st, kb);
+    });
+    if constexpr (sl == SLOTS - 1) prefetch(kb + PFD - 1);
+  };
+  auto issue_all = [&](int st, int kb) {
+    static_for<NLD>([&](auto L) { issue_load(L, st, kb); });
+    prefetch(kb + PFD - 1);
+  };
+  issue_all(0, 0);
   wait_vmcnt_barrier<2>();
-  issue(1, 1);
-  prefetch(PFD);
+  static_for<SLOTS>([&](auto S) { if constexpr (decltype(S)::value == 0) issue_slot(S, 1, 1); });
   load_regs(0);
   for (int kb = 0; kb < KB; ++kb) {
     const int st = kb & 1;
     static_for<TM>([&](auto I) {
       constexpr int i = decltype(I)::value;
-      if constexpr (i == TM - 1) {
+      // the rest of block kb + 1's loads (its slot 0 was issued at the
+      // previous barrier)
+      if constexpr (i + 1 < SLOTS) issue_slot(std::integral_constant<int, i + 1>{}, st ^ 1, kb + 1);
+      if constexpr (i == TM - LA) {
         wait_vmcnt_barrier<2>();
-        issue(st, kb + 2);
-        prefetch(kb + 1 + PFD);
+        issue_slot(std::integral_constant<int, 0>{}, st, kb + 2);
       }
       tile(I, st);
     });
