@@ -51,6 +51,10 @@
 #ifndef FP8Q_A_LOOKAHEAD
 #define FP8Q_A_LOOKAHEAD 1
 #endif
+// Issue points after the first over which a K block's loads are spread.
+#ifndef FP8Q_LOAD_SLOTS
+#define FP8Q_LOAD_SLOTS 4
+#endif
 
 namespace fp8q {
 
@@ -423,7 +427,7 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
   // s - 1 of the next block, so that the vector-memory queue never receives
   // a whole block's loads at once (a full queue stalls the issuing wave and
   // with it its MFMAs).  The prefetch touches follow the last slot.
-  constexpr int SLOTS = 1 + (TM - LA - 1 < 4 ? TM - LA - 1 : 4);
+  constexpr int SLOTS = 1 + (TM - LA - 1 < FP8Q_LOAD_SLOTS ? TM - LA - 1 : FP8Q_LOAD_SLOTS);
   constexpr int PER = (NLD + SLOTS - 1) / SLOTS;
   auto issue_slot = [&](auto S, int st, int kb) {
     constexpr int sl = decltype(S)::value;
@@ -465,58 +469,99 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
     for (int j = 0; j < TN; ++j) fold_one(std::integral_constant<int, TM - 1>{}, j);
   }
 
-  // Epilogue: four consecutive bf16 columns per lane and tile.
+  // Epilogue.  After the MFMAs, lane (r16, q) = (lane % 16, lane / 16) holds
+  // for column tile j the four columns 16j + 4q + 0..3 of row r16 (+16i).
+  // The four lanes of a row exchange their bf16 pairs with two rounds of
+  // lane swaps (a 4 x 4 transpose over q and j), after which lane (r16, q)
+  // holds the sixteen contiguous columns 16q .. 16q + 15 and writes them as
+  // two 16-byte stores: half as many store instructions, each carrying
+  // 16-byte runs, as storing the MFMA layout directly.
+  static_assert(TN == 4, "the epilogue transpose is 4 x 4");
   float mul = 1.0f;
   if (MODE == MODE_TENSOR)
     mul = static_cast<const float*>(p.sa)[0] * static_cast<const float*>(p.sw)[0];
+  float bias[TN][4];
 #pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int col = n0 + wn * WTN + 16 * j + 4 * lq;
-    float b[4] = {0.f, 0.f, 0.f, 0.f};
-    if (p.bias != nullptr) {
+  for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (col + r < p.N) b[r] = __uint_as_float((uint32_t)p.bias[col + r] << 16);
+    for (int r = 0; r < 4; ++r) {
+      const int col = n0 + wn * WTN + 16 * j + 4 * lq + r;
+      bias[j][r] = (p.bias != nullptr && col < p.N) ? __uint_as_float((uint32_t)p.bias[col] << 16) : 0.0f;
     }
+  const int col0 = n0 + wn * WTN + 16 * lq;           // this lane's columns after the exchange
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int row = m0 + wm * WTM + 16 * i + l16;
-      if (row >= p.M) continue;
+  for (int i = 0; i < TM; ++i) {
+    // D[j][h]: bf16 pair h (columns 16j + 4q + 2h, +1) of column tile j
+    uint32_t d[TN][2];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
       float v[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         v[r] = acc[i][j][r];
         if (MODE == MODE_TENSOR) v[r] = v[r] * mul;
-        v[r] = v[r] + b[r];
+        v[r] = v[r] + bias[j][r];
       }
-      uint16_t* yr = p.y + (int64_t)row * p.ldy;
-      if (col + 4 <= p.N) {
-        *reinterpret_cast<uint2*>(yr + col) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-      } else {
+      d[j][0] = pack_bf16x2(v[0], v[1]);
+      d[j][1] = pack_bf16x2(v[2], v[3]);
+    }
+    // round 1 swaps lane halves (q 0,1 <-> q 2,3) between tiles j and j + 2,
+    // round 2 swaps lane quarters (q 1 <-> q 0, q 3 <-> q 2) between the
+    // results: e[x] then holds columns 16q + 4x + 0..3 (x = source lane q)
+    uint32_t e[4][2];
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (col + r < p.N) yr[col + r] = (uint16_t)f32_to_bf16_bits(v[r]);
+    for (int h = 0; h < 2; ++h) {
+      const auto s02 = __builtin_amdgcn_permlane32_swap(d[0][h], d[2][h], false, false);
+      const auto s13 = __builtin_amdgcn_permlane32_swap(d[1][h], d[3][h], false, false);
+      const auto t01 = __builtin_amdgcn_permlane16_swap(s02[0], s13[0], false, false);
+      const auto t23 = __builtin_amdgcn_permlane16_swap(s02[1], s13[1], false, false);
+      e[0][h] = t01[0];
+      e[1][h] = t01[1];
+      e[2][h] = t23[0];
+      e[3][h] = t23[1];
+    }
+    const int row = m0 + wm * WTM + 16 * i + l16;
+    if (row >= p.M) continue;
+    uint16_t* yr = p.y + (int64_t)row * p.ldy;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int c = col0 + 8 * half;
+      const uint4 o = make_uint4(e[2 * half][0], e[2 * half][1], e[2 * half + 1][0], e[2 * half + 1][1]);
+      if (c + 8 <= p.N) {
+        *reinterpret_cast<uint4*>(yr + c) = o;
+      } else {
+        const uint32_t w[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          if (c + t < p.N) yr[c + t] = (uint16_t)(w[t >> 1] >> ((t & 1) * 16));
       }
     }
   }
 }
 
-// Workgroups [0, full) take whole tiles (in XCD-contiguous group order);
-// the remaining tiles of that order are split into two half-height tiles,
-// one per workgroup.
+// Work items [0, full) are whole tiles (in XCD-contiguous group order); the
+// remaining tiles of that order are split into two half-height tiles, items
+// [full, items).  The kernel is persistent: workgroup g takes items g,
+// g + G, g + 2G, ... (G = gridDim.x, at most one workgroup per slot), so the
+// workgroups of a round start together and keep their XCD (item % 8), and no
+// workgroup is launched per tile.  Between two tiles no barrier is needed: a
+// wave reaches the next tile's first LDS write only after the last K-loop
+// barrier of the previous tile, after which nobody reads LDS data that is
+// still used, and the next tile's first barrier waits for every wave.
 template <class T>
-__global__ __launch_bounds__(T::NW * 64) void gemm_fast_kernel(GemmArgs p, int full) {
+__global__ __launch_bounds__(T::NW * 64) void gemm_fast_kernel(GemmArgs p, int full, int items) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES];
   const int total = p.tiles_m * p.tiles_n;
-  const int b = blockIdx.x;
-  int tm, tn;
-  if (b < full) {
-    group_walk(xcd_contiguous(b, full), p.tiles_m, p.tiles_n, tm, tn);
-    fast_tile<T, false>(p, smem, tm * T::BM, tn * T::BN, tm % 8, tn % T::NTN);
-  } else {
-    const int h = xcd_contiguous(b - full, 2 * (total - full));
-    group_walk(full + (h >> 1), p.tiles_m, p.tiles_n, tm, tn);
-    fast_tile<T, true>(p, smem, tm * T::BM + (h & 1) * (T::BM / 2), tn * T::BN, tm % 8, tn % T::NTN);
+  for (int b = blockIdx.x; b < items; b += gridDim.x) {
+    int tm, tn;
+    if (b < full) {
+      group_walk(xcd_contiguous(b, full), p.tiles_m, p.tiles_n, tm, tn);
+      fast_tile<T, false>(p, smem, tm * T::BM, tn * T::BN, tm % 8, tn % T::NTN);
+    } else {
+      const int h = xcd_contiguous(b - full, 2 * (total - full));
+      group_walk(full + (h >> 1), p.tiles_m, p.tiles_n, tm, tn);
+      fast_tile<T, true>(p, smem, tm * T::BM + (h & 1) * (T::BM / 2), tn * T::BN, tm % 8, tn % T::NTN);
+    }
   }
 }
 
@@ -585,12 +630,16 @@ template <int MODE>
 void launch_plan(GemmArgs p, const Plan& pl, hipStream_t stream) {
   p.tiles_m = pl.tiles_m;
   p.tiles_n = pl.tiles_n;
+  // persistent grid: one workgroup per slot (configuration 0 holds one
+  // workgroup per CU, configuration 1 two), never more than the items
+  const int slots = (pl.cfg == 0 ? 1 : 2) * cu_count();
+  const int grid = pl.grid < slots ? pl.grid : slots;
   if (pl.cfg == 0) {
     using T = FastTile<MODE, 256, 256, 2, 4, 4>;
-    hipLaunchKernelGGL(gemm_fast_kernel<T>, dim3(pl.grid), dim3(T::NW * 64), 0, stream, p, pl.full);
+    hipLaunchKernelGGL(gemm_fast_kernel<T>, dim3(grid), dim3(T::NW * 64), 0, stream, p, pl.full, pl.grid);
   } else {
     using T = FastTile<MODE, 128, 128, 2, 2, 8>;
-    hipLaunchKernelGGL(gemm_fast_kernel<T>, dim3(pl.grid), dim3(T::NW * 64), 0, stream, p, pl.full);
+    hipLaunchKernelGGL(gemm_fast_kernel<T>, dim3(grid), dim3(T::NW * 64), 0, stream, p, pl.full, pl.grid);
   }
 }
 
