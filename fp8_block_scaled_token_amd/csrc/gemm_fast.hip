@@ -155,8 +155,10 @@ struct FastTile {
   static constexpr int SW_OFF = SA_OFF + BM * 4;
   static constexpr int STAGE = ((SW_OFF + BN * 4) + 1023) / 1024 * 1024;
   static constexpr int NS = 2;
-  static constexpr int PF_OFF = NS * STAGE;            // 256 bytes per wave: prefetch sink
-  static constexpr int LDS_BYTES = PF_OFF + NW * 256;
+  // 1 KB per wave: sink for prefetch touches and for loads past the last K
+  // block, so that those never write a stage
+  static constexpr int SINK_OFF = NS * STAGE;
+  static constexpr int LDS_BYTES = SINK_OFF + NW * 1024;
   // scale loads: one 64-word load per wave covers the BM + BN scale words
   static constexpr int SCALE_LOADS = MODE == MODE_TENSOR ? 0 : 1;
   static_assert(NW * 64 == BM + BN, "one scale word per lane");
@@ -167,12 +169,19 @@ struct FastTile {
 
 // One tile: rows [m0, m0 + RM) x columns [n0, n0 + BN), RM = BM (full) or
 // BM / 2 (HALF).
+// `preloaded`: the previous tile of this workgroup already issued this tile's
+// first K block (and its touches) before its epilogue.  `has_next`: issue the
+// first K block of the next tile (nm0, nn0, ngm, ngn; same kind) before this
+// tile's epilogue, so that its latency overlaps the output stores.
 template <class T, bool HALF>
-__device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int m0, int n0, int gm, int gn) {
+__device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int m0, int n0, int gm, int gn,
+                                          bool preloaded, bool has_next, int nm0, int nn0, int ngm, int ngn) {
   constexpr int MODE = T::MODE, BM = T::BM, BN = T::BN, WN = T::WN, NW = T::NW;
   constexpr int RM = HALF ? T::BM / 2 : T::BM;
   constexpr int WTM = RM / T::WM, TM = WTM / 16, WTN = T::WTN, TN = T::TN;
-  constexpr int A_PER = T::A_PER, W_PER = T::W_PER, STAGE = T::STAGE;
+  // a half tile's activation rows are spread over all waves too
+  constexpr int A_PER = RM * 128 / 1024 / NW, W_PER = T::W_PER, STAGE = T::STAGE;
+  static_assert(A_PER >= 1 && A_PER * NW * 1024 == RM * 128, "whole 1 KB activation loads");
   constexpr int ABYTES = T::ABYTES, SA_OFF = T::SA_OFF, SW_OFF = T::SW_OFF;
   static_assert(TM >= 1, "wave tile at least 16 rows");
 
@@ -183,78 +192,96 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
   const i32x4 rA = rsrc(p.a, (int64_t)p.M * p.lda);
   const i32x4 rW = rsrc(p.w, (int64_t)p.N * p.ldw);
 
-  // ---- per-lane load offsets (fixed for the whole K loop)
+  // ---- per-lane load offsets of a tile (fixed for its whole K loop)
   // Load i of wave w fills LDS kilobyte (A_PER*w + i) of the A tile, i.e.
   // tile rows 8*(A_PER*w + i) + lane/8 with lane % 8 the physical chunk; the
   // logical chunk to fetch is (lane % 8) ^ (row % 8) = (lane % 8) ^ (lane / 8).
-  // A half tile needs only its first RM rows: the other loads are kept (for
-  // the vmcnt count) but read nothing.
-  const int lrow = lane >> 3, lchunk = (lane & 7) ^ (lane >> 3);
-  uint32_t offA[A_PER], offW[W_PER];
-#pragma unroll
-  for (int i = 0; i < A_PER; ++i) {
-    const int r = 8 * (A_PER * wave + i) + lrow;
-    offA[i] = (r < RM) ? (uint32_t)((m0 + r) * (int)p.lda + lchunk * 16) : OOB;
-  }
-#pragma unroll
-  for (int i = 0; i < W_PER; ++i)
-    offW[i] = (uint32_t)((n0 + 8 * (W_PER * wave + i) + lrow) * (int)p.ldw + lchunk * 16);
-
   // Scale words: lane l of wave w fetches word q = 64w + l of the stage's
   // scale area.  Activation words are ordered [wm][row % 16][row tile] so a
   // lane reads the TM scales of its rows as consecutive words; MX weight
   // words likewise [wn][row % 16][row tile].  Block mode: weight word b is
   // the scale of 128-column block n0/128 + b.
-  const bool wave_is_a = 64 * wave < BM;    // waves below BM/64 fetch activation scales
-  i32x4 rSA = rA, rSW = rW;
-  uint32_t offS = OOB;
-  uint32_t kstepS = 0;    // scalar offset advance per K block
-  if constexpr (MODE != MODE_TENSOR) {
-    const int q = 64 * wave + lane;
-    const bool is_a = q < BM;
-    if (MODE == MODE_BLOCK) {
-      rSA = rsrc(p.sa, (int64_t)p.M * p.KB * 4);
-      rSW = rsrc(p.sw, (int64_t)p.NB * p.KB * 4);
-    } else {
-      rSA = rsrc(p.sa, (int64_t)p.M * p.KB32);
-      rSW = rsrc(p.sw, (int64_t)p.N * p.KB32);
-    }
-    if (is_a) {
-      const int g = q / WTM, rem = q % WTM;               // q < RM only when g < WM
-      const int row = m0 + g * WTM + 16 * (rem % TM) + rem / TM;
-      const bool live = q < RM && row < p.M;
-      if (MODE == MODE_BLOCK)
-        offS = live ? (uint32_t)(p.sa_col_major ? row * 4 : row * p.KB * 4) : OOB;
-      else
-        offS = live ? (uint32_t)(row * p.KB32) : OOB;
-    } else {
-      const int qw = q - BM;
-      if (MODE == MODE_BLOCK) {
-        const int blk = n0 / 128 + qw;
-        offS = (qw < (BN + 127) / 128 && blk < p.NB) ? (uint32_t)(blk * p.KB * 4) : OOB;
+  // L2 prefetch rows: tiles running together on one XCD share operand rows:
+  // the NTN tiles of a tile row read the same A rows, the 8 tiles of a tile
+  // column (group_walk's group height) the same W rows.  Every workgroup
+  // touches one line (the 128 bytes of a K block) of its share of those rows.
+  constexpr int PFD = FP8Q_PREFETCH_DISTANCE;
+  constexpr int PA = RM / T::NTN / NW, PW = BN / 8 / NW;   // rows per wave
+  static_assert(PA >= 1 && PA <= 64 && PW >= 1 && PW <= 64, "prefetch slice");
+  struct Offs {
+    uint32_t a[A_PER], w[W_PER], s, pfa, pfw;
+  };
+  // `ln` is the lane index; the next tile's offsets are computed from an
+  // opaque copy of it so that no lane-dependent partial term of this tile's
+  // offsets is kept alive through the K loop for reuse
+  auto make_offs = [&](int tm0, int tn0, int tgm, int tgn, int ln) {
+    const int lrow = ln >> 3, lchunk = (ln & 7) ^ (ln >> 3);
+    Offs o;
+#pragma unroll
+    for (int i = 0; i < A_PER; ++i)
+      o.a[i] = (uint32_t)((tm0 + 8 * (A_PER * wave + i) + lrow) * (int)p.lda + lchunk * 16);
+#pragma unroll
+    for (int i = 0; i < W_PER; ++i)
+      o.w[i] = (uint32_t)((tn0 + 8 * (W_PER * wave + i) + lrow) * (int)p.ldw + lchunk * 16);
+    o.s = OOB;
+    if constexpr (MODE != MODE_TENSOR) {
+      const int q = 64 * wave + ln;
+      if (q < BM) {
+        const int g = q / WTM, rem = q % WTM;             // q < RM only when g < WM
+        const int row = tm0 + g * WTM + 16 * (rem % TM) + rem / TM;
+        const bool live = q < RM && row < p.M;
+        if (MODE == MODE_BLOCK)
+          o.s = live ? (uint32_t)(p.sa_col_major ? row * 4 : row * p.KB * 4) : OOB;
+        else
+          o.s = live ? (uint32_t)(row * p.KB32) : OOB;
       } else {
-        const int g = qw / WTN, rem = qw % WTN;
-        const int row = n0 + g * WTN + 16 * (rem % TN) + rem / TN;
-        offS = row < p.N ? (uint32_t)(row * p.KB32) : OOB;
+        const int qw = q - BM;
+        if (MODE == MODE_BLOCK) {
+          const int blk = tn0 / 128 + qw;
+          o.s = (qw < (BN + 127) / 128 && blk < p.NB) ? (uint32_t)(blk * p.KB * 4) : OOB;
+        } else {
+          const int g = qw / WTN, rem = qw % WTN;
+          const int row = tn0 + g * WTN + 16 * (rem % TN) + rem / TN;
+          o.s = row < p.N ? (uint32_t)(row * p.KB32) : OOB;
+        }
       }
     }
-    // the scalar offset of a K block: block-mode column-major activation
-    // scales advance by M words, every other scale array by one word (block)
-    // or four bytes (MX) per K block
-    kstepS = (MODE == MODE_BLOCK && p.sa_col_major && wave_is_a) ? (uint32_t)p.M * 4u : 4u;
+    const int pra = tm0 + tgn * (RM / T::NTN) + wave * PA + ln;
+    const int prw = tn0 + tgm * (BN / 8) + wave * PW + ln;
+    o.pfa = (PFD > 0 && ln < PA && pra < p.M) ? (uint32_t)pra * (uint32_t)p.lda : OOB;
+    o.pfw = (PFD > 0 && ln < PW && prw < p.N) ? (uint32_t)prw * (uint32_t)p.ldw : OOB;
+    return o;
+  };
+  const Offs cur = make_offs(m0, n0, gm, gn, lane);
+
+  const bool wave_is_a = 64 * wave < BM;    // waves below BM/64 fetch activation scales
+  i32x4 rSA = rA, rSW = rW;
+  if constexpr (MODE == MODE_BLOCK) {
+    rSA = rsrc(p.sa, (int64_t)p.M * p.KB * 4);
+    rSW = rsrc(p.sw, (int64_t)p.NB * p.KB * 4);
+  } else if constexpr (MODE == MODE_MX) {
+    rSA = rsrc(p.sa, (int64_t)p.M * p.KB32);
+    rSW = rsrc(p.sw, (int64_t)p.N * p.KB32);
   }
+  // the scalar offset of a K block: block-mode column-major activation
+  // scales advance by M words, every other scale array by one word (block)
+  // or four bytes (MX) per K block
+  const uint32_t kstepS =
+      (MODE == MODE_BLOCK && p.sa_col_major && wave_is_a) ? (uint32_t)p.M * 4u : 4u;
   const i32x4 rS = wave_is_a ? rSA : rSW;
   const uint32_t smem_base = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 
+  const uint32_t sink = smem_base + T::SINK_OFF + wave * 1024;
+
   // Loads of one K block, numbered l = 0 .. NLD-1 (A_PER activation loads,
-  // W_PER weight loads, then the scale load).  issue_load(l, st, kb) fills
-  // its part of stage `st` with K block kb.  Past the last block the
-  // descriptors cover nothing: the loads are still issued (every block
-  // issues the same number) but read nothing and write zeros into the free
-  // stage.
+  // W_PER weight loads, then the scale load).  issue_load(l, st, kb, o) fills
+  // its part of stage `st` with K block kb of the tile whose offsets are o.
+  // Past the last block the descriptors cover nothing: the loads are still
+  // issued (every block issues the same number) but read nothing and write
+  // zeros into this wave's sink.
   const int KB = p.KB;
   constexpr int NLD = A_PER + W_PER + T::SCALE_LOADS;
-  auto issue_load = [&](auto L, int st, int kb) {
+  auto issue_load = [&](auto L, int st, int kb, const Offs& o) {
     constexpr int l = decltype(L)::value;
     const bool valid = kb < KB;
     const int kbv = valid ? kb : 0;
@@ -262,42 +289,30 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
     if constexpr (l < A_PER) {
       i32x4 r = rA;
       r.z = valid ? r.z : 0;
-      dma16(r, base + (wave * A_PER + l) * 1024, offA[l], (uint32_t)kbv * 128u);
+      dma16(r, valid ? base + (wave * A_PER + l) * 1024 : sink, o.a[l], (uint32_t)kbv * 128u);
     } else if constexpr (l < A_PER + W_PER) {
       i32x4 r = rW;
       r.z = valid ? r.z : 0;
-      dma16(r, base + ABYTES + (wave * W_PER + l - A_PER) * 1024, offW[l - A_PER], (uint32_t)kbv * 128u);
+      dma16(r, valid ? base + ABYTES + (wave * W_PER + l - A_PER) * 1024 : sink, o.w[l - A_PER],
+            (uint32_t)kbv * 128u);
     } else {
       i32x4 r = rS;
       r.z = valid ? r.z : 0;
-      dma4(r, base + SA_OFF + wave * 256, offS, (uint32_t)kbv * kstepS);
+      dma4(r, valid ? base + SA_OFF + wave * 256 : sink, o.s, (uint32_t)kbv * kstepS);
     }
   };
-  // L2 prefetch.  Tiles running together on one XCD share operand rows: the
-  // NTN tiles of a tile row read the same A rows, the 8 tiles of a tile
-  // column (group_walk's group height) the same W rows.  Every workgroup
-  // touches one line (the 128 bytes of a K block) of its share of those rows,
-  // PFD K blocks ahead, so that the operand loads find them in L2.  The
-  // touches go to a per-wave LDS sink; they are issued after the operand
-  // loads of a step and may stay in flight until the next step's wait.
-  // Past the last K block the descriptors cover nothing and the touches read
-  // nothing.
-  constexpr int PFD = FP8Q_PREFETCH_DISTANCE;
-  constexpr int PA = RM / T::NTN / NW, PW = BN / 8 / NW;   // rows per wave
-  static_assert(PA >= 1 && PA <= 64 && PW >= 1 && PW <= 64, "prefetch slice");
-  const int pra = m0 + gn * (RM / T::NTN) + wave * PA + lane;
-  const int prw = n0 + gm * (BN / 8) + wave * PW + lane;
-  const uint32_t pfa = (PFD > 0 && lane < PA && pra < p.M) ? (uint32_t)pra * (uint32_t)p.lda : OOB;
-  const uint32_t pfw = (PFD > 0 && lane < PW && prw < p.N) ? (uint32_t)prw * (uint32_t)p.ldw : OOB;
-  const uint32_t pf_lds = smem_base + T::PF_OFF + wave * 256;
-  auto prefetch = [&](int kb) {
+  // L2 prefetch touches of K block kb (PFD blocks ahead of the loads they
+  // serve), into the sink; past the last K block they read nothing.  They are
+  // issued after the operand loads of a step and may stay in flight until
+  // the next step's wait.
+  auto prefetch = [&](int kb, const Offs& o) {
     const bool valid = PFD > 0 && kb < p.KB;
     i32x4 ra = rA, rw = rW;
     ra.z = valid ? ra.z : 0;
     rw.z = valid ? rw.z : 0;
     const uint32_t kofs = valid ? (uint32_t)kb * 128u : 0u;
-    dma4(ra, pf_lds, pfa, kofs);
-    dma4(rw, pf_lds, pfw, kofs);
+    dma4(ra, sink, o.pfa, kofs);
+    dma4(rw, sink, o.pfw, kofs);
   };
 
   // acc[i][j]: output rows m0 + wm*WTM + 16i + lane%16, columns
@@ -432,16 +447,22 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
   auto issue_slot = [&](auto S, int st, int kb) {
     constexpr int sl = decltype(S)::value;
     static_for<NLD>([&](auto L) {
-      if constexpr (decltype(L)::value / PER == sl) issue_load(L, st, kb);
+      if constexpr (decltype(L)::value / PER == sl) issue_load(L, st, kb, cur);
     });
-    if constexpr (sl == SLOTS - 1) prefetch(kb + PFD - 1);
+    if constexpr (sl == SLOTS - 1) prefetch(kb + PFD - 1, cur);
   };
-  auto issue_all = [&](int st, int kb) {
-    static_for<NLD>([&](auto L) { issue_load(L, st, kb); });
-    prefetch(kb + PFD - 1);
+  auto issue_all = [&](int st, int kb, const Offs& o) {
+    static_for<NLD>([&](auto L) { issue_load(L, st, kb, o); });
+    prefetch(kb + PFD - 1, o);
   };
-  issue_all(0, 0);
-  wait_vmcnt_barrier<2>();
+  if (preloaded) {
+    // block 0 was issued before the previous tile's output stores: wait for
+    // everything (the stores have had the loads' latency to drain)
+    wait_vmcnt_barrier<0>();
+  } else {
+    issue_all(0, 0, cur);
+    wait_vmcnt_barrier<2>();
+  }
   static_for<SLOTS>([&](auto S) { if constexpr (decltype(S)::value == 0) issue_slot(S, 1, 1); });
   load_regs(0);
   for (int kb = 0; kb < KB; ++kb) {
@@ -458,12 +479,20 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
       tile(I, st);
     });
     // keep the next block's reads behind the last tile's MFMAs, which still
-    // read the weight fragments being replaced
+    // read the weight fragments being replaced.  After the last block this
+    // reads a stale stage (possibly while the next tile's first loads land
+    // in it): harmless, the values are never used, and reading
+    // unconditionally keeps the old and new fragments from being live at once.
     __builtin_amdgcn_sched_barrier(0);
     load_regs(st ^ 1);
   }
-  // the prefetch touches still write the LDS sink: let them land before exit
-  wait_vmcnt<0>();
+  // After the last barrier of the K loop no wave reads a stage any more:
+  // start the next tile's first K block now.
+  if (has_next) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    issue_all(0, 0, make_offs(nm0, nn0, ngm, ngn, ln));
+  }
   if constexpr (MODE == MODE_BLOCK) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) fold_one(std::integral_constant<int, TM - 1>{}, j);
@@ -545,24 +574,44 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
 // g + G, g + 2G, ... (G = gridDim.x, at most one workgroup per slot), so the
 // workgroups of a round start together and keep their XCD (item % 8), and no
 // workgroup is launched per tile.  Between two tiles no barrier is needed: a
-// wave reaches the next tile's first LDS write only after the last K-loop
-// barrier of the previous tile, after which nobody reads LDS data that is
-// still used, and the next tile's first barrier waits for every wave.
+// wave issues the next tile's first LDS writes only after the last K-loop
+// barrier of the previous tile, after which nobody reads a stage, and the
+// next tile's first barrier waits for every wave.
 template <class T>
 __global__ __launch_bounds__(T::NW * 64) void gemm_fast_kernel(GemmArgs p, int full, int items) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES];
   const int total = p.tiles_m * p.tiles_n;
-  for (int b = blockIdx.x; b < items; b += gridDim.x) {
+  // item -> tile origin and prefetch group coordinates; true for a half tile
+  auto decode = [&](int x, int& m0, int& n0, int& gm, int& gn) {
     int tm, tn;
-    if (b < full) {
-      group_walk(xcd_contiguous(b, full), p.tiles_m, p.tiles_n, tm, tn);
-      fast_tile<T, false>(p, smem, tm * T::BM, tn * T::BN, tm % 8, tn % T::NTN);
+    if (x < full) {
+      group_walk(xcd_contiguous(x, full), p.tiles_m, p.tiles_n, tm, tn);
+      m0 = tm * T::BM;
     } else {
-      const int h = xcd_contiguous(b - full, 2 * (total - full));
+      const int h = xcd_contiguous(x - full, 2 * (total - full));
       group_walk(full + (h >> 1), p.tiles_m, p.tiles_n, tm, tn);
-      fast_tile<T, true>(p, smem, tm * T::BM + (h & 1) * (T::BM / 2), tn * T::BN, tm % 8, tn % T::NTN);
+      m0 = tm * T::BM + (h & 1) * (T::BM / 2);
     }
+    n0 = tn * T::BN;
+    gm = tm % 8;
+    gn = tn % T::NTN;
+    return x >= full;
+  };
+  bool preloaded = false;
+  for (int b = blockIdx.x; b < items; b += gridDim.x) {
+    int m0, n0, gm, gn, nm0 = 0, nn0 = 0, ngm = 0, ngn = 0;
+    const bool half = decode(b, m0, n0, gm, gn);
+    const int nb = b + gridDim.x;
+    const bool has_next = nb < items && decode(nb, nm0, nn0, ngm, ngn) == half;
+    if (!half)
+      fast_tile<T, false>(p, smem, m0, n0, gm, gn, preloaded, has_next, nm0, nn0, ngm, ngn);
+    else
+      fast_tile<T, true>(p, smem, m0, n0, gm, gn, preloaded, has_next, nm0, nn0, ngm, ngn);
+    preloaded = has_next;
   }
+  // the last touches and past-the-end loads still write the LDS sink: let
+  // them land before the workgroup ends
+  wait_vmcnt<0>();
 }
 
 namespace {
