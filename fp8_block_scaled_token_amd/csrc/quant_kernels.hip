@@ -65,11 +65,18 @@ __device__ __forceinline__ void group_scales(const float (&amax)[CH], float (&s)
   }
 }
 
+// Codes of 8 values with a scale derived from their group's (or block's, or
+// tensor's) maximum: |x| <= amax and s = RN(max(amax, 1e-10)/448) >=
+// (amax/448)(1 - 2^-24), so |x/s| <= 448 (1 + 2^-23) < 464.  The hardware
+// conversion rounds every magnitude up to 464 to nearest-even E4M3 and so
+// maps (448, 464) to 448 itself (measured on gfx950): the saturating clamp of
+// the quantization formula is implied and not executed here.  (Static scales,
+// which bound nothing, clamp explicitly.)
 __device__ __forceinline__ uint2 quant8(const uint4& raw, float s, float r) {
   float v[8], t[8];
   unpack8(raw, v);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) t[e] = clamp448(div_by_scale(v[e], s, r));
+  for (int e = 0; e < 8; ++e) t[e] = div_by_scale(v[e], s, r);
   return encode8(t);
 }
 
@@ -300,18 +307,31 @@ __device__ __forceinline__ double sumsq_seg(const uint4 (&raw)[CH], double ss) {
 // r = fp32(1 / sqrt(sum / K + eps)) from the wave partials; `part` holds one
 // slot per wave, written here, and the caller's barrier discipline keeps a
 // slot set from being overwritten while another wave still reads it.
-__device__ __forceinline__ float rms_inv(double ss, double* part, int64_t K, float eps) {
+// fp32 rounding of 1/sqrt(v) for v > 0 (normal): the hardware estimate
+// refined by two Newton steps in fp64, y <- y + y (1/2 - (v/2) y^2), each of
+// which squares the relative error, to within a few fp64 ulps of the exact
+// value; the fp32 rounding is then that of the exact value unless this lies
+// within about 2^-50 of an fp32 rounding boundary.
+__device__ __forceinline__ float rsqrt_f64_to_f32(double v) {
+  const double h = 0.5 * v;
+  double y = __builtin_amdgcn_rsq(v);
+  y = __builtin_fma(y, __builtin_fma(-h * y, y, 0.5), y);
+  y = __builtin_fma(y, __builtin_fma(-h * y, y, 0.5), y);
+  return (float)y;
+}
+
+__device__ __forceinline__ float rms_inv(double ss, double* part, double inv_k, float eps) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   ss = sum_wave_f64(ss);
   if (lane == 0) part[wave] = ss;
   __syncthreads();
   ss = ((part[0] + part[1]) + part[2]) + part[3];
-  return (float)(1.0 / sqrt(ss / (double)K + (double)eps));
+  return rsqrt_f64_to_f32(__builtin_fma(ss, inv_k, (double)eps));
 }
 
 // y = bf16((x * r) * g) for one segment, then its group quantization.
 template <int CH>
-__device__ __forceinline__ void norm_quant_seg(const RmsArgs& a, uint4 (&raw)[CH], const uint4 (&gr)[CH],
+__device__ __forceinline__ void norm_quant_seg(const RmsArgs& a, uint4 (&raw)[CH], const float (&gf)[CH][8],
                                                float rn, int64_t row, int64_t seg0) {
   const int lane = threadIdx.x & 63;
   const int64_t K = a.K;
@@ -322,9 +342,9 @@ __device__ __forceinline__ void norm_quant_seg(const RmsArgs& a, uint4 (&raw)[CH
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int64_t k0 = seg0 + 512 * c + 8 * lane;
-    float v[8], g[8];
+    float v[8];
     unpack8(raw[c], v);
-    unpack8(gr[c], g);
+    const float* g = gf[c];
     uint32_t yb[4];
 #pragma unroll
     for (int e = 0; e < 8; e += 2) yb[e >> 1] = pack_bf16x2((v[e] * rn) * g[e], (v[e + 1] * rn) * g[e + 1]);
@@ -355,17 +375,28 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_rows_kernel(RmsArgs a, int 
   const int64_t r1 = r0 + rows_per_wg < a.M ? r0 + rows_per_wg : a.M;
   if (r0 >= a.M) return;                       // whole workgroup
   const int64_t seg0 = (int64_t)wave * (512 * CH);
-  uint4 gr[CH], cur[CH], nxt[CH];
-  load_row_seg<CH>(gr, a.gamma, seg0, a.K);
+  uint4 cur[CH], nxt[CH];
+  float gf[CH][8];          // gamma of this wave's segment, unpacked once
+  {
+    uint4 gr[CH];
+    load_row_seg<CH>(gr, a.gamma, seg0, a.K);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) unpack8(gr[c], gf[c]);
+  }
   load_row_seg<CH>(cur, a.x + r0 * a.ldx, seg0, a.K);
-  for (int64_t row = r0; row < r1; ++row) {
-    if (row + 1 < r1) load_row_seg<CH>(nxt, a.x + (row + 1) * a.ldx, seg0, a.K);
+  const double inv_k = 1.0 / (double)a.K;
+  // one row: its successor's loads go into the other buffer first
+  auto step = [&](uint4 (&buf)[CH], uint4 (&other)[CH], int64_t row) {
+    if (row + 1 < r1) load_row_seg<CH>(other, a.x + (row + 1) * a.ldx, seg0, a.K);
     // the two slot sets alternate; the barrier inside rms_inv of row i+1
     // orders every read of set (i & 1) before the writes of row i+2
-    const float rn = rms_inv(sumsq_seg<CH>(cur, 0.0), part[(row - r0) & 1], a.K, a.eps);
-    if (seg0 < a.K) norm_quant_seg<CH>(a, cur, gr, rn, row, seg0);
-#pragma unroll
-    for (int c = 0; c < CH; ++c) cur[c] = nxt[c];
+    const float rn = rms_inv(sumsq_seg<CH>(buf, 0.0), part[(row - r0) & 1], inv_k, a.eps);
+    if (seg0 < a.K) norm_quant_seg<CH>(a, buf, gf, rn, row, seg0);
+  };
+  // rows alternate between the two buffers (no copies between rows)
+  for (int64_t row = r0; row < r1; row += 2) {
+    step(cur, nxt, row);
+    if (row + 1 < r1) step(nxt, cur, row + 1);
   }
 }
 
@@ -383,13 +414,16 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(RmsArgs a) {
     load_row_seg<CH>(raw, xr, (4 * it + wave) * SEG, a.K);
     ss = sumsq_seg<CH>(raw, ss);
   }
-  const float rn = rms_inv(ss, part, a.K, a.eps);
+  const float rn = rms_inv(ss, part, 1.0 / (double)a.K, a.eps);
   for (int64_t it = 0; it < npass; ++it) {
     const int64_t seg0 = (4 * it + wave) * SEG;
     if (seg0 >= a.K) break;
     load_row_seg<CH>(raw, xr, seg0, a.K);
     load_row_seg<CH>(gr, a.gamma, seg0, a.K);
-    norm_quant_seg<CH>(a, raw, gr, rn, row, seg0);
+    float gf[CH][8];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) unpack8(gr[c], gf[c]);
+    norm_quant_seg<CH>(a, raw, gf, rn, row, seg0);
   }
 }
 
@@ -515,7 +549,10 @@ hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, float 
   }
   // four workgroups per CU, each a run of consecutive rows (measured best
   // against two per CU and against one workgroup per row)
-  const int64_t wgs = (int64_t)device_cu_count() * 4;
+#ifndef FP8Q_RMS_WGS_PER_CU
+#define FP8Q_RMS_WGS_PER_CU 4
+#endif
+  const int64_t wgs = (int64_t)device_cu_count() * FP8Q_RMS_WGS_PER_CU;
   const int rows = (int)ceil_div(M, wgs);
   const dim3 grid((unsigned)ceil_div(M, rows));
 #define FP8Q_RMS(CH) hipLaunchKernelGGL((rmsnorm_quant_rows_kernel<CH>), grid, block, 0, stream, a, rows)

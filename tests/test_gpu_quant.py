@@ -180,6 +180,44 @@ def test_rmsnorm_quant_parity(M, K, layout):
         assert any(match), f"row {i}"
 
 
+# Without the y output, row lengths that are multiples of 2048 take the
+# one-wave-per-row kernel: fewer rows than waves, a ragged share of rows per
+# wave, and every row length it is built for (padded rows, canaries).
+@pytest.mark.parametrize("M,K", [(5, 2048), (64, 4096), (2500, 6144), (37, 8192), (3100, 6144),
+                                 (1, 6144), (300, 2048)])
+@pytest.mark.parametrize("layout", [0, 1])
+def test_rmsnorm_quant_no_y_parity(M, K, layout):
+    log(f"rmsnorm_quant (no y) M={M} K={K} layout={layout}")
+    m = fq()
+    x = workloads.activations(M, K, seed=K + 21, outlier_frac=0.001)
+    g = workloads.gamma(K, seed=K + 22)
+    eps = 1e-6
+    xb, xd = padded(M, K, torch.bfloat16, 8, CANARY_BF16)
+    xd.copy_(x.cuda())
+    qb, q = padded(M, K, torch.uint8, 16, CANARY_U8)
+    G = -(-K // 128)
+    s = torch.empty((G, M) if layout else (M, G), dtype=torch.float32, device="cuda")
+    m.fp8q_rmsnorm_quant(xd, g.cuda(), eps, layout, q, s, None)
+    torch.cuda.synchronize()
+    assert canary_intact(qb, K, CANARY_U8)
+    qg, sg = q.cpu().numpy(), s.cpu().numpy()
+    if layout:
+        sg = sg.T
+    xh, gh = bf16_host(x), bf16_host(g)
+    ref, amb = _rms_expected(xh, gh, eps, None)
+    ok = np.ones(M, bool)
+    ok[amb] = False
+    np.testing.assert_array_equal(qg[ok], ref["q"][ok])
+    np.testing.assert_array_equal(sg[ok], ref["s"][ok])
+    for i in amb:   # either neighbour of r, then bit-exact for that r
+        r_alt = ref["r"].copy()
+        r_alt[i] = ref["r_alt"][i]
+        alt = oq.rmsnorm_quant(xh, gh, eps, r=r_alt)
+        match = [np.array_equal(qg[i], cand["q"][i]) and np.array_equal(sg[i], cand["s"][i])
+                 for cand in (ref, alt)]
+        assert any(match), f"row {i}"
+
+
 @pytest.mark.parametrize("layout", [0, 1])
 def test_rmsnorm_quant_full_size_sampled_rows(layout):
     # layout 1 is the bench's launch configuration
