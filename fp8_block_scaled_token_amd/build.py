@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfp8q.so")
 
-SOURCES = ["api.cpp", "quant_kernels.hip", "gemm_kernels.hip", "gemm_fast.hip"]
+SOURCES = ["api.cpp", "quant_kernels.hip", "gemm_kernels.hip", "gemm_fast.hip", "gemm_decode.hip"]
 
 ARCH = "gfx950"
 
@@ -27,6 +27,7 @@ ARCH = "gfx950"
 EXTRA_FLAGS = {
     # MFMA results feed VALU rescale FMAs: keep them in VGPRs, not AGPRs
     "gemm_fast.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "gemm_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -112,4 +112,8 @@ __device__ __forceinline__ void store_tile_bf16(const GemmArgs& p, const v4f& ac
 bool gemm_fast_eligible(const GemmArgs& p, int mode);
 hipError_t launch_gemm_fast(GemmArgs p, int mode, hipStream_t stream);
 
+// Decode path (gemm_decode.hip): shapes it accepts, and its launcher.
+bool gemm_decode_eligible(const GemmArgs& p);
+hipError_t launch_gemm_decode(GemmArgs p, int mode, hipStream_t stream);
+
 }  // namespace fp8q

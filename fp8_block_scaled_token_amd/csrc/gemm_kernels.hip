@@ -340,6 +340,7 @@ static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 template <int MODE>
 static hipError_t launch_mode(GemmArgs p, hipStream_t stream) {
+  if (p.M <= 64 && gemm_decode_eligible(p)) return launch_gemm_decode(p, MODE, stream);
   if (p.M <= 64) {
     // decode: one 16-row MFMA tile row per 16 rows of M; 6 column tiles per
     // workgroup (96 columns) when N is large enough to fill the chip
