@@ -26,6 +26,12 @@ Definitions followed
   ([GLM17] "第 4 站:索引器——FP8 与排名稳定性").
 * RMSNorm: y = x / sqrt(mean(x^2) + eps) * g, statistics in high precision,
   bf16 output ([GLM17] "第 1 站:RMSNorm 的两个出口").
+* Residual add: each decoder layer first adds the sublayer output back into
+  the bf16 residual stream and normalizes the sum; with a static per-tensor
+  activation scale add, norm and the fixed-scale cast are one step, with
+  blockwise weights the group quantizer follows the norm
+  ([GLM17] "第 1 站:RMSNorm 的两个出口"; the stream stays bf16 across layers,
+  "第 6 站:o_proj、残差流与 AllReduce 为什么停在 BF16").
 
 Readings where the pages leave a step open
 ------------------------------------------
@@ -41,6 +47,11 @@ Readings where the pages leave a step open
       The quantizer consumes the bf16 y.
 (vii) MX exponent: e = the smallest integer with max(amax, 1e-10) <= 448*2^e,
       stored as the byte e + 127; q = E4M3(x * 2^-e) (exact scaling).
+(viii) Residual add: the updated stream is z = bf16(x + h), the correctly
+      rounded sum (one rounding); RMSNorm and the quantizer then read that
+      bf16 z, as they would read it back from memory in the unfused sequence.
+      The static exit applies the same formula as the static quantizer,
+      q = E4M3(clamp(RN32(y / s))).
 """
 from __future__ import annotations
 
@@ -210,3 +221,37 @@ def rmsnorm_quant(x, g, eps: float, group: int = 128, r=None):
     y = rmsnorm_apply(x, g, r)
     q, s = quant_group(bf16.to_f32(y), group)
     return {"q": q, "s": s, "y": y, "r": r, "r_alt": r_alt, "ambiguous": amb}
+
+
+def residual_add(x, h):
+    """Updated residual stream z = bf16(x + h), correctly rounded (reading viii).
+
+    x and h hold bf16 values.  Their fp64 sum is rounded to bf16 once: an
+    fp64 sum of two 8-bit-significand values rounded again to 8 bits gives the
+    correctly rounded result, because 53 >= 2*8 + 1 (the classical condition
+    under which a double rounding through the wider format is innocuous for
+    addition).  Returns uint16 bits.
+    """
+    return bf16.round_from_f64(np.asarray(x, dtype=np.float64) + np.asarray(h, dtype=np.float64))
+
+
+def add_rmsnorm_quant(x, h, g, eps: float, static_scale=None, group: int = 128, r=None):
+    """Residual add -> RMSNorm -> bf16 -> quantization (readings vi, viii).
+
+    static_scale None: dynamic group quantization (q, s per group);
+    otherwise per-tensor static quantization with that fp32 scale (s = None).
+    Returns dict(z, q, s, y, r, r_alt, ambiguous); pass ``r`` to evaluate the
+    pipeline with a chosen per-row factor (for near-tie rows).
+    """
+    z = residual_add(x, h)
+    zf = bf16.to_f32(z)
+    if r is None:
+        r, r_alt, amb = rms_inv(zf, eps)
+    else:
+        r_alt, amb = None, None
+    y = rmsnorm_apply(zf, g, r)
+    if static_scale is None:
+        q, s = quant_group(bf16.to_f32(y), group)
+    else:
+        q, s = quant_static(bf16.to_f32(y), static_scale), None
+    return {"z": z, "q": q, "s": s, "y": y, "r": r, "r_alt": r_alt, "ambiguous": amb}

@@ -146,3 +146,53 @@ def test_rmsnorm_missing_eps_or_sqrt_is_caught():
     assert r[0] == expect
     assert np.float32(1.0 / math.sqrt(float(c) ** 2)) != expect       # eps dropped
     assert np.float32(1.0 / (float(c) ** 2 + 1e-6)) != expect          # sqrt dropped
+
+
+# ------------------------------------------------------------ residual add
+
+def _add_wrong_sign(x, h):
+    from oracle import bf16
+    return bf16.round_from_f64(np.asarray(x, np.float64) - np.asarray(h, np.float64))
+
+
+def _add_truncating(x, h):
+    s = (np.asarray(x, np.float64) + np.asarray(h, np.float64)).astype(np.float32)
+    return (s.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+@pytest.mark.parametrize("bad", [_add_wrong_sign, _add_truncating])
+def test_residual_add_mistakes_are_caught(monkeypatch, bad):
+    import tests.test_oracle_residual as pins
+    monkeypatch.setattr(quant, "residual_add", bad)
+    with pytest.raises(AssertionError):
+        pins.test_residual_add_is_correctly_rounded()
+
+
+def _norm_of_unrounded_sum(x, h, g, eps, static_scale=None, group=128, r=None):
+    from oracle import bf16
+    z = quant.residual_add(x, h)
+    exact = (np.asarray(x, np.float64) + np.asarray(h, np.float64)).astype(np.float32)
+    r, r_alt, amb = quant.rms_inv(exact, eps)
+    y = quant.rmsnorm_apply(exact, g, r)
+    q, s = quant.quant_group(bf16.to_f32(y), group)
+    return {"z": z, "q": q, "s": s, "y": y, "r": r, "r_alt": r_alt, "ambiguous": amb}
+
+
+def _norm_of_stream_before_add(x, h, g, eps, static_scale=None, group=128, r=None):
+    out = quant.rmsnorm_quant(np.asarray(x, np.float32), g, eps)
+    out["z"] = quant.residual_add(x, h)
+    return out
+
+
+@pytest.mark.parametrize("bad", [_norm_of_unrounded_sum, _norm_of_stream_before_add])
+def test_fused_norm_input_mistakes_are_caught(monkeypatch, bad):
+    import tests.test_oracle_residual as pins
+    monkeypatch.setattr(quant, "add_rmsnorm_quant", bad)
+    caught = 0
+    for pin in (pins.test_constant_sum_rows_closed_form, pins.test_symmetric_in_stream_and_sublayer_output,
+                pins.test_norm_reads_the_stored_stream):
+        try:
+            pin()
+        except AssertionError:
+            caught += 1
+    assert caught >= 1
