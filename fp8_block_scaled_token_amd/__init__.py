@@ -19,9 +19,9 @@ import torch
 
 __all__ = [
     "load_library", "FP8QError", "abi_version",
-    "fp8q_quant_act_group", "fp8q_rmsnorm_quant", "fp8q_quant_weight_block",
+    "fp8q_quant_act_group", "fp8q_rmsnorm_quant", "fp8q_add_rmsnorm_quant", "fp8q_quant_weight_block",
     "fp8q_gemm_blockscale", "fp8q_gemm_mxfp8",
-    "quant_act_group", "quant_act_static", "quant_act_mx", "rmsnorm_quant",
+    "quant_act_group", "quant_act_static", "quant_act_mx", "rmsnorm_quant", "add_rmsnorm_quant",
     "quant_weight_block", "quant_weight_mx", "quant_weight_tensor",
     "gemm_blockscale", "gemm_pertensor", "gemm_mxfp8",
     "SCALE_F32", "SCALE_UE8M0", "ROW_MAJOR", "COL_MAJOR", "GRAN_BLOCK128", "GRAN_PER_TENSOR",
@@ -43,6 +43,8 @@ SIGNATURES = {
     "fp8q_abi_version": (ctypes.c_int, []),
     "fp8q_quant_act_group": (ctypes.c_int, [_P, _I64, _I64, _I64, _I32, _I32, _I32, _P, _P, _I64, _P, _P]),
     "fp8q_rmsnorm_quant": (ctypes.c_int, [_P, _P, _F, _I64, _I64, _I64, _I32, _P, _I64, _P, _P, _I64, _P]),
+    "fp8q_add_rmsnorm_quant": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _I64, _P, _F, _I64, _I64, _I32, _P, _P, _I64,
+                                              _P, _P, _I64, _P]),
     "fp8q_quant_weight_block": (ctypes.c_int, [_P, _I64, _I64, _I64, _I32, _I32, _I32, _P, _I64, _P, _P]),
     "fp8q_gemm_blockscale": (ctypes.c_int, [_P, _I64, _P, _I32, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _P]),
     "fp8q_gemm_mxfp8": (ctypes.c_int, [_P, _I64, _P, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _I64, _P]),
@@ -137,6 +139,26 @@ def fp8q_rmsnorm_quant(x, gamma, eps, layout, q, scales, y_out=None, stream=None
                                              _stream(stream)), "fp8q_rmsnorm_quant")
 
 
+def fp8q_add_rmsnorm_quant(x, h, residual_out, gamma, eps, layout, static_scale, q, scales, y_out=None,
+                           stream=None):
+    M, K, ldx = _rows(x, torch.bfloat16, "x")
+    Mh, Kh, ldh = _rows(h, torch.bfloat16, "h")
+    Mr, Kr, ldr = _rows(residual_out, torch.bfloat16, "residual_out")
+    if (Mh, Kh) != (M, K) or (Mr, Kr) != (M, K):
+        raise ValueError("h and residual_out must have the shape of x")
+    q = _u8(q)
+    _, _, ldq = _rows(q, torch.uint8, "q")
+    ldy = 0
+    if y_out is not None:
+        _, _, ldy = _rows(y_out, torch.bfloat16, "y_out")
+    if gamma.dtype != torch.bfloat16 or gamma.numel() != K or not gamma.is_contiguous():
+        raise ValueError("gamma must be a contiguous bf16 tensor of K elements")
+    _check(load_library().fp8q_add_rmsnorm_quant(_ptr(x), ldx, _ptr(h), ldh, _ptr(residual_out), ldr,
+                                                 _ptr(gamma), float(eps), M, K, layout, _ptr(static_scale),
+                                                 _ptr(q), ldq, _ptr(scales), _ptr(y_out), ldy,
+                                                 _stream(stream)), "fp8q_add_rmsnorm_quant")
+
+
 def fp8q_quant_weight_block(w, block_n, block_k, fmt, q, scale_inv, stream=None):
     N, K, ldw = _rows(w, torch.bfloat16, "w")
     q = _u8(q)
@@ -219,6 +241,23 @@ def rmsnorm_quant(x, gamma, eps: float = 1e-6, layout: int = ROW_MAJOR, return_y
     s = torch.empty((G, M) if layout == COL_MAJOR else (M, G), dtype=torch.float32, device=x.device)
     y = torch.empty(M, K, dtype=torch.bfloat16, device=x.device) if return_y else None
     fp8q_rmsnorm_quant(x, gamma, eps, layout, q, s, y, stream)
+    return (q, s, y) if return_y else (q, s)
+
+
+def add_rmsnorm_quant(x, h, gamma, eps: float = 1e-6, layout: int = ROW_MAJOR, static_scale=None,
+                      return_y: bool = False, stream=None):
+    """Residual add in place (x <- bf16(x + h)), then RMSNorm and quantization.
+
+    Returns (q, scales[, y]); scales is None with a static scale.
+    """
+    M, K = x.shape
+    G = _cdiv(K, 128)
+    q = _q_like(M, K, x.device)
+    s = None
+    if static_scale is None:
+        s = torch.empty((G, M) if layout == COL_MAJOR else (M, G), dtype=torch.float32, device=x.device)
+    y = torch.empty(M, K, dtype=torch.bfloat16, device=x.device) if return_y else None
+    fp8q_add_rmsnorm_quant(x, h, x, gamma, eps, layout, static_scale, q, s, y, stream)
     return (q, s, y) if return_y else (q, s)
 
 

@@ -7,6 +7,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <utility>
 
 #include "launch.h"
 
@@ -142,6 +143,43 @@ fp8q_status_t fp8q_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, float
   return launch_status(fp8q::launch_rmsnorm_quant(x, gamma, eps, M, K, ldx, q, ldq, scales,
                                                    layout == FP8Q_SCALES_COL_MAJOR, y_out, ldy,
                                                    static_cast<hipStream_t>(stream)));
+}
+
+fp8q_status_t fp8q_add_rmsnorm_quant(const uint16_t* x, int64_t ldx, const uint16_t* h, int64_t ldh,
+                                     uint16_t* residual_out, int64_t ldr, const uint16_t* gamma,
+                                     float eps, int64_t M, int64_t K, int32_t layout,
+                                     const float* static_scale, uint8_t* q, int64_t ldq,
+                                     float* scales, uint16_t* y_out, int64_t ldy, void* stream) {
+  if (M < 0 || K <= 0 || M > kMaxRows || K > kMaxK) return FP8Q_ERR_SHAPE;
+  if (static_scale == nullptr && layout != FP8Q_SCALES_ROW_MAJOR && layout != FP8Q_SCALES_COL_MAJOR)
+    return FP8Q_ERR_UNSUPPORTED;
+  if (!(eps > 0.0f) || !std::isfinite(eps)) return FP8Q_ERR_VALUE;
+  if (M == 0) return FP8Q_OK;
+  FP8Q_TRY(check_matrix(x, K, ldx, 2));
+  FP8Q_TRY(check_matrix(h, K, ldh, 2));
+  FP8Q_TRY(check_matrix(residual_out, K, ldr, 2));
+  FP8Q_TRY(check_matrix(q, K, ldq, 1));
+  if (gamma == nullptr || (static_scale == nullptr && scales == nullptr)) return FP8Q_ERR_NULL;
+  if (!aligned16(gamma)) return FP8Q_ERR_MISALIGNED;
+  if (static_scale == nullptr && (reinterpret_cast<uintptr_t>(scales) & 3u)) return FP8Q_ERR_MISALIGNED;
+  if (static_scale != nullptr && (reinterpret_cast<uintptr_t>(static_scale) & 3u)) return FP8Q_ERR_MISALIGNED;
+  if (y_out != nullptr) FP8Q_TRY(check_matrix(y_out, K, ldy, 2));
+  // the residual output is x or h exactly, or disjoint from both
+  const auto span = [M, K](const uint16_t* p, int64_t ld) {
+    const uintptr_t b = reinterpret_cast<uintptr_t>(p);
+    return std::make_pair(b, b + static_cast<uintptr_t>(((M - 1) * ld + K) * 2));
+  };
+  const auto zr = span(residual_out, ldr);
+  for (const auto& in : {std::make_pair(static_cast<const uint16_t*>(x), ldx), std::make_pair(h, ldh)}) {
+    if (in.first == residual_out && in.second == ldr) continue;
+    const auto ir = span(in.first, in.second);
+    if (zr.first < ir.second && ir.first < zr.second) return FP8Q_ERR_VALUE;
+  }
+  FP8Q_TRY(check_device());
+  return launch_status(fp8q::launch_add_rmsnorm_quant(x, ldx, h, ldh, residual_out, ldr, gamma, eps, M, K,
+                                                       static_scale, q, ldq, scales,
+                                                       layout == FP8Q_SCALES_COL_MAJOR, y_out, ldy,
+                                                       static_cast<hipStream_t>(stream)));
 }
 
 fp8q_status_t fp8q_quant_weight_block(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,

@@ -20,6 +20,13 @@ hipError_t launch_quant_static(const uint16_t* x, int64_t M, int64_t K, int64_t 
 hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, float eps, int64_t M,
                                 int64_t K, int64_t ldx, uint8_t* q, int64_t ldq, float* scales,
                                 int col_major, uint16_t* y_out, int64_t ldy, hipStream_t stream);
+// Residual add (z = bf16(x + h) written to z_out), RMSNorm of z, then the
+// group-128 quantizer or, with static_scale, the per-tensor static one.
+hipError_t launch_add_rmsnorm_quant(const uint16_t* x, int64_t ldx, const uint16_t* h, int64_t ldh,
+                                    uint16_t* z_out, int64_t ldz, const uint16_t* gamma, float eps,
+                                    int64_t M, int64_t K, const float* static_scale, uint8_t* q,
+                                    int64_t ldq, float* scales, int col_major, uint16_t* y_out,
+                                    int64_t ldy, hipStream_t stream);
 hipError_t launch_weight_block128(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
                                   uint8_t* q, int64_t ldq, float* scale_inv, hipStream_t stream);
 hipError_t launch_weight_tensor(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q,

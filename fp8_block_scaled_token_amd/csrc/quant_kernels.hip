@@ -7,7 +7,10 @@
 //                     "4. 블록 양자화 스케일 관리"; round-up exponent of [GLM17]
 //                     "第 4 站:索引器——FP8 与排名稳定性").
 //  * quant_static     per-tensor static scale ([SGL19] "激活量化的三种选择").
-//  * rmsnorm_quant    RMSNorm -> bf16 -> group-128 quantizer in one pass.
+//  * rmsnorm_quant    RMSNorm -> bf16 -> group-128 quantizer in one pass,
+//                     optionally preceded by the residual add and with the
+//                     static per-tensor exit instead of group scales ([GLM17]
+//                     "第 1 站:RMSNorm 的两个出口").
 //  * weight_block     128x128 weight blocks and the per-tensor weight scale
 //                     ([SGL19] "建权重:先决定 scale 的形状", "从浮点到 FP8 的基本公式").
 //
@@ -253,12 +256,18 @@ __global__ __launch_bounds__(256) void quant_static_kernel(
 // (4i + w) * 512*CH in pass i.  The per-wave fp64 partial sums of squares
 // meet in LDS and are added in wave order (deterministic).
 //
+// ADD: the row first becomes z = bf16(x + h), which is written to the
+// residual output and is what the norm reads.  STAT: the normalized row is
+// quantized with one fixed per-tensor scale (no group scales).
+//
 // rmsnorm_quant_rows_kernel (K <= 4 * 512*CH): the workgroup owns a run of
 // consecutive rows (runs in XCD-contiguous order) and keeps a row in
 // registers from the sum of squares to the quantization; the next row's
 // loads are issued before the current row is computed, so HBM traffic
 // overlaps the arithmetic.  gamma is loaded once.
-// rmsnorm_quant_kernel (longer rows): one row per workgroup, read twice.
+// rmsnorm_quant_kernel (longer rows): one row per workgroup, read twice (with
+// ADD the sum is formed in both passes and stored in the second, so a
+// residual output that is x itself is read before it is overwritten).
 
 struct RmsArgs {
   const uint16_t* x;
@@ -271,6 +280,11 @@ struct RmsArgs {
   int col_major;
   uint16_t* y_out;
   int64_t ldy;
+  const uint16_t* h;         // ADD: sublayer output
+  int64_t ldh;
+  uint16_t* z_out;           // ADD: updated residual stream
+  int64_t ldz;
+  const float* static_scale; // STAT: per-tensor scale
 };
 
 template <int CH>
@@ -285,6 +299,36 @@ __device__ __forceinline__ void load_row_seg(uint4 (&raw)[CH], const uint16_t* x
       const int64_t k0 = seg0 + 512 * c + 8 * lane;
       raw[c] = (k0 < K) ? load8_bf16_masked(xr, k0, K) : make_uint4(0, 0, 0, 0);
     }
+  }
+}
+
+// z = bf16(x + h) for a segment, in place in x: one fp32 addition and one
+// round-to-nearest-even to bf16.  The fp32 sum of two bf16 values rounded to
+// bf16 is the correctly rounded sum (24 >= 2*8 + 1 bits: the double rounding
+// is innocuous); zero padding past K stays zero.
+template <int CH>
+__device__ __forceinline__ void add_seg(uint4 (&x)[CH], const uint4 (&h)[CH]) {
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    float a[8], b[8];
+    unpack8(x[c], a);
+    unpack8(h[c], b);
+    uint32_t o[4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) o[e >> 1] = pack_bf16x2(a[e] + b[e], a[e + 1] + b[e + 1]);
+    x[c] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+template <int CH>
+__device__ __forceinline__ void store_row_seg(uint16_t* zr, const uint4 (&z)[CH], int64_t seg0, int64_t K) {
+  const int lane = threadIdx.x & 63;
+  const bool full = seg0 + 512 * CH <= K;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int64_t k0 = seg0 + 512 * c + 8 * lane;
+    if (full) *reinterpret_cast<uint4*>(zr + k0) = z[c];
+    else if (k0 < K) store8_bf16_masked(zr, k0, K, z[c]);
   }
 }
 
@@ -329,10 +373,11 @@ __device__ __forceinline__ float rms_inv(double ss, double* part, double inv_k, 
   return rsqrt_f64_to_f32(__builtin_fma(ss, inv_k, (double)eps));
 }
 
-// y = bf16((x * r) * g) for one segment, then its group quantization.
-template <int CH>
+// y = bf16((x * r) * g) for one segment, then its group quantization (STAT:
+// q = E4M3(clamp(fp32(y / s))) with the static scale s, IEEE division).
+template <int CH, bool STAT>
 __device__ __forceinline__ void norm_quant_seg(const RmsArgs& a, uint4 (&raw)[CH], const float (&gf)[CH][8],
-                                               float rn, int64_t row, int64_t seg0) {
+                                               float rn, float s_stat, int64_t row, int64_t seg0) {
   const int lane = threadIdx.x & 63;
   const int64_t K = a.K;
   const bool full = seg0 + 512 * CH <= K;
@@ -353,7 +398,21 @@ __device__ __forceinline__ void norm_quant_seg(const RmsArgs& a, uint4 (&raw)[CH
       if (full) *reinterpret_cast<uint4*>(yr + k0) = raw[c];
       else if (k0 < K) store8_bf16_masked(yr, k0, K, raw[c]);
     }
-    amax[c] = max_row16(absmax8(raw[c]));
+    if (!STAT) amax[c] = max_row16(absmax8(raw[c]));
+  }
+  if (STAT) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int64_t k0 = seg0 + 512 * c + 8 * lane;
+      float v[8], t[8];
+      unpack8(raw[c], v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) t[e] = clamp448(v[e] / s_stat);   // IEEE division
+      const uint2 o = encode8(t);
+      if (full) st8(qr + k0, o);
+      else if (k0 < K) store8_masked(qr, k0, K, o);
+    }
+    return;
   }
   float s[CH], r[CH], s_mine;
   group_scales<CH>(amax, s, r, s_mine);
@@ -367,7 +426,7 @@ __device__ __forceinline__ void norm_quant_seg(const RmsArgs& a, uint4 (&raw)[CH
   store_group_scales<CH>(a.scales, s_mine, seg0 / 128, (K + 127) >> 7, a.M, row, a.col_major);
 }
 
-template <int CH>
+template <int CH, bool ADD, bool STAT>
 __global__ __launch_bounds__(256) void rmsnorm_quant_rows_kernel(RmsArgs a, int rows_per_wg) {
   __shared__ double part[2][4];
   const int wave = threadIdx.x >> 6;
@@ -375,7 +434,9 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_rows_kernel(RmsArgs a, int 
   const int64_t r1 = r0 + rows_per_wg < a.M ? r0 + rows_per_wg : a.M;
   if (r0 >= a.M) return;                       // whole workgroup
   const int64_t seg0 = (int64_t)wave * (512 * CH);
+  const float s_stat = STAT ? *a.static_scale : 1.0f;
   uint4 cur[CH], nxt[CH];
+  uint4 hcur[ADD ? CH : 1], hnxt[ADD ? CH : 1];
   float gf[CH][8];          // gamma of this wave's segment, unpacked once
   {
     uint4 gr[CH];
@@ -383,35 +444,50 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_rows_kernel(RmsArgs a, int 
 #pragma unroll
     for (int c = 0; c < CH; ++c) unpack8(gr[c], gf[c]);
   }
-  load_row_seg<CH>(cur, a.x + r0 * a.ldx, seg0, a.K);
+  auto load = [&](uint4 (&xb)[CH], uint4 (&hb)[ADD ? CH : 1], int64_t row) {
+    load_row_seg<CH>(xb, a.x + row * a.ldx, seg0, a.K);
+    if constexpr (ADD) load_row_seg<CH>(hb, a.h + row * a.ldh, seg0, a.K);
+  };
+  load(cur, hcur, r0);
   const double inv_k = 1.0 / (double)a.K;
-  // one row: its successor's loads go into the other buffer first
-  auto step = [&](uint4 (&buf)[CH], uint4 (&other)[CH], int64_t row) {
-    if (row + 1 < r1) load_row_seg<CH>(other, a.x + (row + 1) * a.ldx, seg0, a.K);
+  // one row: its successor's loads go into the other buffers first
+  auto step = [&](uint4 (&buf)[CH], uint4 (&hbuf)[ADD ? CH : 1], uint4 (&other)[CH],
+                  uint4 (&hother)[ADD ? CH : 1], int64_t row) {
+    if (row + 1 < r1) load(other, hother, row + 1);
+    if constexpr (ADD) {
+      add_seg<CH>(buf, hbuf);
+      if (seg0 < a.K) store_row_seg<CH>(a.z_out + row * a.ldz, buf, seg0, a.K);
+    }
     // the two slot sets alternate; the barrier inside rms_inv of row i+1
     // orders every read of set (i & 1) before the writes of row i+2
     const float rn = rms_inv(sumsq_seg<CH>(buf, 0.0), part[(row - r0) & 1], inv_k, a.eps);
-    if (seg0 < a.K) norm_quant_seg<CH>(a, buf, gf, rn, row, seg0);
+    if (seg0 < a.K) norm_quant_seg<CH, STAT>(a, buf, gf, rn, s_stat, row, seg0);
   };
-  // rows alternate between the two buffers (no copies between rows)
+  // rows alternate between the two buffer sets (no copies between rows)
   for (int64_t row = r0; row < r1; row += 2) {
-    step(cur, nxt, row);
-    if (row + 1 < r1) step(nxt, cur, row + 1);
+    step(cur, hcur, nxt, hnxt, row);
+    if (row + 1 < r1) step(nxt, hnxt, cur, hcur, row + 1);
   }
 }
 
-template <int CH>
+template <int CH, bool ADD, bool STAT>
 __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(RmsArgs a) {
   __shared__ double part[4];
   const int wave = threadIdx.x >> 6;
   const int64_t row = xcd_contiguous(blockIdx.x, gridDim.x);
   const uint16_t* xr = a.x + row * a.ldx;
+  const uint16_t* hr = ADD ? a.h + row * a.ldh : nullptr;
   constexpr int64_t SEG = 512 * CH;
   const int64_t npass = (a.K + 4 * SEG - 1) / (4 * SEG);
+  const float s_stat = STAT ? *a.static_scale : 1.0f;
   uint4 raw[CH], gr[CH];
   double ss = 0.0;
   for (int64_t it = 0; it < npass; ++it) {
     load_row_seg<CH>(raw, xr, (4 * it + wave) * SEG, a.K);
+    if constexpr (ADD) {
+      load_row_seg<CH>(gr, hr, (4 * it + wave) * SEG, a.K);
+      add_seg<CH>(raw, gr);
+    }
     ss = sumsq_seg<CH>(raw, ss);
   }
   const float rn = rms_inv(ss, part, 1.0 / (double)a.K, a.eps);
@@ -419,11 +495,16 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(RmsArgs a) {
     const int64_t seg0 = (4 * it + wave) * SEG;
     if (seg0 >= a.K) break;
     load_row_seg<CH>(raw, xr, seg0, a.K);
+    if constexpr (ADD) {
+      load_row_seg<CH>(gr, hr, seg0, a.K);
+      add_seg<CH>(raw, gr);
+      store_row_seg<CH>(a.z_out + row * a.ldz, raw, seg0, a.K);
+    }
     load_row_seg<CH>(gr, a.gamma, seg0, a.K);
     float gf[CH][8];
 #pragma unroll
     for (int c = 0; c < CH; ++c) unpack8(gr[c], gf[c]);
-    norm_quant_seg<CH>(a, raw, gf, rn, row, seg0);
+    norm_quant_seg<CH, STAT>(a, raw, gf, rn, s_stat, row, seg0);
   }
 }
 
@@ -538,24 +619,37 @@ hipError_t launch_quant_static(const uint16_t* x, int64_t M, int64_t K, int64_t 
   return hipGetLastError();
 }
 
-hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, float eps, int64_t M,
-                                int64_t K, int64_t ldx, uint8_t* q, int64_t ldq, float* scales,
-                                int col_major, uint16_t* y_out, int64_t ldy, hipStream_t stream) {
-  const RmsArgs a{x, gamma, eps, M, K, ldx, q, ldq, scales, col_major, y_out, ldy};
+namespace {
+
+// 256-thread workgroups of `kern` that one CU holds at once (at least 1)
+int resident_wgs(const void* kern) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, 256, 0) != hipSuccess || n < 1) n = 1;
+  return n;
+}
+
+template <bool ADD, bool STAT>
+hipError_t dispatch_rmsnorm(const RmsArgs& a, hipStream_t stream) {
   const dim3 block(256);
-  if (K > 4 * 512 * 8) {   // long rows: one workgroup per row, two reads
-    hipLaunchKernelGGL(rmsnorm_quant_kernel<4>, dim3((unsigned)M), block, 0, stream, a);
+  if (a.K > 4 * 512 * 8) {   // long rows: one workgroup per row, two reads
+    hipLaunchKernelGGL((rmsnorm_quant_kernel<4, ADD, STAT>), dim3((unsigned)a.M), block, 0, stream, a);
     return hipGetLastError();
   }
-  // four workgroups per CU, each a run of consecutive rows (measured best
-  // against two per CU and against one workgroup per row)
+  // up to four workgroups per CU, each a run of consecutive rows (measured
+  // best against two per CU and against one workgroup per row); never more
+  // than fit at once, so that no CU runs a second round of runs
 #ifndef FP8Q_RMS_WGS_PER_CU
 #define FP8Q_RMS_WGS_PER_CU 4
 #endif
-  const int64_t wgs = (int64_t)device_cu_count() * FP8Q_RMS_WGS_PER_CU;
-  const int rows = (int)ceil_div(M, wgs);
-  const dim3 grid((unsigned)ceil_div(M, rows));
-#define FP8Q_RMS(CH) hipLaunchKernelGGL((rmsnorm_quant_rows_kernel<CH>), grid, block, 0, stream, a, rows)
+#define FP8Q_RMS(CH)                                                                                   \
+  do {                                                                                                 \
+    const auto kern = rmsnorm_quant_rows_kernel<CH, ADD, STAT>;                                        \
+    static const int fit = resident_wgs(reinterpret_cast<const void*>(kern));                          \
+    const int64_t wgs = (int64_t)device_cu_count() * (fit < FP8Q_RMS_WGS_PER_CU ? fit : FP8Q_RMS_WGS_PER_CU); \
+    const int rows = (int)ceil_div(a.M, wgs);                                                          \
+    hipLaunchKernelGGL(kern, dim3((unsigned)ceil_div(a.M, rows)), block, 0, stream, a, rows);          \
+  } while (0)
+  const int64_t K = a.K;
   if (K <= 2048) FP8Q_RMS(1);
   else if (K <= 4096) FP8Q_RMS(2);
   else if (K <= 6144) FP8Q_RMS(3);
@@ -564,6 +658,27 @@ hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, float 
   else FP8Q_RMS(8);
 #undef FP8Q_RMS
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, float eps, int64_t M,
+                                int64_t K, int64_t ldx, uint8_t* q, int64_t ldq, float* scales,
+                                int col_major, uint16_t* y_out, int64_t ldy, hipStream_t stream) {
+  const RmsArgs a{x, gamma, eps, M, K, ldx, q, ldq, scales, col_major, y_out, ldy,
+                  nullptr, 0, nullptr, 0, nullptr};
+  return dispatch_rmsnorm<false, false>(a, stream);
+}
+
+hipError_t launch_add_rmsnorm_quant(const uint16_t* x, int64_t ldx, const uint16_t* h, int64_t ldh,
+                                    uint16_t* z_out, int64_t ldz, const uint16_t* gamma, float eps,
+                                    int64_t M, int64_t K, const float* static_scale, uint8_t* q,
+                                    int64_t ldq, float* scales, int col_major, uint16_t* y_out,
+                                    int64_t ldy, hipStream_t stream) {
+  const RmsArgs a{x, gamma, eps, M, K, ldx, q, ldq, scales, col_major, y_out, ldy,
+                  h, ldh, z_out, ldz, static_scale};
+  return static_scale != nullptr ? dispatch_rmsnorm<true, true>(a, stream)
+                                 : dispatch_rmsnorm<true, false>(a, stream);
 }
 
 hipError_t launch_weight_block128(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,

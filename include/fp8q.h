@@ -2,7 +2,8 @@
  * fp8q -- FP8 blockwise linear layer for AMD Instinct MI355X (gfx950).
  *
  * C ABI of the hot path: a dynamic per-token-group activation quantizer
- * (optionally fused after RMSNorm), a 128x128 weight-block quantizer, and
+ * (optionally fused after RMSNorm, or after residual add + RMSNorm), a
+ * 128x128 weight-block quantizer, and
  * W8A8 GEMMs with per-K-block fp32 rescaling (plus per-tensor and MXFP8
  * variants).  Plain pointers and sizes only; every compute step runs in
  * hand-written HIP kernels on the caller's stream.
@@ -125,6 +126,40 @@ fp8q_status_t fp8q_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, float
                                  int64_t M, int64_t K, int64_t ldx, int32_t layout,
                                  uint8_t* q, int64_t ldq, float* scales,
                                  uint16_t* y_out, int64_t ldy, void* stream);
+
+/*
+ * fp8q_add_rmsnorm_quant -- residual add, RMSNorm and FP8 quantization in one pass.
+ *
+ * [GLM17] "第 1 站:RMSNorm 的两个出口": every decoder layer begins by adding
+ * the sublayer output back into the bf16 residual stream and normalizing the
+ * sum; with a static per-tensor activation scale, add, norm and the
+ * fixed-scale cast form one kernel, with blockwise weights the per-token group
+ * quantizer follows the norm.  Both exits are offered; the stream stays bf16
+ * ("第 6 站:o_proj、残差流与 AllReduce 为什么停在 BF16").  Per row:
+ *   z_k = bf16(x_k + h_k)   (the correctly rounded sum)  -> residual_out,
+ *   r, y as in fp8q_rmsnorm_quant, computed on z,
+ *   static_scale == NULL: (q, scales) = group-128 quantization of y (F32,
+ *                         `layout` as in fp8q_quant_act_group);
+ *   static_scale != NULL: q = E4M3(clamp(fp32(y / s))) with the device fp32
+ *                         scalar s > 0; `scales` and `layout` are ignored and
+ *                         `scales` may be NULL.
+ * The outputs are bit-identical to an add, fp8q_rmsnorm_quant (or RMSNorm
+ * then fp8q_quant_act_group with static_scale) run one after the other.
+ *
+ *   x             bf16 [M, ldx]  residual stream (input).
+ *   h             bf16 [M, ldh]  sublayer output (input).
+ *   residual_out  bf16 [M, ldr]  updated stream z.  It may be x itself (same
+ *                 pointer and ldr == ldx, the in-place update) or h itself;
+ *                 any other overlap with x or h -> FP8Q_ERR_VALUE.
+ *   gamma bf16 [K];  eps > 0 (finite);  q E4M3 [M, ldq];
+ *   y_out optional bf16 [M, ldy] copy of the normalized rows (NULL = skip).
+ * A sum that overflows bf16 gives an infinite z and unspecified q, scales, y.
+ */
+fp8q_status_t fp8q_add_rmsnorm_quant(const uint16_t* x, int64_t ldx, const uint16_t* h, int64_t ldh,
+                                     uint16_t* residual_out, int64_t ldr, const uint16_t* gamma,
+                                     float eps, int64_t M, int64_t K, int32_t layout,
+                                     const float* static_scale, uint8_t* q, int64_t ldq,
+                                     float* scales, uint16_t* y_out, int64_t ldy, void* stream);
 
 /*
  * fp8q_quant_weight_block -- offline weight quantization.

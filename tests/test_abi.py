@@ -26,9 +26,9 @@ def lib():
     return fq.load_library()
 
 
-def test_header_declares_the_five_entry_points():
+def test_header_declares_the_entry_points():
     names = _declared_functions()
-    for n in ("fp8q_quant_act_group", "fp8q_rmsnorm_quant", "fp8q_quant_weight_block",
+    for n in ("fp8q_quant_act_group", "fp8q_rmsnorm_quant", "fp8q_add_rmsnorm_quant", "fp8q_quant_weight_block",
               "fp8q_gemm_blockscale", "fp8q_gemm_mxfp8", "fp8q_status_string", "fp8q_abi_version"):
         assert n in names
 
@@ -88,6 +88,41 @@ def test_rmsnorm_quant_validation(lib):
     assert f(A, B, 1e-6, 4, 128, 128, 0, B, 128, C, A, 100, None) == 2     # ldy < K
 
 
+def test_add_rmsnorm_quant_validation(lib):
+    f = lib.fp8q_add_rmsnorm_quant
+    D = ctypes.c_void_p(0x400000)
+    E = ctypes.c_void_p(0x500000)
+    ok = (A, 128, B, 128, C, 128, D, 1e-6, 4, 128, 0, None, E, 128, D, None, 0, None)
+
+    def call(**kw):
+        names = ["x", "ldx", "h", "ldh", "z", "ldz", "g", "eps", "M", "K", "layout", "stat", "q", "ldq",
+                 "s", "y", "ldy", "stream"]
+        args = list(ok)
+        for k, v in kw.items():
+            args[names.index(k)] = v
+        return f(*args)
+
+    assert call(M=-1) == 2
+    assert call(K=0) == 2
+    assert call(eps=0.0) == 7
+    assert call(eps=float("inf")) == 7
+    assert call(layout=3) == 3
+    assert call(M=0, x=None, h=None, z=None) == 0                         # no-op
+    assert call(h=None) == 1
+    assert call(z=None) == 1
+    assert call(g=None) == 1
+    assert call(s=None) == 1                                              # dynamic exit needs scales
+    assert call(ldh=120) == 2
+    assert call(ldz=132) == 4
+    assert call(y=E, ldy=100) == 2
+    assert call(stat=ctypes.c_void_p(0x600002)) == 4                      # static scale alignment
+    # residual output: x or h exactly, else disjoint
+    assert call(z=ctypes.c_void_p(0x100000 + 16)) == 7                    # overlaps x
+    assert call(z=ctypes.c_void_p(0x200000), ldz=256) == 7                # h's base, other stride
+    assert call(z=ctypes.c_void_p(0x200000 - 256)) == 7                   # runs into h
+    # accepted layouts reach the device check: see test_device_check_without_gpu
+
+
 def test_quant_weight_block_validation(lib):
     f = lib.fp8q_quant_weight_block
     assert f(A, 256, 256, 256, 64, 64, 0, B, 256, C, None) == 3          # 64x64 blocks
@@ -117,6 +152,14 @@ def test_device_check_without_gpu(lib):
         pytest.skip("a GPU is present: valid-looking fake pointers must never reach a launch")
     f = lib.fp8q_quant_act_group
     assert f(A, 4, 128, 128, 128, 0, 0, None, B, 128, C, None) == 5
+    # accepted residual outputs (in place on x or h, or just past x) and the
+    # static exit with an unused layout pass validation and stop here
+    g = lib.fp8q_add_rmsnorm_quant
+    E = ctypes.c_void_p(0x500000)
+    for z in (A, B, ctypes.c_void_p(0x100000 + 128 * 2 * 4)):
+        assert g(A, 128, B, 128, z, 128, C, 1e-6, 4, 128, 0, None, E, 128, C, None, 0, None) == 5
+    assert g(A, 128, B, 128, A, 128, C, 1e-6, 4, 128, 3, ctypes.c_void_p(0x600000), E, 128, None, None, 0,
+             None) == 5
 
 
 @pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")

@@ -180,9 +180,9 @@ def test_rmsnorm_quant_parity(M, K, layout):
         assert any(match), f"row {i}"
 
 
-# Without the y output, row lengths that are multiples of 2048 take the
-# one-wave-per-row kernel: fewer rows than waves, a ragged share of rows per
-# wave, and every row length it is built for (padded rows, canaries).
+# Without the y output: row lengths at each width of the rows kernel, fewer
+# rows than workgroups, a ragged share of rows per workgroup (padded rows,
+# canaries).
 @pytest.mark.parametrize("M,K", [(5, 2048), (64, 4096), (2500, 6144), (37, 8192), (3100, 6144),
                                  (1, 6144), (300, 2048)])
 @pytest.mark.parametrize("layout", [0, 1])
