@@ -3,7 +3,9 @@
 
 A step is one forward pass of the linear layer over one batch of synthetic
 activations already resident in HBM: the activation quantizer (fused with
-RMSNorm for the prefill-with-norm workload) followed by the scaled GEMM.  The
+RMSNorm for the prefill-with-norm workload, and with the residual add in front
+of it for the add-norm workload, which updates the stream in place) followed
+by the scaled GEMM.  The
 weight is quantized once before timing (it is offline preparation).  Inputs
 and outputs rotate over several buffer sets whose total exceeds the 256 MB
 Infinity Cache, so HBM rates are not inflated by cache hits.
@@ -43,7 +45,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="prefill_norm",
-                    choices=["tiny", "decode", "prefill_norm", "large", "mx", "pertensor"])
+                    choices=["tiny", "decode", "prefill_norm", "prefill_addnorm", "large", "mx", "pertensor"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample (0 = skip)")
     return ap.parse_args()
@@ -113,12 +115,15 @@ def main() -> int:
         sx_static = torch.tensor([np.float32(np.float32(amax) / np.float32(448.0))], device="cuda")
 
     # ---- rotating activation / output sets (beat the Infinity Cache)
-    set_bytes = M * K * 2 + M * K + M * KB * 4 + M * N * 2
+    set_bytes = M * K * 2 + M * K + M * KB * 4 + M * N * 2 + (M * K * 2 if wl.residual else 0)
     nsets = max(1, min(8, math.ceil(MALL_DEFEAT_BYTES / set_bytes)))
     xg = x_cpu.cuda()
+    hg = d["h"].cuda() if wl.residual else None
     sets = []
     for _ in range(nsets):
         s = {"x": xg.clone(), "q": torch.empty(M, K, dtype=torch.uint8, device="cuda")}
+        if wl.residual:
+            s["h"] = hg.clone()
         if name == "mx":
             s["s"] = torch.empty(M, math.ceil(K / 32), dtype=torch.uint8, device="cuda")
         elif name == "pertensor":
@@ -127,13 +132,15 @@ def main() -> int:
             s["s"] = torch.empty(KB, M, dtype=torch.float32, device="cuda")
         s["y"] = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
         sets.append(s)
-    del xg
+    del xg, hg
 
     # activation group scales travel column-major ([K/128, M]): a K block's
     # scales for consecutive rows are contiguous, one cache line per 32 rows
     # for the GEMM (the row-major form costs a line per row)
     def quant(s):
-        if wl.norm:
+        if wl.residual:
+            fq.fp8q_add_rmsnorm_quant(s["x"], s["h"], s["x"], gamma, d["eps"], fq.COL_MAJOR, None, s["q"], s["s"])
+        elif wl.norm:
             fq.fp8q_rmsnorm_quant(s["x"], gamma, d["eps"], fq.COL_MAJOR, s["q"], s["s"])
         elif name == "mx":
             fq.fp8q_quant_act_group(s["x"], 32, fq.SCALE_UE8M0, fq.ROW_MAJOR, None, s["q"], s["s"])
@@ -204,7 +211,7 @@ def main() -> int:
         q_bytes = M * K * 2 + M * K
         g_bytes = M * K + N * K + 8 + 2 * M * N
     else:
-        q_bytes = M * K * 2 + M * K + 4 * M * KB + (2 * K if wl.norm else 0)
+        q_bytes = M * K * 2 + M * K + 4 * M * KB + (2 * K if wl.norm else 0) + (4 * M * K if wl.residual else 0)
         g_bytes = M * K + N * K + 4 * M * KB + 4 * NB * KB + 2 * M * N
     gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
     gemm_gbps = g_bytes / (gemm_ms * 1e-3) / 1e9
@@ -218,14 +225,14 @@ def main() -> int:
         roof = {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_FP8_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "traffic": traffic}
 
-    kernel_q = {"prefill_norm": "rmsnorm_quant", "mx": "quant_group32mx",
+    kernel_q = {"prefill_norm": "rmsnorm_quant", "prefill_addnorm": "add_rmsnorm_quant", "mx": "quant_group32mx",
                 "pertensor": "quant_static"}.get(name, "quant_group128")
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8_e4m3 (fp32 accumulate)", "data": "synthetic",
-        "config": {"workload": name, "M": M, "N": N, "K": K, "norm": wl.norm,
+        "config": {"workload": name, "M": M, "N": N, "K": K, "norm": wl.norm, "residual_add": wl.residual,
                    "scales": {"mx": "1x32 ue8m0", "pertensor": "per-tensor fp32"}.get(name, "group128 + 128x128 fp32"),
                    "rotating_buffer_sets": nsets},
         "roofline": roof,
@@ -265,10 +272,14 @@ def cpu_baseline(name, wl, d, target_s):
     else:
         qw, sw = oq.quant_weight_block(wh)
     gh = d["gamma"].float().numpy() if wl.norm else None
+    hh = d["h"].float().numpy() if wl.residual else None
 
     def run(rows):
         xs = xh[:rows]
-        if wl.norm:
+        if wl.residual:
+            r = oq.add_rmsnorm_quant(xs, hh[:rows], gh, d["eps"])
+            og.gemm_blockscale(r["q"], r["s"], qw, sw)
+        elif wl.norm:
             r = oq.rmsnorm_quant(xs, gh, d["eps"])
             og.gemm_blockscale(r["q"], r["s"], qw, sw)
         elif name == "mx":

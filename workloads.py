@@ -18,7 +18,9 @@ with round-to-nearest-even):
   channels (chosen by a seeded permutation) are multiplied by ``outlier_mult``
   in every row;
 * weights ~ N(0, std) with std = 1/sqrt(K) unless stated;
-* RMSNorm gain g ~ U(0.5, 1.5).
+* RMSNorm gain g ~ U(0.5, 1.5);
+* sublayer output added to the residual stream: activations of their own
+  seed (outlier channels included) times 0.25, an exact power-of-two scaling.
 """
 from __future__ import annotations
 
@@ -84,6 +86,7 @@ class Workload:
     outlier_frac: float = 0.0
     w_std: float | None = None      # None -> 1/sqrt(K)
     norm: bool = False              # RMSNorm front end (eps 1e-6, g ~ U(0.5,1.5))
+    residual: bool = False          # residual add before the norm (h = 0.25 x N(0,1) + outliers)
     mx: bool = False                # also exercised with 1x32 UE8M0 scales
 
     def make(self, device: str = "cpu") -> dict:
@@ -95,6 +98,9 @@ class Workload:
         if self.norm:
             d["gamma"] = gamma(self.K, s + 3, device=device)
             d["eps"] = 1e-6
+        if self.residual:
+            h = activations(self.M, self.K, s + 4, self.outlier_frac, device=device)
+            d["h"] = (h.float() * 0.25).to(torch.bfloat16)
         return d
 
 
@@ -106,6 +112,9 @@ WORKLOADS = {
     # prefill-shaped with RMSNorm front end: x [4096,6144], W [6144,6144]
     "prefill_norm": Workload("prefill_norm", 4096, 6144, 6144, seed=2,
                              outlier_frac=0.001, norm=True),
+    # the same with the residual add in front: z = x + h -> RMSNorm -> quant
+    "prefill_addnorm": Workload("prefill_addnorm", 4096, 6144, 6144, seed=2,
+                                outlier_frac=0.001, norm=True, residual=True),
     # large prefill: A [8192,7168] with outliers, W [18432,7168]
     "large": Workload("large", 8192, 18432, 7168, seed=3, outlier_frac=0.001),
     # MXFP8 / per-tensor: A [2048,7168], W [7168,7168], both N(0,1)
