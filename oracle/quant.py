@@ -47,6 +47,15 @@ Readings where the pages leave a step open
       The quantizer consumes the bf16 y.
 (vii) MX exponent: e = the smallest integer with max(amax, 1e-10) <= 448*2^e,
       stored as the byte e + 127; q = E4M3(x * 2^-e) (exact scaling).
+(ix)  Power-of-two ("UE8M0") block scales held in fp32: the block-FP8 data
+      consumed as an MXFP8 view keeps the 128-wide activation groups and the
+      128x128 weight blocks but restricts every scale to a power of two,
+      s = 2^e with e from the round-up rule of (vii); q = E4M3(x * 2^-e).
+      The fp32 value 2^e carries the UE8M0 byte e + 127 as its exponent field.
+(x)   Re-quantizing an existing block (codes q, fp32 scale s) to a power of
+      two: e' = the smallest integer with s <= 2^e' (the round-up rule applied
+      to s, which stands for amax/448), q' = E4M3(decode(q) * s * 2^-e'); as
+      s * 2^-e' <= 1, no code grows past 448.
 (viii) Residual add: the updated stream is z = bf16(x + h), the correctly
       rounded sum (one rounding); RMSNorm and the quantizer then read that
       bf16 z, as they would read it back from memory in the unfused sequence.
@@ -255,3 +264,55 @@ def add_rmsnorm_quant(x, h, g, eps: float, static_scale=None, group: int = 128, 
     else:
         q, s = quant_static(bf16.to_f32(y), static_scale), None
     return {"z": z, "q": q, "s": s, "y": y, "r": r, "r_alt": r_alt, "ambiguous": amb}
+
+
+def pow2_scale(e) -> np.ndarray:
+    """fp32 value 2^e of integer exponents (exact)."""
+    return np.ldexp(1.0, np.asarray(e, dtype=np.int64)).astype(np.float32)
+
+
+def quant_group_pow2(x, group: int = 128):
+    """Per-token-group quantization with power-of-two fp32 scales (reading ix).
+
+    The group's exponent follows the MX round-up rule, so this is the MX
+    quantizer with 128-wide groups and the scale stored as the fp32 2^e.
+    Returns (q uint8 [M, K], s float32 [M, ceil(K/group)]).
+    """
+    q, sb = quant_mx(x, group)
+    return q, pow2_scale(sb.astype(np.int64) - UE8M0_BIAS)
+
+
+def quant_weight_block_pow2(w, block_n: int = 128, block_k: int = 128):
+    """128x128 weight blocks with power-of-two fp32 scales (reading ix).
+
+    Returns (q uint8 [N, K], s float32 [ceil(N/128), ceil(K/128)]).
+    """
+    w = np.asarray(w, dtype=np.float32)
+    N, K = w.shape
+    NB, KB = _ngroups(N, block_n), _ngroups(K, block_k)
+    q = np.empty((N, K), dtype=np.uint8)
+    s = np.empty((NB, KB), dtype=np.float32)
+    for i in range(NB):
+        rows = slice(i * block_n, min(N, (i + 1) * block_n))
+        for j in range(KB):
+            cols = slice(j * block_k, min(K, (j + 1) * block_k))
+            blk = w[rows, cols].astype(np.float64)
+            e = int(mx_exponent(np.max(np.abs(blk))))
+            s[i, j] = pow2_scale(e)
+            q[rows, cols] = e4m3.encode(np.clip(np.ldexp(blk, -e), -448.0, 448.0))
+    return q, s
+
+
+def requant_weight_pow2(q, s, block_n: int = 128, block_k: int = 128):
+    """Re-quantize block-FP8 weights (codes q, fp32 block scales s) to
+    power-of-two block scales (reading x).  Returns (q', s')."""
+    q = np.asarray(q, dtype=np.uint8)
+    s = np.asarray(s, dtype=np.float32)
+    N, K = q.shape
+    f, k = np.frexp(s.astype(np.float64))          # s = f * 2^k, f in [0.5, 1)
+    e = np.where(f == 0.5, k - 1, k).astype(np.int64)
+    s2 = pow2_scale(e)
+    m = s.astype(np.float64) / s2.astype(np.float64)   # exact: in (1/2, 1]
+    mult = np.repeat(np.repeat(m, block_n, axis=0), block_k, axis=1)[:N, :K]
+    v = e4m3.decode(q) * mult                       # exact in fp64 (4 x 24 bits)
+    return e4m3.encode(np.clip(v, -448.0, 448.0)), s2

@@ -196,3 +196,59 @@ def test_fused_norm_input_mistakes_are_caught(monkeypatch, bad):
         except AssertionError:
             caught += 1
     assert caught >= 1
+
+
+# ------------------------------------------------------ power-of-two scales
+
+def _requant_floor_exponent(q, s, block_n=128, block_k=128):
+    from oracle import e4m3
+    q = np.asarray(q, np.uint8)
+    N, K = q.shape
+    e = np.floor(np.log2(np.asarray(s, np.float64))).astype(np.int64)     # rounds down
+    s2 = quant.pow2_scale(e)
+    m = np.repeat(np.repeat(np.asarray(s, np.float64) / s2, block_n, 0), block_k, 1)[:N, :K]
+    return e4m3.encode(np.clip(e4m3.decode(q) * m, -448.0, 448.0)), s2
+
+
+def _requant_truncating(q, s, block_n=128, block_k=128):
+    from oracle import e4m3
+    q = np.asarray(q, np.uint8)
+    N, K = q.shape
+    f, k = np.frexp(np.asarray(s, np.float64))
+    s2 = quant.pow2_scale(np.where(f == 0.5, k - 1, k))
+    m = np.repeat(np.repeat(np.asarray(s, np.float64) / s2, block_n, 0), block_k, 1)[:N, :K]
+    v = e4m3.decode(q) * m
+    e = np.floor(np.log2(np.maximum(np.abs(v), 2.0 ** -9)))
+    step = np.exp2(np.maximum(e, -6) - 3)
+    return e4m3.encode(np.clip(np.trunc(v / step) * step, -448.0, 448.0)), s2     # drops the rounding
+
+
+@pytest.mark.parametrize("bad", [_requant_floor_exponent, _requant_truncating])
+def test_requant_mistakes_are_caught(monkeypatch, bad):
+    import tests.test_oracle_pow2 as pins
+    monkeypatch.setattr(quant, "requant_weight_pow2", bad)
+    with pytest.raises(AssertionError):
+        pins.test_requant_every_code_against_exact_rounding()
+
+
+def _group_pow2_nearest_exponent(x, group=128):
+    x = np.asarray(x, np.float32)
+    M, K = x.shape
+    G = -(-K // group)
+    from oracle import e4m3
+    q = np.empty((M, K), np.uint8)
+    s = np.empty((M, G), np.float32)
+    for g in range(G):
+        cols = slice(g * group, min(K, (g + 1) * group))
+        amax = np.maximum(np.max(np.abs(x[:, cols]), axis=1), np.float32(1e-10)).astype(np.float64)
+        e = np.round(np.log2(amax / 448.0)).astype(np.int64)
+        s[:, g] = quant.pow2_scale(e)
+        q[:, cols] = e4m3.encode(np.clip(np.ldexp(x[:, cols].astype(np.float64), -e[:, None]), -448, 448))
+    return q, s
+
+
+def test_group_pow2_mistake_is_caught(monkeypatch):
+    import tests.test_oracle_pow2 as pins
+    monkeypatch.setattr(quant, "quant_group_pow2", _group_pow2_nearest_exponent)
+    with pytest.raises(AssertionError):
+        pins.test_group_pow2_scales_bracket_amax()
