@@ -20,18 +20,19 @@ import torch
 __all__ = [
     "load_library", "FP8QError", "abi_version",
     "fp8q_quant_act_group", "fp8q_rmsnorm_quant", "fp8q_add_rmsnorm_quant", "fp8q_quant_weight_block",
-    "fp8q_gemm_blockscale", "fp8q_gemm_mxfp8",
-    "quant_act_group", "quant_act_static", "quant_act_mx", "rmsnorm_quant", "add_rmsnorm_quant",
-    "quant_weight_block", "quant_weight_mx", "quant_weight_tensor",
-    "gemm_blockscale", "gemm_pertensor", "gemm_mxfp8",
-    "SCALE_F32", "SCALE_UE8M0", "ROW_MAJOR", "COL_MAJOR", "GRAN_BLOCK128", "GRAN_PER_TENSOR",
+    "fp8q_requant_weight_pow2", "fp8q_gemm_blockscale", "fp8q_gemm_mxfp8",
+    "quant_act_group", "quant_act_group_pow2", "rmsnorm_quant_pow2", "quant_act_static", "quant_act_mx", "rmsnorm_quant", "add_rmsnorm_quant",
+    "quant_weight_block", "quant_weight_block_pow2", "requant_weight_pow2", "quant_weight_mx", "quant_weight_tensor",
+    "gemm_blockscale", "gemm_blockscale_pow2", "gemm_pertensor", "gemm_mxfp8",
+    "SCALE_F32", "SCALE_UE8M0", "SCALE_F32_POW2", "ROW_MAJOR", "COL_MAJOR", "GRAN_BLOCK128", "GRAN_PER_TENSOR",
+    "GRAN_BLOCK128_POW2",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8q.so")
 
-SCALE_F32, SCALE_UE8M0 = 0, 1
+SCALE_F32, SCALE_UE8M0, SCALE_F32_POW2 = 0, 1, 2
 ROW_MAJOR, COL_MAJOR = 0, 1
-GRAN_BLOCK128, GRAN_PER_TENSOR = 0, 1
+GRAN_BLOCK128, GRAN_PER_TENSOR, GRAN_BLOCK128_POW2 = 0, 1, 2
 
 _STATUS = {0: "ok", 1: "null", 2: "shape", 3: "unsupported", 4: "misaligned",
            5: "device", 6: "launch", 7: "value"}
@@ -43,8 +44,9 @@ SIGNATURES = {
     "fp8q_abi_version": (ctypes.c_int, []),
     "fp8q_quant_act_group": (ctypes.c_int, [_P, _I64, _I64, _I64, _I32, _I32, _I32, _P, _P, _I64, _P, _P]),
     "fp8q_rmsnorm_quant": (ctypes.c_int, [_P, _P, _F, _I64, _I64, _I64, _I32, _P, _I64, _P, _P, _I64, _P]),
-    "fp8q_add_rmsnorm_quant": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _I64, _P, _F, _I64, _I64, _I32, _P, _P, _I64,
-                                              _P, _P, _I64, _P]),
+    "fp8q_add_rmsnorm_quant": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _I64, _P, _F, _I64, _I64, _I32, _I32, _P, _P,
+                                              _I64, _P, _P, _I64, _P]),
+    "fp8q_requant_weight_pow2": (ctypes.c_int, [_P, _I64, _P, _I64, _I64, _P, _I64, _P, _P]),
     "fp8q_quant_weight_block": (ctypes.c_int, [_P, _I64, _I64, _I64, _I32, _I32, _I32, _P, _I64, _P, _P]),
     "fp8q_gemm_blockscale": (ctypes.c_int, [_P, _I64, _P, _I32, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _P]),
     "fp8q_gemm_mxfp8": (ctypes.c_int, [_P, _I64, _P, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _I64, _P]),
@@ -139,13 +141,15 @@ def fp8q_rmsnorm_quant(x, gamma, eps, layout, q, scales, y_out=None, stream=None
                                              _stream(stream)), "fp8q_rmsnorm_quant")
 
 
-def fp8q_add_rmsnorm_quant(x, h, residual_out, gamma, eps, layout, static_scale, q, scales, y_out=None,
+def fp8q_add_rmsnorm_quant(x, h, residual_out, gamma, eps, fmt, layout, static_scale, q, scales, y_out=None,
                            stream=None):
     M, K, ldx = _rows(x, torch.bfloat16, "x")
-    Mh, Kh, ldh = _rows(h, torch.bfloat16, "h")
-    Mr, Kr, ldr = _rows(residual_out, torch.bfloat16, "residual_out")
-    if (Mh, Kh) != (M, K) or (Mr, Kr) != (M, K):
-        raise ValueError("h and residual_out must have the shape of x")
+    ldh = ldr = 0
+    if h is not None:
+        Mh, Kh, ldh = _rows(h, torch.bfloat16, "h")
+        Mr, Kr, ldr = _rows(residual_out, torch.bfloat16, "residual_out")
+        if (Mh, Kh) != (M, K) or (Mr, Kr) != (M, K):
+            raise ValueError("h and residual_out must have the shape of x")
     q = _u8(q)
     _, _, ldq = _rows(q, torch.uint8, "q")
     ldy = 0
@@ -154,9 +158,23 @@ def fp8q_add_rmsnorm_quant(x, h, residual_out, gamma, eps, layout, static_scale,
     if gamma.dtype != torch.bfloat16 or gamma.numel() != K or not gamma.is_contiguous():
         raise ValueError("gamma must be a contiguous bf16 tensor of K elements")
     _check(load_library().fp8q_add_rmsnorm_quant(_ptr(x), ldx, _ptr(h), ldh, _ptr(residual_out), ldr,
-                                                 _ptr(gamma), float(eps), M, K, layout, _ptr(static_scale),
+                                                 _ptr(gamma), float(eps), M, K, fmt, layout, _ptr(static_scale),
                                                  _ptr(q), ldq, _ptr(scales), _ptr(y_out), ldy,
                                                  _stream(stream)), "fp8q_add_rmsnorm_quant")
+
+
+def fp8q_requant_weight_pow2(q_in, s_in, q_out, s_out, stream=None):
+    q_in, q_out = _u8(q_in), _u8(q_out)
+    N, K, ldi = _rows(q_in, torch.uint8, "q_in")
+    No, Ko, ldo = _rows(q_out, torch.uint8, "q_out")
+    if (No, Ko) != (N, K):
+        raise ValueError("q_out must have the shape of q_in")
+    shape = (_cdiv(N, 128), _cdiv(K, 128))
+    for t, name in ((s_in, "s_in"), (s_out, "s_out")):
+        if t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 tensor of shape {shape}")
+    _check(load_library().fp8q_requant_weight_pow2(_ptr(q_in), ldi, _ptr(s_in), N, K, _ptr(q_out), ldo,
+                                                   _ptr(s_out), _stream(stream)), "fp8q_requant_weight_pow2")
 
 
 def fp8q_quant_weight_block(w, block_n, block_k, fmt, q, scale_inv, stream=None):
@@ -216,6 +234,16 @@ def quant_act_group(x: torch.Tensor, layout: int = ROW_MAJOR, stream=None):
     return q, s
 
 
+def quant_act_group_pow2(x: torch.Tensor, layout: int = ROW_MAJOR, stream=None):
+    """(q, power-of-two fp32 scales) with 128-wide groups (block FP8 as an MXFP8 view)."""
+    M, K = x.shape
+    G = _cdiv(K, 128)
+    q = _q_like(M, K, x.device)
+    s = torch.empty((G, M) if layout == COL_MAJOR else (M, G), dtype=torch.float32, device=x.device)
+    fp8q_quant_act_group(x, 128, SCALE_F32_POW2, layout, None, q, s, stream)
+    return q, s
+
+
 def quant_act_mx(x: torch.Tensor, stream=None):
     """(q uint8 [M,K], UE8M0 scale bytes uint8 [M, ceil(K/32)])."""
     M, K = x.shape
@@ -245,7 +273,7 @@ def rmsnorm_quant(x, gamma, eps: float = 1e-6, layout: int = ROW_MAJOR, return_y
 
 
 def add_rmsnorm_quant(x, h, gamma, eps: float = 1e-6, layout: int = ROW_MAJOR, static_scale=None,
-                      return_y: bool = False, stream=None):
+                      return_y: bool = False, fmt: int = SCALE_F32, stream=None):
     """Residual add in place (x <- bf16(x + h)), then RMSNorm and quantization.
 
     Returns (q, scales[, y]); scales is None with a static scale.
@@ -257,8 +285,15 @@ def add_rmsnorm_quant(x, h, gamma, eps: float = 1e-6, layout: int = ROW_MAJOR, s
     if static_scale is None:
         s = torch.empty((G, M) if layout == COL_MAJOR else (M, G), dtype=torch.float32, device=x.device)
     y = torch.empty(M, K, dtype=torch.bfloat16, device=x.device) if return_y else None
-    fp8q_add_rmsnorm_quant(x, h, x, gamma, eps, layout, static_scale, q, s, y, stream)
+    fp8q_add_rmsnorm_quant(x, h, x if h is not None else None, gamma, eps, fmt, layout, static_scale, q, s, y,
+                           stream)
     return (q, s, y) if return_y else (q, s)
+
+
+def rmsnorm_quant_pow2(x, gamma, eps: float = 1e-6, layout: int = ROW_MAJOR, return_y: bool = False,
+                       stream=None):
+    """(q, power-of-two scales[, y]) of RMSNorm(x) followed by group-128 quantization."""
+    return add_rmsnorm_quant(x, None, gamma, eps, layout, None, return_y, SCALE_F32_POW2, stream)
 
 
 def quant_weight_block(w: torch.Tensor, stream=None):
@@ -268,6 +303,24 @@ def quant_weight_block(w: torch.Tensor, stream=None):
     s = torch.empty(_cdiv(N, 128), _cdiv(K, 128), dtype=torch.float32, device=w.device)
     fp8q_quant_weight_block(w, 128, 128, SCALE_F32, q, s, stream)
     return q, s
+
+
+def quant_weight_block_pow2(w: torch.Tensor, stream=None):
+    """(q uint8 [N,K], power-of-two scale_inv fp32 [ceil(N/128), ceil(K/128)])."""
+    N, K = w.shape
+    q = _q_like(N, K, w.device)
+    s = torch.empty(_cdiv(N, 128), _cdiv(K, 128), dtype=torch.float32, device=w.device)
+    fp8q_quant_weight_block(w, 128, 128, SCALE_F32_POW2, q, s, stream)
+    return q, s
+
+
+def requant_weight_pow2(q: torch.Tensor, s: torch.Tensor, stream=None):
+    """Block-FP8 (q, fp32 block scales) -> (q', power-of-two scales), new buffers."""
+    N, K = q.shape
+    q2 = _q_like(N, K, q.device)
+    s2 = torch.empty_like(s)
+    fp8q_requant_weight_pow2(q, s, q2, s2, stream)
+    return q2, s2
 
 
 def quant_weight_mx(w: torch.Tensor, stream=None):
@@ -294,6 +347,13 @@ def _y(M: int, N: int, device) -> torch.Tensor:
 def gemm_blockscale(a, a_scales, w, w_scale_inv, bias=None, a_layout: int = ROW_MAJOR, stream=None):
     y = _y(a.shape[0], w.shape[0], a.device)
     fp8q_gemm_blockscale(a, a_scales, a_layout, w, w_scale_inv, bias, y, GRAN_BLOCK128, stream)
+    return y
+
+
+def gemm_blockscale_pow2(a, a_scales, w, w_scale_inv, bias=None, a_layout: int = ROW_MAJOR, stream=None):
+    """Block GEMM on power-of-two scales, applied by the scaled MFMA."""
+    y = _y(a.shape[0], w.shape[0], a.device)
+    fp8q_gemm_blockscale(a, a_scales, a_layout, w, w_scale_inv, bias, y, GRAN_BLOCK128_POW2, stream)
     return y
 
 

@@ -46,6 +46,17 @@ fp8q_status check_matrix(const void* p, int64_t K, int64_t ld, int elem_bytes) {
   return FP8Q_OK;
 }
 
+// Byte range [lo, hi) of a row-major [rows, cols] matrix with stride ld
+// (elements of elem bytes); a contiguous array is one row.
+struct Span {
+  uintptr_t lo, hi;
+};
+Span span(const void* p, int64_t rows, int64_t ld, int64_t cols, int elem) {
+  const uintptr_t b = reinterpret_cast<uintptr_t>(p);
+  return {b, b + static_cast<uintptr_t>(((rows - 1) * ld + cols) * elem)};
+}
+bool overlap(const Span& a, const Span& b) { return a.lo < b.hi && b.lo < a.hi; }
+
 #define FP8Q_TRY(expr)                 \
   do {                                 \
     const fp8q_status s_ = (expr);     \
@@ -102,7 +113,7 @@ fp8q_status_t fp8q_quant_act_group(const uint16_t* x, int64_t M, int64_t K, int6
                                    void* scales, void* stream) {
   if (M < 0 || K <= 0 || M > kMaxRows || K > kMaxK) return FP8Q_ERR_SHAPE;
   if (static_scale == nullptr) {
-    const bool g128 = group_size == 128 && fmt == FP8Q_SCALE_F32;
+    const bool g128 = group_size == 128 && (fmt == FP8Q_SCALE_F32 || fmt == FP8Q_SCALE_F32_POW2);
     const bool g32 = group_size == 32 && fmt == FP8Q_SCALE_UE8M0;
     if (!g128 && !g32) return FP8Q_ERR_UNSUPPORTED;
     if (layout != FP8Q_SCALES_ROW_MAJOR && layout != FP8Q_SCALES_COL_MAJOR) return FP8Q_ERR_UNSUPPORTED;
@@ -111,7 +122,7 @@ fp8q_status_t fp8q_quant_act_group(const uint16_t* x, int64_t M, int64_t K, int6
   FP8Q_TRY(check_matrix(x, K, ldx, 2));
   FP8Q_TRY(check_matrix(q, K, ldq, 1));
   if (static_scale == nullptr && scales == nullptr) return FP8Q_ERR_NULL;
-  if (static_scale == nullptr && fmt == FP8Q_SCALE_F32 && (reinterpret_cast<uintptr_t>(scales) & 3u))
+  if (static_scale == nullptr && fmt != FP8Q_SCALE_UE8M0 && (reinterpret_cast<uintptr_t>(scales) & 3u))
     return FP8Q_ERR_MISALIGNED;
   FP8Q_TRY(check_device());
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -120,7 +131,8 @@ fp8q_status_t fp8q_quant_act_group(const uint16_t* x, int64_t M, int64_t K, int6
   if (static_scale != nullptr)
     e = fp8q::launch_quant_static(x, M, K, ldx, static_scale, q, ldq, st);
   else if (group_size == 128)
-    e = fp8q::launch_quant_group128(x, M, K, ldx, q, ldq, static_cast<float*>(scales), colm, st);
+    e = fp8q::launch_quant_group128(x, M, K, ldx, q, ldq, static_cast<float*>(scales), colm,
+                                    fmt == FP8Q_SCALE_F32_POW2, st);
   else
     e = fp8q::launch_quant_group32mx(x, M, K, ldx, q, ldq, static_cast<uint8_t*>(scales), colm, st);
   return launch_status(e);
@@ -147,38 +159,39 @@ fp8q_status_t fp8q_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, float
 
 fp8q_status_t fp8q_add_rmsnorm_quant(const uint16_t* x, int64_t ldx, const uint16_t* h, int64_t ldh,
                                      uint16_t* residual_out, int64_t ldr, const uint16_t* gamma,
-                                     float eps, int64_t M, int64_t K, int32_t layout,
+                                     float eps, int64_t M, int64_t K, int32_t fmt, int32_t layout,
                                      const float* static_scale, uint8_t* q, int64_t ldq,
                                      float* scales, uint16_t* y_out, int64_t ldy, void* stream) {
   if (M < 0 || K <= 0 || M > kMaxRows || K > kMaxK) return FP8Q_ERR_SHAPE;
-  if (static_scale == nullptr && layout != FP8Q_SCALES_ROW_MAJOR && layout != FP8Q_SCALES_COL_MAJOR)
-    return FP8Q_ERR_UNSUPPORTED;
+  if (static_scale == nullptr) {
+    if (layout != FP8Q_SCALES_ROW_MAJOR && layout != FP8Q_SCALES_COL_MAJOR) return FP8Q_ERR_UNSUPPORTED;
+    if (fmt != FP8Q_SCALE_F32 && fmt != FP8Q_SCALE_F32_POW2) return FP8Q_ERR_UNSUPPORTED;
+  }
   if (!(eps > 0.0f) || !std::isfinite(eps)) return FP8Q_ERR_VALUE;
+  if (h == nullptr && residual_out != nullptr) return FP8Q_ERR_VALUE;
   if (M == 0) return FP8Q_OK;
   FP8Q_TRY(check_matrix(x, K, ldx, 2));
-  FP8Q_TRY(check_matrix(h, K, ldh, 2));
-  FP8Q_TRY(check_matrix(residual_out, K, ldr, 2));
+  if (h != nullptr) {
+    FP8Q_TRY(check_matrix(h, K, ldh, 2));
+    FP8Q_TRY(check_matrix(residual_out, K, ldr, 2));
+  }
   FP8Q_TRY(check_matrix(q, K, ldq, 1));
   if (gamma == nullptr || (static_scale == nullptr && scales == nullptr)) return FP8Q_ERR_NULL;
   if (!aligned16(gamma)) return FP8Q_ERR_MISALIGNED;
   if (static_scale == nullptr && (reinterpret_cast<uintptr_t>(scales) & 3u)) return FP8Q_ERR_MISALIGNED;
   if (static_scale != nullptr && (reinterpret_cast<uintptr_t>(static_scale) & 3u)) return FP8Q_ERR_MISALIGNED;
   if (y_out != nullptr) FP8Q_TRY(check_matrix(y_out, K, ldy, 2));
-  // the residual output is x or h exactly, or disjoint from both
-  const auto span = [M, K](const uint16_t* p, int64_t ld) {
-    const uintptr_t b = reinterpret_cast<uintptr_t>(p);
-    return std::make_pair(b, b + static_cast<uintptr_t>(((M - 1) * ld + K) * 2));
-  };
-  const auto zr = span(residual_out, ldr);
-  for (const auto& in : {std::make_pair(static_cast<const uint16_t*>(x), ldx), std::make_pair(h, ldh)}) {
-    if (in.first == residual_out && in.second == ldr) continue;
-    const auto ir = span(in.first, in.second);
-    if (zr.first < ir.second && ir.first < zr.second) return FP8Q_ERR_VALUE;
+  if (h != nullptr) {
+    // the residual output is x or h exactly, or disjoint from both
+    for (const auto& in : {std::make_pair(x, ldx), std::make_pair(h, ldh)}) {
+      if (in.first == residual_out && in.second == ldr) continue;
+      if (overlap(span(in.first, M, in.second, K, 2), span(residual_out, M, ldr, K, 2))) return FP8Q_ERR_VALUE;
+    }
   }
   FP8Q_TRY(check_device());
   return launch_status(fp8q::launch_add_rmsnorm_quant(x, ldx, h, ldh, residual_out, ldr, gamma, eps, M, K,
-                                                       static_scale, q, ldq, scales,
-                                                       layout == FP8Q_SCALES_COL_MAJOR, y_out, ldy,
+                                                       static_scale, fmt == FP8Q_SCALE_F32_POW2, q, ldq,
+                                                       scales, layout == FP8Q_SCALES_COL_MAJOR, y_out, ldy,
                                                        static_cast<hipStream_t>(stream)));
 }
 
@@ -186,8 +199,9 @@ fp8q_status_t fp8q_quant_weight_block(const uint16_t* w, int64_t N, int64_t K, i
                                       int32_t block_n, int32_t block_k, int32_t fmt, uint8_t* q,
                                       int64_t ldq, void* scale_inv, void* stream) {
   if (N < 0 || K <= 0 || N > kMaxRows || K > kMaxK) return FP8Q_ERR_SHAPE;
-  enum { BLOCK, MX, TENSOR } kind;
+  enum { BLOCK, BLOCK_POW2, MX, TENSOR } kind;
   if (block_n == 128 && block_k == 128 && fmt == FP8Q_SCALE_F32) kind = BLOCK;
+  else if (block_n == 128 && block_k == 128 && fmt == FP8Q_SCALE_F32_POW2) kind = BLOCK_POW2;
   else if (block_n == 1 && block_k == 32 && fmt == FP8Q_SCALE_UE8M0) kind = MX;
   else if (block_n == N && block_k == K && fmt == FP8Q_SCALE_F32) kind = TENSOR;
   else return FP8Q_ERR_UNSUPPORTED;
@@ -199,10 +213,33 @@ fp8q_status_t fp8q_quant_weight_block(const uint16_t* w, int64_t N, int64_t K, i
   FP8Q_TRY(check_device());
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
-  if (kind == BLOCK) e = fp8q::launch_weight_block128(w, N, K, ldw, q, ldq, static_cast<float*>(scale_inv), st);
+  if (kind == BLOCK || kind == BLOCK_POW2)
+    e = fp8q::launch_weight_block128(w, N, K, ldw, q, ldq, static_cast<float*>(scale_inv), kind == BLOCK_POW2, st);
   else if (kind == MX) e = fp8q::launch_quant_group32mx(w, N, K, ldw, q, ldq, static_cast<uint8_t*>(scale_inv), 0, st);
   else e = fp8q::launch_weight_tensor(w, N, K, ldw, q, ldq, static_cast<float*>(scale_inv), st);
   return launch_status(e);
+}
+
+fp8q_status_t fp8q_requant_weight_pow2(const uint8_t* q_in, int64_t ldi, const float* s_in, int64_t N,
+                                       int64_t K, uint8_t* q_out, int64_t ldo, float* s_out, void* stream) {
+  if (N < 0 || K <= 0 || N > kMaxRows || K > kMaxK) return FP8Q_ERR_SHAPE;
+  if (N == 0) return FP8Q_OK;
+  FP8Q_TRY(check_matrix(q_in, K, ldi, 1));
+  FP8Q_TRY(check_matrix(q_out, K, ldo, 1));
+  if (s_in == nullptr || s_out == nullptr) return FP8Q_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(s_in) & 3u) || (reinterpret_cast<uintptr_t>(s_out) & 3u))
+    return FP8Q_ERR_MISALIGNED;
+  // outputs: in place on their own input, else disjoint from every input and
+  // from each other
+  const int64_t nscales = ((N + 127) / 128) * ((K + 127) / 128);
+  const Span qi = span(q_in, N, ldi, K, 1), qo = span(q_out, N, ldo, K, 1);
+  const Span si = span(s_in, 1, nscales, nscales, 4), so = span(s_out, 1, nscales, nscales, 4);
+  if (!(q_out == q_in && ldo == ldi) && overlap(qo, qi)) return FP8Q_ERR_VALUE;
+  if (s_out != s_in && overlap(so, si)) return FP8Q_ERR_VALUE;
+  if (overlap(qo, si) || overlap(so, qi) || overlap(qo, so)) return FP8Q_ERR_VALUE;
+  FP8Q_TRY(check_device());
+  return launch_status(fp8q::launch_requant_pow2(q_in, ldi, s_in, N, K, q_out, ldo, s_out,
+                                                  static_cast<hipStream_t>(stream)));
 }
 
 fp8q_status_t fp8q_gemm_blockscale(const uint8_t* a, int64_t lda, const float* a_scales,
@@ -212,7 +249,8 @@ fp8q_status_t fp8q_gemm_blockscale(const uint8_t* a, int64_t lda, const float* a
                                    void* stream) {
   if (M < 0 || N < 0 || K <= 0 || M > kMaxRows || N > kMaxRows || K > kMaxK) return FP8Q_ERR_SHAPE;
   if ((M / 128 + 1) * (N / 128 + 1) >= (int64_t(1) << 24)) return FP8Q_ERR_SHAPE;   // tile grid
-  if (gran != FP8Q_GRAN_BLOCK128 && gran != FP8Q_GRAN_PER_TENSOR) return FP8Q_ERR_UNSUPPORTED;
+  if (gran != FP8Q_GRAN_BLOCK128 && gran != FP8Q_GRAN_PER_TENSOR && gran != FP8Q_GRAN_BLOCK128_POW2)
+    return FP8Q_ERR_UNSUPPORTED;
   if (a_layout != FP8Q_SCALES_ROW_MAJOR && a_layout != FP8Q_SCALES_COL_MAJOR) return FP8Q_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) return FP8Q_OK;
   FP8Q_TRY(check_matrix(a, K, lda, 1));
@@ -225,8 +263,7 @@ fp8q_status_t fp8q_gemm_blockscale(const uint8_t* a, int64_t lda, const float* a
   FP8Q_TRY(check_device());
   return launch_status(fp8q::launch_gemm_blockscale(a, lda, a_scales, a_layout == FP8Q_SCALES_COL_MAJOR,
                                                      w, ldw, w_scale_inv, bias, y, ldy, M, N, K,
-                                                     gran == FP8Q_GRAN_PER_TENSOR,
-                                                     static_cast<hipStream_t>(stream)));
+                                                     gran, static_cast<hipStream_t>(stream)));
 }
 
 fp8q_status_t fp8q_gemm_mxfp8(const uint8_t* a, int64_t lda, const uint8_t* a_scales,

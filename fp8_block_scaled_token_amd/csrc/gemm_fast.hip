@@ -69,6 +69,8 @@ using namespace dma;
 template <int MODE_, int BM_, int BN_, int WM_, int WN_, int NTN_>
 struct FastTile {
   static constexpr int MODE = MODE_, BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  // fp32 scale words (block mode, and its power-of-two view)
+  static constexpr bool FP32S = MODE == MODE_BLOCK || MODE == MODE_BMX;
   // tile columns of one XCD's concurrently running group of tiles (the XCD's
   // workgroup slots divided by the group height of group_walk)
   static constexpr int NTN = NTN_;
@@ -103,6 +105,7 @@ template <class T, bool HALF>
 __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int m0, int n0, int gm, int gn,
                                           bool preloaded, bool has_next, int nm0, int nn0, int ngm, int ngn) {
   constexpr int MODE = T::MODE, BM = T::BM, BN = T::BN, WN = T::WN, NW = T::NW;
+  constexpr bool FP32S = T::FP32S;
   constexpr int RM = HALF ? T::BM / 2 : T::BM;
   constexpr int WTM = RM / T::WM, TM = WTM / 16, WTN = T::WTN, TN = T::TN;
   // a half tile's activation rows are spread over all waves too
@@ -156,13 +159,13 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
         const int g = q / WTM, rem = q % WTM;             // q < RM only when g < WM
         const int row = tm0 + g * WTM + 16 * (rem % TM) + rem / TM;
         const bool live = q < RM && row < p.M;
-        if (MODE == MODE_BLOCK)
+        if (FP32S)
           o.s = live ? (uint32_t)(p.sa_col_major ? row * 4 : row * p.KB * 4) : OOB;
         else
           o.s = live ? (uint32_t)(row * p.KB32) : OOB;
       } else {
         const int qw = q - BM;
-        if (MODE == MODE_BLOCK) {
+        if (FP32S) {
           const int blk = tn0 / 128 + qw;
           o.s = (qw < (BN + 127) / 128 && blk < p.NB) ? (uint32_t)(blk * p.KB * 4) : OOB;
         } else {
@@ -182,7 +185,7 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
 
   const bool wave_is_a = 64 * wave < BM;    // waves below BM/64 fetch activation scales
   i32x4 rSA = rA, rSW = rW;
-  if constexpr (MODE == MODE_BLOCK) {
+  if constexpr (FP32S) {
     rSA = rsrc(p.sa, (int64_t)p.M * p.KB * 4);
     rSW = rsrc(p.sw, (int64_t)p.NB * p.KB * 4);
   } else if constexpr (MODE == MODE_MX) {
@@ -193,7 +196,7 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
   // scales advance by M words, every other scale array by one word (block)
   // or four bytes (MX) per K block
   const uint32_t kstepS =
-      (MODE == MODE_BLOCK && p.sa_col_major && wave_is_a) ? (uint32_t)p.M * 4u : 4u;
+      (FP32S && p.sa_col_major && wave_is_a) ? (uint32_t)p.M * 4u : 4u;
   const i32x4 rS = wave_is_a ? rSA : rSW;
   const uint32_t smem_base = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 
@@ -302,6 +305,7 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
   Frag fb[TN], fr[LA + 1];
   uint32_t sav[TM] = {}, swb[TN] = {};    // activation / weight scale words
   float swv = 0.f;                        // block mode: this wave's weight scale
+  int swe = 127;                          // power-of-two view: its exponent byte
   auto load_regs = [&](int st) {
     const uint8_t* a = smem + st * STAGE;
     const uint8_t* w = a + ABYTES;
@@ -314,6 +318,8 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
                  std::integral_constant<int, TM>{});
     if constexpr (MODE == MODE_BLOCK)
       swv = __uint_as_float(reinterpret_cast<const uint32_t*>(a + SW_OFF)[(wn * WTN) / 128]);
+    if constexpr (MODE == MODE_BMX)
+      swe = (int)((reinterpret_cast<const uint32_t*>(a + SW_OFF)[(wn * WTN) / 128] >> 23) & 0xFFu);
     if constexpr (MODE == MODE_MX)
       read_words(reinterpret_cast<const uint32_t*>(a + SW_OFF) + wn * WTN + l16 * TN, swb,
                  std::integral_constant<int, TN>{});
@@ -342,6 +348,14 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
     } else if constexpr (MODE == MODE_TENSOR) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[i][j] = mfma_plain(fb[j].v, fa.v, acc[i][j]);
+    } else if constexpr (MODE == MODE_BMX) {
+      // power-of-two fp32 scales: the exponent field is the UE8M0 byte the
+      // scaled MFMA applies to all four 32-wide parts of the 128-wide block,
+      // so the rescale happens inside the MFMA and the accumulators carry
+      // across K blocks
+      const int sab = (int)((sav[i] >> 23) & 0xFFu);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma_mx(fb[j].v, fa.v, acc[i][j], swe, sab);
     } else {
       // scale byte of this lane's 32-wide K block (lane / 16) in each word
       const int sh = 8 * lq;
@@ -634,6 +648,7 @@ hipError_t launch_gemm_fast(GemmArgs p, int mode, hipStream_t stream) {
   const Plan pl = choose_plan(p);
   if (mode == MODE_BLOCK) launch_plan<MODE_BLOCK>(p, pl, stream);
   else if (mode == MODE_TENSOR) launch_plan<MODE_TENSOR>(p, pl, stream);
+  else if (mode == MODE_BMX) launch_plan<MODE_BMX>(p, pl, stream);
   else launch_plan<MODE_MX>(p, pl, stream);
   return hipGetLastError();
 }

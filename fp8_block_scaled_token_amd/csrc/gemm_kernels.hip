@@ -12,9 +12,17 @@
 //  MODE_MX      1x32 UE8M0 scales consumed by the scaled MFMA itself
 //               ([SGLFP8] "4. 블록 양자화 스케일 관리"; [SGL19] "Triton 分块内核在做什么":
 //               scale multiplies become exponent adds).
+//  MODE_BMX     block scales restricted to powers of two (block FP8 read as
+//               an MXFP8 view, [SGL19] "分块路径的后处理", "前向:激活怎么量化,
+//               GEMM 走哪条内核"; the scale as part of the MMA, [GLM17] "第 7 站:
+//               MoE——被排除在 FP8 之外的门控与 dispatch 的量化"): the formula of MODE_BLOCK, with
+//               the exponent bytes handed to the scaled MFMA (fast kernel
+//               only; the other kernels run these scales in MODE_BLOCK,
+//               which gives the same sum, as the products by powers of two
+//               are exact).
 //
 // Page titles: [SGL19] "SGLang 源码完全拆解(十九):量化方法的注册与层分派",
-// [SGLFP8] "[SGLang] FP8".
+// [SGLFP8] "[SGLang] FP8", [GLM17] "GLM-5.3 推理全链路(十七):精度账本".
 //
 // The contraction runs on v_mfma_*_16x16x128_f8f6f4: one instruction is
 // exactly one 128-wide K block of a 16x16 output tile, so P_b comes out of a
@@ -369,13 +377,15 @@ static hipError_t launch_mode(GemmArgs p, hipStream_t stream) {
 hipError_t launch_gemm_blockscale(const uint8_t* a, int64_t lda, const float* sa, int sa_col_major,
                                   const uint8_t* w, int64_t ldw, const float* sw,
                                   const uint16_t* bias, uint16_t* y, int64_t ldy, int64_t M,
-                                  int64_t N, int64_t K, int per_tensor, hipStream_t stream) {
+                                  int64_t N, int64_t K, int gran, hipStream_t stream) {
   GemmArgs p{};
   p.a = a; p.lda = lda; p.sa = sa; p.sa_col_major = sa_col_major;
   p.w = w; p.ldw = ldw; p.sw = sw; p.bias = bias; p.y = y; p.ldy = ldy;
   p.M = (int)M; p.N = (int)N; p.K = (int)K;
   p.KB = cdiv(K, 128); p.KB32 = cdiv(K, 32); p.NB = cdiv(N, 128);
-  return per_tensor ? launch_mode<MODE_TENSOR>(p, stream) : launch_mode<MODE_BLOCK>(p, stream);
+  if (gran == 1) return launch_mode<MODE_TENSOR>(p, stream);
+  if (gran == 2 && p.M > 64 && gemm_fast_eligible(p, MODE_BMX)) return launch_gemm_fast(p, MODE_BMX, stream);
+  return launch_mode<MODE_BLOCK>(p, stream);
 }
 
 hipError_t launch_gemm_mxfp8(const uint8_t* a, int64_t lda, const uint8_t* sa, const uint8_t* w,

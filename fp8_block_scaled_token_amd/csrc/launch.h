@@ -9,8 +9,9 @@ namespace fp8q {
 // Compute units of the current device (cached per device).
 int device_cu_count();
 
+// pow2: power-of-two fp32 scales (MX exponent rule on 128-wide groups)
 hipError_t launch_quant_group128(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
-                                 uint8_t* q, int64_t ldq, float* scales, int col_major,
+                                 uint8_t* q, int64_t ldq, float* scales, int col_major, int pow2,
                                  hipStream_t stream);
 hipError_t launch_quant_group32mx(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                   uint8_t* q, int64_t ldq, uint8_t* scales, int col_major,
@@ -20,24 +21,29 @@ hipError_t launch_quant_static(const uint16_t* x, int64_t M, int64_t K, int64_t 
 hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, float eps, int64_t M,
                                 int64_t K, int64_t ldx, uint8_t* q, int64_t ldq, float* scales,
                                 int col_major, uint16_t* y_out, int64_t ldy, hipStream_t stream);
-// Residual add (z = bf16(x + h) written to z_out), RMSNorm of z, then the
-// group-128 quantizer or, with static_scale, the per-tensor static one.
+// Residual add (z = bf16(x + h) written to z_out; none when h is null),
+// RMSNorm of z, then the group-128 quantizer (power-of-two scales if pow2)
+// or, with static_scale, the per-tensor static one.
 hipError_t launch_add_rmsnorm_quant(const uint16_t* x, int64_t ldx, const uint16_t* h, int64_t ldh,
                                     uint16_t* z_out, int64_t ldz, const uint16_t* gamma, float eps,
-                                    int64_t M, int64_t K, const float* static_scale, uint8_t* q,
+                                    int64_t M, int64_t K, const float* static_scale, int pow2, uint8_t* q,
                                     int64_t ldq, float* scales, int col_major, uint16_t* y_out,
                                     int64_t ldy, hipStream_t stream);
 hipError_t launch_weight_block128(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
-                                  uint8_t* q, int64_t ldq, float* scale_inv, hipStream_t stream);
+                                  uint8_t* q, int64_t ldq, float* scale_inv, int pow2, hipStream_t stream);
+// Block-FP8 codes and fp32 128x128 scales -> power-of-two scales (in place allowed).
+hipError_t launch_requant_pow2(const uint8_t* q_in, int64_t ldi, const float* s_in, int64_t N, int64_t K,
+                               uint8_t* q_out, int64_t ldo, float* s_out, hipStream_t stream);
 hipError_t launch_weight_tensor(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q,
                                 int64_t ldq, float* scale_inv, hipStream_t stream);
 
 // Scaled GEMMs: Y[M,N] (bf16) = A[M,K] (E4M3) * W[N,K]^T (E4M3).
-//   gran 0: 128-block fp32 scales; gran 1: per-tensor fp32 scalars.
+//   gran 0: 128-block fp32 scales; gran 1: per-tensor fp32 scalars;
+//   gran 2: 128-block power-of-two fp32 scales (applied inside the MFMA).
 hipError_t launch_gemm_blockscale(const uint8_t* a, int64_t lda, const float* sa, int sa_col_major,
                                   const uint8_t* w, int64_t ldw, const float* sw,
                                   const uint16_t* bias, uint16_t* y, int64_t ldy, int64_t M,
-                                  int64_t N, int64_t K, int per_tensor, hipStream_t stream);
+                                  int64_t N, int64_t K, int gran, hipStream_t stream);
 hipError_t launch_gemm_mxfp8(const uint8_t* a, int64_t lda, const uint8_t* sa, const uint8_t* w,
                              int64_t ldw, const uint8_t* sw, const uint16_t* bias, uint16_t* y,
                              int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t stream);

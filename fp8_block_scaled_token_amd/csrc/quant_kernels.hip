@@ -83,6 +83,43 @@ __device__ __forceinline__ uint2 quant8(const uint4& raw, float s, float r) {
   return encode8(t);
 }
 
+// Scale byte e + 127 for a block max a (>= 1e-10, a normal fp32 number
+// m * 2^E, 1 <= m < 2): 448 = 1.75 * 2^8, so the smallest e with a <= 448*2^e
+// is E - 8 when m <= 1.75 and E - 7 otherwise.
+__device__ __forceinline__ uint32_t ue8m0_byte(float amax) {
+  const uint32_t b = __float_as_uint(fmaxf(amax, kAmaxFloor));
+  const uint32_t biased = b >> 23;            // E + 127 (a > 0, normal)
+  const uint32_t man = b & 0x7FFFFFu;
+  return biased - 8u + (man > 0x600000u ? 1u : 0u);
+}
+
+// x * 2^-e is exact and |x| <= amax <= 448 * 2^e, so no clamp is needed.
+__device__ __forceinline__ uint2 quant8_mx(const uint4& raw, uint32_t byte) {
+  // 2^-e = 2^(127 - byte) as an fp32 bit pattern (byte <= 253 for bf16 input)
+  const float inv = __uint_as_float((254u - byte) << 23);
+  float v[8], t[8];
+  unpack8(raw, v);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) t[e] = v[e] * inv;
+  return encode8(t);
+}
+
+// Power-of-two group scales (the MX exponent rule on 128-wide groups):
+// amax[c] as in group_scales; byte[c] is the UE8M0 byte of this lane's group
+// in chunk c, s_mine (lane j < 4*CH) the fp32 scale 2^(byte-127) of group j.
+template <int CH>
+__device__ __forceinline__ void pow2_group_scales(const float (&amax)[CH], uint32_t (&byte)[CH], float& s_mine) {
+  const int lane = threadIdx.x & 63;
+  uint32_t b = 127u;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    byte[c] = ue8m0_byte(amax[c]);
+    const uint32_t v = (uint32_t)__shfl((int)byte[c], (lane & 3) << 4);
+    if ((lane >> 2) == c) b = v;
+  }
+  s_mine = __uint_as_float(b << 23);
+}
+
 // Store the wave's group scales: lane j < 4*CH holds group first_group + j.
 template <int CH>
 __device__ __forceinline__ void store_group_scales(float* scales, float s_mine, int64_t first_group,
@@ -106,7 +143,9 @@ __device__ __forceinline__ void row_block(int segs, int64_t& row, int64_t& seg) 
   seg = b % segs;
 }
 
-template <int CH>
+// POW2: scales restricted to powers of two (2^e, e by the MX round-up rule),
+// stored as fp32; codes x * 2^-e.
+template <int CH, bool POW2>
 __global__ __launch_bounds__(256) void quant_group128_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
     uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ scales, int col_major, int segs) {
@@ -132,18 +171,21 @@ __global__ __launch_bounds__(256) void quant_group128_kernel(
     }
   }
   float amax[CH], s[CH], r[CH], s_mine;
+  uint32_t byte[CH];
 #pragma unroll
   for (int c = 0; c < CH; ++c) amax[c] = max_row16(absmax8(raw[c]));
-  group_scales<CH>(amax, s, r, s_mine);
+  if constexpr (POW2) pow2_group_scales<CH>(amax, byte, s_mine);
+  else group_scales<CH>(amax, s, r, s_mine);
+  auto codes = [&](int c) { return POW2 ? quant8_mx(raw[c], byte[c]) : quant8(raw[c], s[c], r[c]); };
   if (full) {
     uint8_t* qs = qr + seg0 + 8 * lane;
 #pragma unroll
-    for (int c = 0; c < CH; ++c) st8(qs + 512 * c, quant8(raw[c], s[c], r[c]));
+    for (int c = 0; c < CH; ++c) st8(qs + 512 * c, codes(c));
   } else {
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int64_t k0 = seg0 + 512 * c + 8 * lane;
-      const uint2 o = quant8(raw[c], s[c], r[c]);
+      const uint2 o = codes(c);
       if (k0 < K) store8_masked(qr, k0, K, o);
     }
   }
@@ -152,27 +194,6 @@ __global__ __launch_bounds__(256) void quant_group128_kernel(
 
 // --------------------------------------------------------------------------
 // MXFP8 1x32 quantizer (UE8M0 scale bytes)
-
-// Scale byte e + 127 for a block max a (>= 1e-10, a normal fp32 number
-// m * 2^E, 1 <= m < 2): 448 = 1.75 * 2^8, so the smallest e with a <= 448*2^e
-// is E - 8 when m <= 1.75 and E - 7 otherwise.
-__device__ __forceinline__ uint32_t ue8m0_byte(float amax) {
-  const uint32_t b = __float_as_uint(fmaxf(amax, kAmaxFloor));
-  const uint32_t biased = b >> 23;            // E + 127 (a > 0, normal)
-  const uint32_t man = b & 0x7FFFFFu;
-  return biased - 8u + (man > 0x600000u ? 1u : 0u);
-}
-
-// x * 2^-e is exact and |x| <= amax <= 448 * 2^e, so no clamp is needed.
-__device__ __forceinline__ uint2 quant8_mx(const uint4& raw, uint32_t byte) {
-  // 2^-e = 2^(127 - byte) as an fp32 bit pattern (byte <= 253 for bf16 input)
-  const float inv = __uint_as_float((254u - byte) << 23);
-  float v[8], t[8];
-  unpack8(raw, v);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) t[e] = v[e] * inv;
-  return encode8(t);
-}
 
 template <int CH>
 __global__ __launch_bounds__(256) void quant_group32mx_kernel(
@@ -257,8 +278,9 @@ __global__ __launch_bounds__(256) void quant_static_kernel(
 // meet in LDS and are added in wave order (deterministic).
 //
 // ADD: the row first becomes z = bf16(x + h), which is written to the
-// residual output and is what the norm reads.  STAT: the normalized row is
-// quantized with one fixed per-tensor scale (no group scales).
+// residual output and is what the norm reads.  EXIT: how the normalized row
+// is quantized -- group-128 fp32 scales, one fixed per-tensor scale (no
+// group scales), or group-128 power-of-two scales.
 //
 // rmsnorm_quant_rows_kernel (K <= 4 * 512*CH): the workgroup owns a run of
 // consecutive rows (runs in XCD-contiguous order) and keeps a row in
@@ -284,7 +306,7 @@ struct RmsArgs {
   int64_t ldh;
   uint16_t* z_out;           // ADD: updated residual stream
   int64_t ldz;
-  const float* static_scale; // STAT: per-tensor scale
+  const float* static_scale; // EXIT_STATIC: per-tensor scale
 };
 
 template <int CH>
@@ -373,9 +395,12 @@ __device__ __forceinline__ float rms_inv(double ss, double* part, double inv_k, 
   return rsqrt_f64_to_f32(__builtin_fma(ss, inv_k, (double)eps));
 }
 
-// y = bf16((x * r) * g) for one segment, then its group quantization (STAT:
-// q = E4M3(clamp(fp32(y / s))) with the static scale s, IEEE division).
-template <int CH, bool STAT>
+enum { EXIT_GROUP = 0, EXIT_STATIC = 1, EXIT_POW2 = 2 };
+
+// y = bf16((x * r) * g) for one segment, then its quantization: group
+// scales, the static scale s (q = E4M3(clamp(fp32(y / s))), IEEE division),
+// or power-of-two group scales.
+template <int CH, int EXIT>
 __device__ __forceinline__ void norm_quant_seg(const RmsArgs& a, uint4 (&raw)[CH], const float (&gf)[CH][8],
                                                float rn, float s_stat, int64_t row, int64_t seg0) {
   const int lane = threadIdx.x & 63;
@@ -398,9 +423,9 @@ __device__ __forceinline__ void norm_quant_seg(const RmsArgs& a, uint4 (&raw)[CH
       if (full) *reinterpret_cast<uint4*>(yr + k0) = raw[c];
       else if (k0 < K) store8_bf16_masked(yr, k0, K, raw[c]);
     }
-    if (!STAT) amax[c] = max_row16(absmax8(raw[c]));
+    if (EXIT != EXIT_STATIC) amax[c] = max_row16(absmax8(raw[c]));
   }
-  if (STAT) {
+  if (EXIT == EXIT_STATIC) {
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int64_t k0 = seg0 + 512 * c + 8 * lane;
@@ -415,18 +440,20 @@ __device__ __forceinline__ void norm_quant_seg(const RmsArgs& a, uint4 (&raw)[CH
     return;
   }
   float s[CH], r[CH], s_mine;
-  group_scales<CH>(amax, s, r, s_mine);
+  uint32_t byte[CH];
+  if constexpr (EXIT == EXIT_POW2) pow2_group_scales<CH>(amax, byte, s_mine);
+  else group_scales<CH>(amax, s, r, s_mine);
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int64_t k0 = seg0 + 512 * c + 8 * lane;
-    const uint2 o = quant8(raw[c], s[c], r[c]);
+    const uint2 o = EXIT == EXIT_POW2 ? quant8_mx(raw[c], byte[c]) : quant8(raw[c], s[c], r[c]);
     if (full) st8(qr + k0, o);
     else if (k0 < K) store8_masked(qr, k0, K, o);
   }
   store_group_scales<CH>(a.scales, s_mine, seg0 / 128, (K + 127) >> 7, a.M, row, a.col_major);
 }
 
-template <int CH, bool ADD, bool STAT>
+template <int CH, bool ADD, int EXIT>
 __global__ __launch_bounds__(256) void rmsnorm_quant_rows_kernel(RmsArgs a, int rows_per_wg) {
   __shared__ double part[2][4];
   const int wave = threadIdx.x >> 6;
@@ -434,7 +461,7 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_rows_kernel(RmsArgs a, int 
   const int64_t r1 = r0 + rows_per_wg < a.M ? r0 + rows_per_wg : a.M;
   if (r0 >= a.M) return;                       // whole workgroup
   const int64_t seg0 = (int64_t)wave * (512 * CH);
-  const float s_stat = STAT ? *a.static_scale : 1.0f;
+  const float s_stat = EXIT == EXIT_STATIC ? *a.static_scale : 1.0f;
   uint4 cur[CH], nxt[CH];
   uint4 hcur[ADD ? CH : 1], hnxt[ADD ? CH : 1];
   float gf[CH][8];          // gamma of this wave's segment, unpacked once
@@ -461,7 +488,7 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_rows_kernel(RmsArgs a, int 
     // the two slot sets alternate; the barrier inside rms_inv of row i+1
     // orders every read of set (i & 1) before the writes of row i+2
     const float rn = rms_inv(sumsq_seg<CH>(buf, 0.0), part[(row - r0) & 1], inv_k, a.eps);
-    if (seg0 < a.K) norm_quant_seg<CH, STAT>(a, buf, gf, rn, s_stat, row, seg0);
+    if (seg0 < a.K) norm_quant_seg<CH, EXIT>(a, buf, gf, rn, s_stat, row, seg0);
   };
   // rows alternate between the two buffer sets (no copies between rows)
   for (int64_t row = r0; row < r1; row += 2) {
@@ -470,7 +497,7 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_rows_kernel(RmsArgs a, int 
   }
 }
 
-template <int CH, bool ADD, bool STAT>
+template <int CH, bool ADD, int EXIT>
 __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(RmsArgs a) {
   __shared__ double part[4];
   const int wave = threadIdx.x >> 6;
@@ -479,7 +506,7 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(RmsArgs a) {
   const uint16_t* hr = ADD ? a.h + row * a.ldh : nullptr;
   constexpr int64_t SEG = 512 * CH;
   const int64_t npass = (a.K + 4 * SEG - 1) / (4 * SEG);
-  const float s_stat = STAT ? *a.static_scale : 1.0f;
+  const float s_stat = EXIT == EXIT_STATIC ? *a.static_scale : 1.0f;
   uint4 raw[CH], gr[CH];
   double ss = 0.0;
   for (int64_t it = 0; it < npass; ++it) {
@@ -504,7 +531,7 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(RmsArgs a) {
     float gf[CH][8];
 #pragma unroll
     for (int c = 0; c < CH; ++c) unpack8(gr[c], gf[c]);
-    norm_quant_seg<CH, STAT>(a, raw, gf, rn, s_stat, row, seg0);
+    norm_quant_seg<CH, EXIT>(a, raw, gf, rn, s_stat, row, seg0);
   }
 }
 
@@ -516,6 +543,8 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(RmsArgs a) {
 //   MODE 1: per-tensor pass 1 -- fold the block amax into *slot (integer max
 //           of the non-negative fp32 bit patterns: order independent).
 //   MODE 2: per-tensor pass 2 -- quantize with s from the tensor amax in *slot.
+//   MODE 3: block scale = the power of two 2^e of the MX round-up rule;
+//           codes w * 2^-e.
 
 template <int MODE>
 __global__ __launch_bounds__(256) void weight_block_kernel(
@@ -547,6 +576,16 @@ __global__ __launch_bounds__(256) void weight_block_kernel(
   } else {
     amax = __uint_as_float(*slot);
   }
+  if constexpr (MODE == 3) {
+    const uint32_t byte = ue8m0_byte(amax);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t n = bn * 128 + (t >> 4) + 16 * i;
+      if (n < N && k0 < K) store8_masked(q + n * ldq, k0, K, quant8_mx(raw[i], byte));
+    }
+    if (t == 0) scale_out[bn * KB + bk] = __uint_as_float(byte << 23);
+    return;
+  }
   const float s = fmaxf(amax, kAmaxFloor) / kFp8Max;
   const float r = 1.0f / s;
 #pragma unroll
@@ -555,6 +594,69 @@ __global__ __launch_bounds__(256) void weight_block_kernel(
     if (n < N && k0 < K) store8_masked(q + n * ldq, k0, K, quant8(raw[i], s, r));
   }
   if (MODE == 0 && t == 0) scale_out[bn * KB + bk] = s;
+}
+
+// fp32 product a * b rounded to odd: the nearest-rounded product, moved one
+// ulp toward the exact value (whose remainder an FMA gives exactly) when it is
+// inexact and its last bit is even.  Rounding that to a format at least two
+// bits narrower is the correct rounding of the exact product.
+__device__ __forceinline__ float mul_round_odd(float a, float b) {
+  const float p = a * b;
+  const float e = __builtin_fmaf(a, b, -p);
+  uint32_t bits = __float_as_uint(p);
+  if (e != 0.0f && (bits & 1u) == 0u) bits += ((__float_as_uint(e) ^ bits) & 0x80000000u) ? 0xFFFFFFFFu : 1u;
+  return __uint_as_float(bits);
+}
+
+// Re-quantization of one 128x128 block-FP8 block to a power-of-two scale:
+// s' = the smallest power of two >= s, codes E4M3(decode(q) * (s / s')).  For
+// a positive normal s = 1.f * 2^E, s' = 2^E when f = 0 and 2^(E+1) otherwise,
+// and s / s' (1 or 0.1f in binary) keeps s's mantissa.  The exact product of
+// a 4-bit code value and that 24-bit ratio can need 28 bits, and its
+// nearest fp32 value can be an E4M3 rounding midpoint that the exact value is
+// not; the product is therefore rounded to odd in fp32 before the E4M3
+// conversion rounds it to nearest-even.  |decode(q)| <= 448 and s / s' <= 1,
+// so nothing saturates.  In place is allowed (q_out == q_in, s_out == s_in):
+// every thread reads its codes before writing them, and the scale is written
+// after a barrier that follows every thread's read of it.
+__global__ __launch_bounds__(256) void requant_pow2_kernel(
+    const uint8_t* q_in, int64_t ldi, const float* s_in, int64_t N, int64_t K,
+    uint8_t* q_out, int64_t ldo, float* s_out, int64_t KB) {
+  const int t = threadIdx.x;
+  const int64_t bn = blockIdx.y, bk = blockIdx.x;
+  const int64_t k0 = bk * 128 + 8 * (t & 15);
+  const uint32_t b = __float_as_uint(s_in[bn * KB + bk]);
+  const uint32_t f = b & 0x7FFFFFu;
+  const uint32_t eb = (b >> 23) + (f ? 1u : 0u);              // biased exponent of s'
+  const float mul = __uint_as_float(f | ((f ? 126u : 127u) << 23));
+#pragma unroll 4
+  for (int i = 0; i < 8; ++i) {
+    const int64_t n = bn * 128 + (t >> 4) + 16 * i;
+    if (n >= N || k0 >= K) continue;
+    const uint8_t* src = q_in + n * ldi;
+    uint2 c;
+    if (k0 + 8 <= K) {
+      c = *reinterpret_cast<const uint2*>(src + k0);
+    } else {
+      uint32_t w[2] = {0u, 0u};
+      for (int e = 0; k0 + e < K; ++e) w[e >> 2] |= (uint32_t)src[k0 + e] << (8 * (e & 3));
+      c = make_uint2(w[0], w[1]);
+    }
+    float v[8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t word = h ? c.y : c.x;
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true);
+      v[4 * h + 0] = mul_round_odd(lo[0], mul);
+      v[4 * h + 1] = mul_round_odd(lo[1], mul);
+      v[4 * h + 2] = mul_round_odd(hi[0], mul);
+      v[4 * h + 3] = mul_round_odd(hi[1], mul);
+    }
+    store8_masked(q_out + n * ldo, k0, K, encode8(v));
+  }
+  __syncthreads();
+  if (t == 0) s_out[bn * KB + bk] = __uint_as_float(eb << 23);
 }
 
 __global__ void zero_slot_kernel(uint32_t* slot) { *slot = 0u; }
@@ -579,18 +681,24 @@ static inline bool row_grid_fits(int64_t M, int64_t segs) { return ceil_div(M, 4
 static inline dim3 row_grid(int64_t M, int64_t segs) { return dim3((unsigned)(ceil_div(M, 4) * segs)); }
 
 hipError_t launch_quant_group128(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
-                                 uint8_t* q, int64_t ldq, float* scales, int col_major,
+                                 uint8_t* q, int64_t ldq, float* scales, int col_major, int pow2,
                                  hipStream_t stream) {
   const int ch = row_chunks(K);
   const int segs = (int)ceil_div(K, 512 * ch);
   if (!row_grid_fits(M, segs)) return hipErrorInvalidConfiguration;
   const dim3 grid = row_grid(M, segs), block(256);
-  if (ch == 1)
-    hipLaunchKernelGGL(quant_group128_kernel<1>, grid, block, 0, stream, x, M, K, ldx, q, ldq, scales, col_major, segs);
-  else if (ch == 2)
-    hipLaunchKernelGGL(quant_group128_kernel<2>, grid, block, 0, stream, x, M, K, ldx, q, ldq, scales, col_major, segs);
-  else
-    hipLaunchKernelGGL(quant_group128_kernel<4>, grid, block, 0, stream, x, M, K, ldx, q, ldq, scales, col_major, segs);
+#define FP8Q_G128(CH, P2) \
+  hipLaunchKernelGGL((quant_group128_kernel<CH, P2>), grid, block, 0, stream, x, M, K, ldx, q, ldq, scales, col_major, segs)
+  if (pow2) {
+    if (ch == 1) FP8Q_G128(1, true);
+    else if (ch == 2) FP8Q_G128(2, true);
+    else FP8Q_G128(4, true);
+  } else {
+    if (ch == 1) FP8Q_G128(1, false);
+    else if (ch == 2) FP8Q_G128(2, false);
+    else FP8Q_G128(4, false);
+  }
+#undef FP8Q_G128
   return hipGetLastError();
 }
 
@@ -628,11 +736,11 @@ int resident_wgs(const void* kern) {
   return n;
 }
 
-template <bool ADD, bool STAT>
+template <bool ADD, int EXIT>
 hipError_t dispatch_rmsnorm(const RmsArgs& a, hipStream_t stream) {
   const dim3 block(256);
   if (a.K > 4 * 512 * 8) {   // long rows: one workgroup per row, two reads
-    hipLaunchKernelGGL((rmsnorm_quant_kernel<4, ADD, STAT>), dim3((unsigned)a.M), block, 0, stream, a);
+    hipLaunchKernelGGL((rmsnorm_quant_kernel<4, ADD, EXIT>), dim3((unsigned)a.M), block, 0, stream, a);
     return hipGetLastError();
   }
   // up to four workgroups per CU, each a run of consecutive rows (measured
@@ -643,7 +751,7 @@ hipError_t dispatch_rmsnorm(const RmsArgs& a, hipStream_t stream) {
 #endif
 #define FP8Q_RMS(CH)                                                                                   \
   do {                                                                                                 \
-    const auto kern = rmsnorm_quant_rows_kernel<CH, ADD, STAT>;                                        \
+    const auto kern = rmsnorm_quant_rows_kernel<CH, ADD, EXIT>;                                        \
     static const int fit = resident_wgs(reinterpret_cast<const void*>(kern));                          \
     const int64_t wgs = (int64_t)device_cu_count() * (fit < FP8Q_RMS_WGS_PER_CU ? fit : FP8Q_RMS_WGS_PER_CU); \
     const int rows = (int)ceil_div(a.M, wgs);                                                          \
@@ -667,26 +775,42 @@ hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, float 
                                 int col_major, uint16_t* y_out, int64_t ldy, hipStream_t stream) {
   const RmsArgs a{x, gamma, eps, M, K, ldx, q, ldq, scales, col_major, y_out, ldy,
                   nullptr, 0, nullptr, 0, nullptr};
-  return dispatch_rmsnorm<false, false>(a, stream);
+  return dispatch_rmsnorm<false, EXIT_GROUP>(a, stream);
 }
 
 hipError_t launch_add_rmsnorm_quant(const uint16_t* x, int64_t ldx, const uint16_t* h, int64_t ldh,
                                     uint16_t* z_out, int64_t ldz, const uint16_t* gamma, float eps,
-                                    int64_t M, int64_t K, const float* static_scale, uint8_t* q,
+                                    int64_t M, int64_t K, const float* static_scale, int pow2, uint8_t* q,
                                     int64_t ldq, float* scales, int col_major, uint16_t* y_out,
                                     int64_t ldy, hipStream_t stream) {
   const RmsArgs a{x, gamma, eps, M, K, ldx, q, ldq, scales, col_major, y_out, ldy,
                   h, ldh, z_out, ldz, static_scale};
-  return static_scale != nullptr ? dispatch_rmsnorm<true, true>(a, stream)
-                                 : dispatch_rmsnorm<true, false>(a, stream);
+  if (h == nullptr) {
+    if (static_scale != nullptr) return dispatch_rmsnorm<false, EXIT_STATIC>(a, stream);
+    return pow2 ? dispatch_rmsnorm<false, EXIT_POW2>(a, stream) : dispatch_rmsnorm<false, EXIT_GROUP>(a, stream);
+  }
+  if (static_scale != nullptr) return dispatch_rmsnorm<true, EXIT_STATIC>(a, stream);
+  return pow2 ? dispatch_rmsnorm<true, EXIT_POW2>(a, stream) : dispatch_rmsnorm<true, EXIT_GROUP>(a, stream);
 }
 
 hipError_t launch_weight_block128(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
-                                  uint8_t* q, int64_t ldq, float* scale_inv, hipStream_t stream) {
+                                  uint8_t* q, int64_t ldq, float* scale_inv, int pow2, hipStream_t stream) {
   const int64_t KB = ceil_div(K, 128);
   const dim3 grid((unsigned)KB, (unsigned)ceil_div(N, 128)), block(256);
-  hipLaunchKernelGGL(weight_block_kernel<0>, grid, block, 0, stream, w, N, K, ldw, q, ldq, scale_inv,
-                     (uint32_t*)nullptr, KB);
+  if (pow2)
+    hipLaunchKernelGGL(weight_block_kernel<3>, grid, block, 0, stream, w, N, K, ldw, q, ldq, scale_inv,
+                       (uint32_t*)nullptr, KB);
+  else
+    hipLaunchKernelGGL(weight_block_kernel<0>, grid, block, 0, stream, w, N, K, ldw, q, ldq, scale_inv,
+                       (uint32_t*)nullptr, KB);
+  return hipGetLastError();
+}
+
+hipError_t launch_requant_pow2(const uint8_t* q_in, int64_t ldi, const float* s_in, int64_t N, int64_t K,
+                               uint8_t* q_out, int64_t ldo, float* s_out, hipStream_t stream) {
+  const int64_t KB = ceil_div(K, 128);
+  const dim3 grid((unsigned)KB, (unsigned)ceil_div(N, 128)), block(256);
+  hipLaunchKernelGGL(requant_pow2_kernel, grid, block, 0, stream, q_in, ldi, s_in, N, K, q_out, ldo, s_out, KB);
   return hipGetLastError();
 }
 

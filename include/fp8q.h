@@ -65,9 +65,12 @@ typedef enum {
   FP8Q_ERR_VALUE = 7         /* invalid scalar argument (e.g. eps <= 0)         */
 } fp8q_status_t;
 
-typedef enum { FP8Q_SCALE_F32 = 0, FP8Q_SCALE_UE8M0 = 1 } fp8q_scale_fmt_t;
+/* FP8Q_SCALE_F32_POW2: fp32 scales restricted to powers of two 2^e (e from the
+ * round-up rule below), so that each one is exactly a UE8M0 value: its fp32
+ * exponent field is the byte e + 127 ("block FP8 as an MXFP8 view"). */
+typedef enum { FP8Q_SCALE_F32 = 0, FP8Q_SCALE_UE8M0 = 1, FP8Q_SCALE_F32_POW2 = 2 } fp8q_scale_fmt_t;
 typedef enum { FP8Q_SCALES_ROW_MAJOR = 0, FP8Q_SCALES_COL_MAJOR = 1 } fp8q_scale_layout_t;
-typedef enum { FP8Q_GRAN_BLOCK128 = 0, FP8Q_GRAN_PER_TENSOR = 1 } fp8q_gran_t;
+typedef enum { FP8Q_GRAN_BLOCK128 = 0, FP8Q_GRAN_PER_TENSOR = 1, FP8Q_GRAN_BLOCK128_POW2 = 2 } fp8q_gran_t;
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* fp8q_status_string(fp8q_status_t s);
@@ -92,6 +95,9 @@ int fp8q_abi_version(void);
  *       스케일 관리"): uint8 byte = e + 127 with e the smallest integer such
  *       that max(amax, 1e-10) <= 448 * 2^e (the round-up rule of [GLM17]
  *       "第 4 站:索引器"); q = E4M3(x * 2^-e).
+ *     group_size 128, fmt FP8Q_SCALE_F32_POW2 (the power-of-two activation
+ *       scales of [SGL19] "Triton 分块内核在做什么", act_scale_ue8m0): float
+ *       s = 2^e with e as for MXFP8 over the 128-wide group; q = E4M3(x * 2^-e).
  *   layout  FP8Q_SCALES_ROW_MAJOR: scales[row * G + g];
  *           FP8Q_SCALES_COL_MAJOR: scales[g * M + row] (the [groups, rows]
  *           layout of [GLM17] "第 7 站:MoE").
@@ -99,8 +105,8 @@ int fp8q_abi_version(void);
  *           device fp32 scalar s ([SGL19] "激活量化的三种选择": a fixed
  *           input_scale); q = E4M3(clamp(fp32(x / s))); group_size, fmt and
  *           layout are ignored and `scales` may be NULL.  s must be > 0.
- * Errors: group_size/fmt pairs other than (128, F32) and (32, UE8M0) ->
- *   FP8Q_ERR_UNSUPPORTED.
+ * Errors: group_size/fmt pairs other than (128, F32), (128, F32_POW2) and
+ *   (32, UE8M0) -> FP8Q_ERR_UNSUPPORTED.
  */
 fp8q_status_t fp8q_quant_act_group(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                    int32_t group_size, int32_t fmt, int32_t layout,
@@ -138,16 +144,18 @@ fp8q_status_t fp8q_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, float
  * ("第 6 站:o_proj、残差流与 AllReduce 为什么停在 BF16").  Per row:
  *   z_k = bf16(x_k + h_k)   (the correctly rounded sum)  -> residual_out,
  *   r, y as in fp8q_rmsnorm_quant, computed on z,
- *   static_scale == NULL: (q, scales) = group-128 quantization of y (F32,
- *                         `layout` as in fp8q_quant_act_group);
+ *   static_scale == NULL: (q, scales) = group-128 quantization of y with
+ *                         fmt FP8Q_SCALE_F32 or FP8Q_SCALE_F32_POW2 (as in
+ *                         fp8q_quant_act_group; `layout` likewise);
  *   static_scale != NULL: q = E4M3(clamp(fp32(y / s))) with the device fp32
- *                         scalar s > 0; `scales` and `layout` are ignored and
- *                         `scales` may be NULL.
- * The outputs are bit-identical to an add, fp8q_rmsnorm_quant (or RMSNorm
- * then fp8q_quant_act_group with static_scale) run one after the other.
+ *                         scalar s > 0; `scales`, `fmt` and `layout` are
+ *                         ignored and `scales` may be NULL.
+ * The outputs are bit-identical to an add, then RMSNorm, then
+ * fp8q_quant_act_group, run one after the other.
  *
  *   x             bf16 [M, ldx]  residual stream (input).
- *   h             bf16 [M, ldh]  sublayer output (input).
+ *   h             bf16 [M, ldh]  sublayer output (input), or NULL: no add
+ *                 (z = x; residual_out must then be NULL too).
  *   residual_out  bf16 [M, ldr]  updated stream z.  It may be x itself (same
  *                 pointer and ldr == ldx, the in-place update) or h itself;
  *                 any other overlap with x or h -> FP8Q_ERR_VALUE.
@@ -157,7 +165,7 @@ fp8q_status_t fp8q_rmsnorm_quant(const uint16_t* x, const uint16_t* gamma, float
  */
 fp8q_status_t fp8q_add_rmsnorm_quant(const uint16_t* x, int64_t ldx, const uint16_t* h, int64_t ldh,
                                      uint16_t* residual_out, int64_t ldr, const uint16_t* gamma,
-                                     float eps, int64_t M, int64_t K, int32_t layout,
+                                     float eps, int64_t M, int64_t K, int32_t fmt, int32_t layout,
                                      const float* static_scale, uint8_t* q, int64_t ldq,
                                      float* scales, uint16_t* y_out, int64_t ldy, void* stream);
 
@@ -177,11 +185,34 @@ fp8q_status_t fp8q_add_rmsnorm_quant(const uint16_t* x, int64_t ldx, const uint1
  *                                    reading of [SGLFP8] "1. Fp8Config 초기화")
  *     (N, K, FP8Q_SCALE_F32)      -> per-tensor: one float at scale_inv[0]
  *                                    (scale_inv is also used as scratch).
+ *     (128, 128, FP8Q_SCALE_F32_POW2) -> float scale_inv [ceil(N/128), ceil(K/128)],
+ *                                    each 2^e with e the smallest integer such
+ *                                    that max(amax, 1e-10) <= 448 * 2^e;
+ *                                    q = E4M3(w * 2^-e).
  *   w bf16 [N, ldw];  q E4M3 [N, ldq].
  */
 fp8q_status_t fp8q_quant_weight_block(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
                                       int32_t block_n, int32_t block_k, int32_t fmt,
                                       uint8_t* q, int64_t ldq, void* scale_inv, void* stream);
+
+/*
+ * fp8q_requant_weight_pow2 -- block-FP8 weights re-expressed with power-of-two scales.
+ *
+ * [SGL19] "分块路径的后处理": block FP8 may be used as an MXFP8 view, whose
+ * hardware consumes power-of-two (UE8M0) scales ("前向:激活怎么量化,GEMM 走哪条
+ * 内核" lists AMD's block-as-MXFP8 path; "为什么显式指定后端仍然可能被改写": a
+ * kernel that needs UE8M0 scales cannot take fp32 block scales as they are).
+ * For each 128x128 block with fp32 scale s: s' = the smallest power of two
+ * >= s, q' = E4M3(decode(q) * s / s') (correctly rounded; never saturates).
+ *
+ *   q_in  E4M3 [N, ldi];  s_in float [ceil(N/128), ceil(K/128)] (positive,
+ *         normal, finite -- other values give unspecified results).
+ *   q_out E4M3 [N, ldo];  s_out float, same shape as s_in.
+ *   In place is allowed: q_out == q_in with ldo == ldi, s_out == s_in;
+ *   any other overlap between an output and an input -> FP8Q_ERR_VALUE.
+ */
+fp8q_status_t fp8q_requant_weight_pow2(const uint8_t* q_in, int64_t ldi, const float* s_in, int64_t N,
+                                       int64_t K, uint8_t* q_out, int64_t ldo, float* s_out, void* stream);
 
 /*
  * fp8q_gemm_blockscale -- Y = A * W^T with FP8 operands and fp32 scales.
@@ -195,6 +226,14 @@ fp8q_status_t fp8q_quant_weight_block(const uint16_t* w, int64_t N, int64_t K, i
  *   w_scale_inv float [ceil(N/128), ceil(K/128)].
  * gran FP8Q_GRAN_PER_TENSOR: Y = bf16(s_a * s_w * sum_k A[i,k]*W[j,k] + bias[j])
  *   with a_scales and w_scale_inv each pointing at one float.
+ * gran FP8Q_GRAN_BLOCK128_POW2: the FP8Q_GRAN_BLOCK128 formula and layouts,
+ *   with every scale a power of two (FP8Q_SCALE_F32_POW2 quantizers,
+ *   fp8q_requant_weight_pow2): the GEMM hands the scales' exponent bytes to
+ *   the scaled MFMA, which applies them itself ([GLM17] "第 7 站:MoE——被排除在
+ *   FP8 之外的门控与 dispatch 的量化": the scale becomes part of the matrix
+ *   instruction and the per-element dequantization disappears).  A scale
+ *   that is not a power of two is read as the power of two of its exponent
+ *   field (its mantissa is ignored).
  *
  *   a    E4M3 [M, lda];  w E4M3 [N, ldw] (row = output channel);
  *   bias optional bf16 [N] (NULL = none);  y bf16 [M, ldy].

@@ -244,11 +244,12 @@ def residual_add(x, h):
     return bf16.round_from_f64(np.asarray(x, dtype=np.float64) + np.asarray(h, dtype=np.float64))
 
 
-def add_rmsnorm_quant(x, h, g, eps: float, static_scale=None, group: int = 128, r=None):
-    """Residual add -> RMSNorm -> bf16 -> quantization (readings vi, viii).
+def add_rmsnorm_quant(x, h, g, eps: float, static_scale=None, group: int = 128, r=None, pow2: bool = False):
+    """Residual add -> RMSNorm -> bf16 -> quantization (readings vi, viii, ix).
 
-    static_scale None: dynamic group quantization (q, s per group);
-    otherwise per-tensor static quantization with that fp32 scale (s = None).
+    static_scale None: dynamic group quantization (q, s per group; power-of-two
+    scales if pow2); otherwise per-tensor static quantization with that fp32
+    scale (s = None).
     Returns dict(z, q, s, y, r, r_alt, ambiguous); pass ``r`` to evaluate the
     pipeline with a chosen per-row factor (for near-tie rows).
     """
@@ -259,10 +260,12 @@ def add_rmsnorm_quant(x, h, g, eps: float, static_scale=None, group: int = 128, 
     else:
         r_alt, amb = None, None
     y = rmsnorm_apply(zf, g, r)
-    if static_scale is None:
-        q, s = quant_group(bf16.to_f32(y), group)
-    else:
+    if static_scale is not None:
         q, s = quant_static(bf16.to_f32(y), static_scale), None
+    elif pow2:
+        q, s = quant_group_pow2(bf16.to_f32(y), group)
+    else:
+        q, s = quant_group(bf16.to_f32(y), group)
     return {"z": z, "q": q, "s": s, "y": y, "r": r, "r_alt": r_alt, "ambiguous": amb}
 
 

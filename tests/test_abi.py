@@ -68,6 +68,7 @@ def test_quant_act_group_validation(lib):
     assert f(A, 4, 128, 128, 64, 0, 0, None, B, 128, C, None) == 3       # group 64
     assert f(A, 4, 128, 128, 128, 1, 0, None, B, 128, C, None) == 3      # UE8M0 with 128
     assert f(A, 4, 128, 128, 32, 0, 0, None, B, 128, C, None) == 3       # f32 with 32
+    assert f(A, 4, 128, 128, 32, 2, 0, None, B, 128, C, None) == 3       # pow2 with 32
     assert f(A, 4, 128, 128, 128, 0, 7, None, B, 128, C, None) == 3      # bad layout
     assert f(A, 0, 128, 128, 128, 0, 0, None, None, 128, None, None) == 0  # M == 0: no-op
     assert f(None, 4, 128, 128, 128, 0, 0, None, B, 128, C, None) == 1   # null x
@@ -92,10 +93,10 @@ def test_add_rmsnorm_quant_validation(lib):
     f = lib.fp8q_add_rmsnorm_quant
     D = ctypes.c_void_p(0x400000)
     E = ctypes.c_void_p(0x500000)
-    ok = (A, 128, B, 128, C, 128, D, 1e-6, 4, 128, 0, None, E, 128, D, None, 0, None)
+    ok = (A, 128, B, 128, C, 128, D, 1e-6, 4, 128, 0, 0, None, E, 128, D, None, 0, None)
 
     def call(**kw):
-        names = ["x", "ldx", "h", "ldh", "z", "ldz", "g", "eps", "M", "K", "layout", "stat", "q", "ldq",
+        names = ["x", "ldx", "h", "ldh", "z", "ldz", "g", "eps", "M", "K", "fmt", "layout", "stat", "q", "ldq",
                  "s", "y", "ldy", "stream"]
         args = list(ok)
         for k, v in kw.items():
@@ -107,8 +108,9 @@ def test_add_rmsnorm_quant_validation(lib):
     assert call(eps=0.0) == 7
     assert call(eps=float("inf")) == 7
     assert call(layout=3) == 3
+    assert call(fmt=1) == 3                                               # UE8M0 bytes: not from the norm
+    assert call(h=None) == 7                                              # no add, but a residual output
     assert call(M=0, x=None, h=None, z=None) == 0                         # no-op
-    assert call(h=None) == 1
     assert call(z=None) == 1
     assert call(g=None) == 1
     assert call(s=None) == 1                                              # dynamic exit needs scales
@@ -123,11 +125,31 @@ def test_add_rmsnorm_quant_validation(lib):
     # accepted layouts reach the device check: see test_device_check_without_gpu
 
 
+def test_requant_weight_pow2_validation(lib):
+    f = lib.fp8q_requant_weight_pow2
+    Q2 = ctypes.c_void_p(0x400000)
+    S2 = ctypes.c_void_p(0x500000)
+    assert f(A, 256, C, -1, 256, Q2, 256, S2, None) == 2
+    assert f(A, 256, C, 256, 0, Q2, 256, S2, None) == 2
+    assert f(A, 256, C, 0, 256, None, 256, None, None) == 0                 # N == 0
+    assert f(A, 256, None, 256, 256, Q2, 256, S2, None) == 1
+    assert f(A, 256, C, 256, 256, Q2, 256, None, None) == 1
+    assert f(A, 200, C, 256, 256, Q2, 256, S2, None) == 2                    # ldi < K
+    assert f(A, 256, C, 256, 256, Q2, 264, S2, None) == 4                    # ldo % 16
+    assert f(A, 256, ctypes.c_void_p(0x300002), 256, 256, Q2, 256, S2, None) == 4
+    assert f(A, 256, C, 256, 256, ctypes.c_void_p(0x100000 + 256), 256, S2, None) == 7   # overlaps q_in
+    assert f(A, 256, C, 256, 256, A, 512, S2, None) == 7                     # q_in's base, other stride
+    assert f(A, 256, C, 256, 256, Q2, 256, ctypes.c_void_p(0x300000 + 4), None) == 7     # overlaps s_in
+    assert f(A, 256, C, 256, 256, ctypes.c_void_p(0x300000), 256, S2, None) == 7        # q_out over s_in
+    assert f(A, 256, C, 256, 256, Q2, 256, ctypes.c_void_p(0x100000), None) == 7        # s_out over q_in
+
+
 def test_quant_weight_block_validation(lib):
     f = lib.fp8q_quant_weight_block
     assert f(A, 256, 256, 256, 64, 64, 0, B, 256, C, None) == 3          # 64x64 blocks
     assert f(A, 256, 256, 256, 1, 32, 0, B, 256, C, None) == 3           # MX block, f32
     assert f(A, 256, 256, 256, 32, 32, 1, B, 256, C, None) == 3          # MX must be 1x32
+    assert f(A, 256, 256, 256, 1, 32, 2, B, 256, C, None) == 3           # pow2 needs 128x128
     assert f(A, 256, 256, 256, 128, 128, 0, B, 256, None, None) == 1
     assert f(A, -2, 256, 256, 128, 128, 0, B, 256, C, None) == 2
 
@@ -136,6 +158,7 @@ def test_gemm_validation(lib):
     g = lib.fp8q_gemm_blockscale
     assert g(A, 128, C, 0, B, 128, C, None, C, 256, 4, 256, 0, 0, None) == 2     # K == 0
     assert g(A, 128, C, 0, B, 128, C, None, C, 256, 4, 256, 128, 9, None) == 3   # gran
+    assert g(A, 128, C, 0, B, 128, C, None, C, 256, 4, 256, 128, 3, None) == 3
     assert g(A, 128, C, 0, B, 128, C, None, C, 256, 0, 256, 128, 0, None) == 0   # M == 0
     assert g(A, 120, C, 0, B, 128, C, None, C, 256, 4, 256, 128, 0, None) == 2   # lda < K
     assert g(A, 128, None, 0, B, 128, C, None, C, 256, 4, 256, 128, 0, None) == 1
@@ -157,9 +180,15 @@ def test_device_check_without_gpu(lib):
     g = lib.fp8q_add_rmsnorm_quant
     E = ctypes.c_void_p(0x500000)
     for z in (A, B, ctypes.c_void_p(0x100000 + 128 * 2 * 4)):
-        assert g(A, 128, B, 128, z, 128, C, 1e-6, 4, 128, 0, None, E, 128, C, None, 0, None) == 5
-    assert g(A, 128, B, 128, A, 128, C, 1e-6, 4, 128, 3, ctypes.c_void_p(0x600000), E, 128, None, None, 0,
+        assert g(A, 128, B, 128, z, 128, C, 1e-6, 4, 128, 0, 0, None, E, 128, C, None, 0, None) == 5
+    assert g(A, 128, B, 128, A, 128, C, 1e-6, 4, 128, 9, 3, ctypes.c_void_p(0x600000), E, 128, None, None, 0,
              None) == 5
+    assert g(A, 128, None, 0, None, 0, C, 1e-6, 4, 128, 2, 1, None, E, 128, C, None, 0, None) == 5  # no add, pow2
+    # power-of-two formats are accepted by the quantizers, the requant and the GEMM
+    assert lib.fp8q_quant_act_group(A, 4, 128, 128, 128, 2, 0, None, B, 128, C, None) == 5
+    assert lib.fp8q_quant_weight_block(A, 256, 256, 256, 128, 128, 2, B, 256, C, None) == 5
+    assert lib.fp8q_requant_weight_pow2(A, 256, C, 256, 256, A, 256, C, None) == 5          # in place
+    assert lib.fp8q_gemm_blockscale(A, 128, C, 0, B, 128, C, None, C, 256, 4, 256, 128, 2, None) == 5
 
 
 @pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")

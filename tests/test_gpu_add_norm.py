@@ -55,7 +55,7 @@ def _check(M, K, mode, inplace, with_y, seed):
     sx = np.float32(0.0137)
     sd = torch.tensor([sx], dtype=torch.float32, device="cuda") if static else None
     s = None if static else torch.empty((G, M) if layout else (M, G), dtype=torch.float32, device="cuda")
-    m.fp8q_add_rmsnorm_quant(xd, hd, zd, g.cuda(), EPS, layout, sd, q, s, y)
+    m.fp8q_add_rmsnorm_quant(xd, hd, zd, g.cuda(), EPS, m.SCALE_F32, layout, sd, q, s, y)
     torch.cuda.synchronize()
     assert canary_intact(zb, K, CANARY_BF16) and canary_intact(qb, K, CANARY_U8)
     assert canary_intact(hb, K, CANARY_BF16)
@@ -127,7 +127,7 @@ def test_add_rmsnorm_quant_in_place_on_h():
     xd, hd = x.cuda(), h.cuda()
     q = torch.empty(M, K, dtype=torch.uint8, device="cuda")
     s = torch.empty(M, K // 128, dtype=torch.float32, device="cuda")
-    m.fp8q_add_rmsnorm_quant(xd, hd, hd, g.cuda(), EPS, 0, None, q, s)
+    m.fp8q_add_rmsnorm_quant(xd, hd, hd, g.cuda(), EPS, m.SCALE_F32, 0, None, q, s)
     torch.cuda.synchronize()
     ref = oq.add_rmsnorm_quant(bf16_host(x), bf16_host(h), bf16_host(g), EPS)
     np.testing.assert_array_equal(bf16_bits(hd), ref["z"])

@@ -178,3 +178,22 @@ def test_pow2_accuracy_cost_vs_fp32_scales():
     e2 = np.linalg.norm(y2 - exact) / np.linalg.norm(exact)
     print(f"relative output error: fp32 scales {e32:.4%}, power-of-two scales {e2:.4%}")
     assert e32 < e2 < 2.0 * e32
+
+
+def test_fused_norm_pow2_exit_is_norm_then_pow2_quant():
+    # the pow2 exit of the fused front end quantizes the bf16 y (pinned
+    # RMSNorm) with the power-of-two group quantizer pinned above
+    rng = np.random.default_rng(9)
+    x = _bf16(rng.standard_normal((8, 640)))
+    h = _bf16(rng.standard_normal((8, 640)) / 4)
+    g = _bf16(rng.uniform(0.5, 1.5, 640))
+    out = quant.add_rmsnorm_quant(x, h, g, 1e-6, pow2=True)
+    assert _is_pow2(out["s"])
+    yv = bf16.to_f64(out["y"])
+    for gi in range(5):
+        cols = slice(128 * gi, 128 * gi + 128)
+        amax = np.max(np.abs(yv[:, cols]), axis=1)
+        assert np.all(amax <= 448.0 * out["s"][:, gi]) and np.all(amax > 224.0 * out["s"][:, gi])
+    plain = quant.add_rmsnorm_quant(x, h, g, 1e-6)
+    np.testing.assert_array_equal(out["y"], plain["y"])
+    np.testing.assert_array_equal(out["z"], plain["z"])
