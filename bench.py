@@ -5,7 +5,8 @@ A step is one forward pass of the linear layer over one batch of synthetic
 activations already resident in HBM: the activation quantizer (fused with
 RMSNorm for the prefill-with-norm workload, and with the residual add in front
 of it for the add-norm workload, which updates the stream in place) followed
-by the scaled GEMM.  The
+by the scaled GEMM (`*_pow2` workloads: the same with power-of-two scales
+-- block FP8 as an MXFP8 view -- applied inside the MFMA).  The
 weight is quantized once before timing (it is offline preparation).  Inputs
 and outputs rotate over several buffer sets whose total exceeds the 256 MB
 Infinity Cache, so HBM rates are not inflated by cache hits.
@@ -45,7 +46,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="prefill_norm",
-                    choices=["tiny", "decode", "prefill_norm", "prefill_addnorm", "large", "mx", "pertensor"])
+                    choices=["tiny", "decode", "prefill_norm", "prefill_addnorm", "large", "mx", "pertensor",
+                             "prefill_norm_pow2", "large_pow2"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample (0 = skip)")
     return ap.parse_args()
@@ -93,7 +95,8 @@ def main() -> int:
     fq.load_library()
 
     name = args.workload
-    wl = workloads.WORKLOADS["mx" if name == "pertensor" else name]
+    pow2 = name.endswith("_pow2")
+    wl = workloads.WORKLOADS["mx" if name == "pertensor" else name[:-5] if pow2 else name]
     M, N, K = wl.M, wl.N, wl.K
     d = wl.make("cpu")
     x_cpu, w_cpu = d["x"], d["w"]
@@ -105,6 +108,9 @@ def main() -> int:
         qw, sw = fq.quant_weight_mx(wd)
     elif name == "pertensor":
         qw, sw = fq.quant_weight_tensor(wd)
+    elif pow2:
+        # a block-FP8 checkpoint re-expressed with power-of-two block scales
+        qw, sw = fq.requant_weight_pow2(*fq.quant_weight_block(wd))
     else:
         qw, sw = fq.quant_weight_block(wd)
     gamma = d["gamma"].cuda() if wl.norm else None
@@ -138,8 +144,14 @@ def main() -> int:
     # scales for consecutive rows are contiguous, one cache line per 32 rows
     # for the GEMM (the row-major form costs a line per row)
     def quant(s):
-        if wl.residual:
-            fq.fp8q_add_rmsnorm_quant(s["x"], s["h"], s["x"], gamma, d["eps"], fq.COL_MAJOR, None, s["q"], s["s"])
+        if pow2 and wl.norm:
+            fq.fp8q_add_rmsnorm_quant(s["x"], None, None, gamma, d["eps"], fq.SCALE_F32_POW2, fq.COL_MAJOR, None,
+                                      s["q"], s["s"])
+        elif pow2:
+            fq.fp8q_quant_act_group(s["x"], 128, fq.SCALE_F32_POW2, fq.COL_MAJOR, None, s["q"], s["s"])
+        elif wl.residual:
+            fq.fp8q_add_rmsnorm_quant(s["x"], s["h"], s["x"], gamma, d["eps"], fq.SCALE_F32, fq.COL_MAJOR, None,
+                                      s["q"], s["s"])
         elif wl.norm:
             fq.fp8q_rmsnorm_quant(s["x"], gamma, d["eps"], fq.COL_MAJOR, s["q"], s["s"])
         elif name == "mx":
@@ -155,7 +167,8 @@ def main() -> int:
         elif name == "pertensor":
             fq.fp8q_gemm_blockscale(s["q"], s["s"], fq.ROW_MAJOR, qw, sw, None, s["y"], fq.GRAN_PER_TENSOR)
         else:
-            fq.fp8q_gemm_blockscale(s["q"], s["s"], fq.COL_MAJOR, qw, sw, None, s["y"], fq.GRAN_BLOCK128)
+            fq.fp8q_gemm_blockscale(s["q"], s["s"], fq.COL_MAJOR, qw, sw, None, s["y"],
+                                    fq.GRAN_BLOCK128_POW2 if pow2 else fq.GRAN_BLOCK128)
 
     for i in range(args.warmup):
         s = sets[i % nsets]
@@ -226,14 +239,16 @@ def main() -> int:
                 "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "traffic": traffic}
 
     kernel_q = {"prefill_norm": "rmsnorm_quant", "prefill_addnorm": "add_rmsnorm_quant", "mx": "quant_group32mx",
-                "pertensor": "quant_static"}.get(name, "quant_group128")
+                "pertensor": "quant_static", "prefill_norm_pow2": "rmsnorm_quant (pow2 scales)",
+                "large_pow2": "quant_group128 (pow2 scales)"}.get(name, "quant_group128")
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8_e4m3 (fp32 accumulate)", "data": "synthetic",
         "config": {"workload": name, "M": M, "N": N, "K": K, "norm": wl.norm, "residual_add": wl.residual,
-                   "scales": {"mx": "1x32 ue8m0", "pertensor": "per-tensor fp32"}.get(name, "group128 + 128x128 fp32"),
+                   "scales": {"mx": "1x32 ue8m0", "pertensor": "per-tensor fp32"}.get(
+                       name, "group128 + 128x128 power-of-two fp32 (in-MFMA)" if pow2 else "group128 + 128x128 fp32"),
                    "rotating_buffer_sets": nsets},
         "roofline": roof,
         "gemm": {"us": round(gemm_ms * 1e3, 2), "TFLOP/s": round(gemm_tflops, 1),
@@ -245,12 +260,12 @@ def main() -> int:
         "cpu_baseline": None,
     }
     if args.cpu_seconds > 0:
-        out["cpu_baseline"] = cpu_baseline(name, wl, d, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(name, wl, d, args.cpu_seconds, pow2)
     print(json.dumps(out), flush=True)
     return 0
 
 
-def cpu_baseline(name, wl, d, target_s):
+def cpu_baseline(name, wl, d, target_s, pow2=False):
     """Time the CPU oracle (as it stands) on a bounded row sample."""
     import numpy as np
     try:
@@ -269,6 +284,8 @@ def cpu_baseline(name, wl, d, target_s):
     elif name == "pertensor":
         qw, sw = oq.quant_tensor(wh)
         sx = np.float32(np.float32(np.abs(xh).max()) / np.float32(448.0))
+    elif pow2:
+        qw, sw = oq.requant_weight_pow2(*oq.quant_weight_block(wh))
     else:
         qw, sw = oq.quant_weight_block(wh)
     gh = d["gamma"].float().numpy() if wl.norm else None
@@ -276,7 +293,13 @@ def cpu_baseline(name, wl, d, target_s):
 
     def run(rows):
         xs = xh[:rows]
-        if wl.residual:
+        if pow2 and wl.norm:
+            r = oq.add_rmsnorm_quant(xs, np.zeros_like(xs), gh, d["eps"], pow2=True)
+            og.gemm_blockscale(r["q"], r["s"], qw, sw)
+        elif pow2:
+            qa, sa = oq.quant_group_pow2(xs)
+            og.gemm_blockscale(qa, sa, qw, sw)
+        elif wl.residual:
             r = oq.add_rmsnorm_quant(xs, hh[:rows], gh, d["eps"])
             og.gemm_blockscale(r["q"], r["s"], qw, sw)
         elif wl.norm:
