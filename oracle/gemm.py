@@ -16,6 +16,13 @@ Definitions followed
   pages use it.
 * Per-tensor: Y = (QX QW^T) * s_x * s_w with scalar scales
   ([SGL19] "一条 GEMM 的三种缩放组合").
+* Grouped (MoE experts): the activation rows are sorted by expert and
+  contiguous; rows offsets[e] .. offsets[e+1] are multiplied by expert e's
+  weight and scales ([SGL19] "MoE:专家权重多一个维度": w13 [E, 2 I_p, H],
+  w2 [E, H, I_p], one scale grid per expert; grouped GEMMs take the
+  expert-sorted contiguous layout).  With stacked shards (w13's gate and
+  up), the weight scale row of output channel j is
+  (j // shard) * ceil(shard/128) + (j % shard) // 128.
 * MXFP8: the same block identity with 1x32 blocks whose scales are powers of
   two 2^(byte-127) ([SGLFP8] "4. 블록 양자화 스케일 관리"; [SGL19]
   "Triton 分块内核在做什么": UE8M0 scales turn the multiply into an exponent
@@ -45,9 +52,19 @@ def _finish(acc, bias):
     return bf16.round_from_f64(acc), acc
 
 
-def gemm_blockscale(qa, sa, qw, sw, bias=None, block: int = 128, rows=None):
+def weight_scale_rows(N: int, shard: int = 0, block: int = 128) -> np.ndarray:
+    """Scale-row index of each output channel j: j // 128, or with stacked
+    shards (j // shard) * ceil(shard/128) + (j % shard) // 128."""
+    j = np.arange(N)
+    if not shard:
+        return j // block
+    return (j // shard) * (-(-shard // block)) + (j % shard) // block
+
+
+def gemm_blockscale(qa, sa, qw, sw, bias=None, block: int = 128, rows=None, shard: int = 0):
     """Block-scaled GEMM.  qa uint8 [M,K], sa fp32 [M, ceil(K/128)],
-    qw uint8 [N,K], sw fp32 [ceil(N/128), ceil(K/128)], bias fp64-able [N].
+    qw uint8 [N,K], sw fp32 [ceil(N/128), ceil(K/128)] (stacked shards:
+    [(N/shard) * ceil(shard/128), ceil(K/128)]), bias fp64-able [N].
 
     ``rows`` optionally restricts the computation to those output rows.
     Returns (Y bf16 bits [m, N], Y before rounding fp64 [m, N]).
@@ -61,13 +78,41 @@ def gemm_blockscale(qa, sa, qw, sw, bias=None, block: int = 128, rows=None):
     M, K = A.shape
     N = W.shape[0]
     sw = np.asarray(sw, dtype=np.float64)
-    sw_cols = sw[np.arange(N) // block]          # [N, KB]: scale of column j's block
+    sw_cols = sw[weight_scale_rows(N, shard, block)]   # [N, KB]: scale of column j's block
     acc = np.zeros((M, N), dtype=np.float64)
     for b in range(_kb(K, block)):
         ks = slice(b * block, min(K, (b + 1) * block))
         P = A[:, ks] @ W[:, ks].T                # exact block sum
         acc += P * sa[:, b].astype(np.float64)[:, None] * sw_cols[:, b][None, :]
     return _finish(acc, bias)
+
+
+def gemm_grouped_blockscale(qa, sa, qw, sw, offsets, shard: int = 0, rows=None):
+    """Grouped block-scaled GEMM over expert-sorted rows.
+
+    qa uint8 [M, K], sa fp32 [M, ceil(K/128)]; qw uint8 [E, N, K] (or a
+    callable e -> qw[e]), sw fp32 [E, NBs, ceil(K/128)] (or a callable);
+    offsets int [E+1], non-decreasing, offsets[0] = 0, offsets[E] = M.
+    ``rows`` restricts the computation to those output rows.
+    Returns Y bf16 bits [m, N].
+    """
+    offsets = np.asarray(offsets, dtype=np.int64)
+    E = len(offsets) - 1
+    M = offsets[-1]
+    rows = np.arange(M) if rows is None else np.asarray(rows, dtype=np.int64)
+    get_w = qw if callable(qw) else (lambda e: qw[e])
+    get_s = sw if callable(sw) else (lambda e: sw[e])
+    expert = np.searchsorted(offsets, rows, side="right") - 1     # expert of each row
+    out = None
+    for e in np.unique(expert):
+        sel = np.flatnonzero(expert == e)
+        y, _ = gemm_blockscale(qa, sa, get_w(e), get_s(e), rows=rows[sel], shard=shard)
+        if out is None:
+            out = np.empty((len(rows), y.shape[1]), dtype=np.uint16)
+        out[sel] = y
+    if out is None:
+        out = np.empty((0, np.asarray(get_w(0)).shape[0]), dtype=np.uint16)
+    return out
 
 
 def gemm_pertensor(qa, sa, qw, sw, bias=None, rows=None):

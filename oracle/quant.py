@@ -56,6 +56,10 @@ Readings where the pages leave a step open
       two: e' = the smallest integer with s <= 2^e' (the round-up rule applied
       to s, which stands for amax/448), q' = E4M3(decode(q) * s * 2^-e'); as
       s * 2^-e' <= 1, no code grows past 448.
+(xi)  Stacked shards (MoE w13 = [gate; up]): each shard of the output rows
+      gets its own ceil grid of 128x128 blocks and the scale rows are
+      concatenated, 2 * ceil(I_p/128) rows rather than ceil(2 I_p/128)
+      ([SGL19] "MoE:专家权重多一个维度").
 (viii) Residual add: the updated stream is z = bf16(x + h), the correctly
       rounded sum (one rounding); RMSNorm and the quantizer then read that
       bf16 z, as they would read it back from memory in the unfused sequence.
@@ -319,3 +323,14 @@ def requant_weight_pow2(q, s, block_n: int = 128, block_k: int = 128):
     mult = np.repeat(np.repeat(m, block_n, axis=0), block_k, axis=1)[:N, :K]
     v = e4m3.decode(q) * mult                       # exact in fp64 (4 x 24 bits)
     return e4m3.encode(np.clip(v, -448.0, 448.0)), s2
+
+
+def quant_weight_block_sharded(w, shard: int):
+    """Block quantization of stacked shards of `shard` output rows each
+    (reading xi).  Returns (q [N, K], s [(N/shard) * ceil(shard/128), ceil(K/128)])."""
+    w = np.asarray(w, dtype=np.float32)
+    N = w.shape[0]
+    if shard <= 0 or N % shard:
+        raise ValueError("N must be a multiple of the shard size")
+    parts = [quant_weight_block(w[i:i + shard]) for i in range(0, N, shard)]
+    return np.concatenate([q for q, _ in parts]), np.concatenate([s for _, s in parts])

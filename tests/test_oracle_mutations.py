@@ -252,3 +252,30 @@ def test_group_pow2_mistake_is_caught(monkeypatch):
     monkeypatch.setattr(quant, "quant_group_pow2", _group_pow2_nearest_exponent)
     with pytest.raises(AssertionError):
         pins.test_group_pow2_scales_bracket_amax()
+
+
+# ------------------------------------------------------------------ MoE
+
+def _sharded_as_one_grid(w, shard):
+    return quant.quant_weight_block(w)
+
+
+def test_shard_rule_mistake_is_caught(monkeypatch):
+    import tests.test_oracle_moe as pins
+    monkeypatch.setattr(quant, "quant_weight_block_sharded", _sharded_as_one_grid)
+    with pytest.raises(AssertionError):
+        pins.test_shard_rule_when_intermediate_is_not_a_multiple_of_128()
+
+
+def test_grouped_offset_mistake_is_caught(monkeypatch):
+    import tests.test_oracle_moe as pins
+    real = gemm.gemm_grouped_blockscale
+
+    def shifted(qa, sa, qw, sw, offsets, shard=0, rows=None):
+        off = np.asarray(offsets).copy()
+        off[1:-1] += 1                                        # rows slip into the next expert
+        return real(qa, sa, qw, sw, off, shard=shard, rows=rows)
+
+    monkeypatch.setattr(gemm, "gemm_grouped_blockscale", shifted)
+    with pytest.raises(AssertionError):
+        pins.test_grouped_gemm_against_per_expert_dequantized_products(0)
