@@ -20,10 +20,10 @@ import torch
 __all__ = [
     "load_library", "FP8QError", "abi_version",
     "fp8q_quant_act_group", "fp8q_rmsnorm_quant", "fp8q_add_rmsnorm_quant", "fp8q_quant_weight_block",
-    "fp8q_requant_weight_pow2", "fp8q_gemm_blockscale", "fp8q_gemm_mxfp8",
+    "fp8q_requant_weight_pow2", "fp8q_gemm_blockscale", "fp8q_gemm_grouped_blockscale", "fp8q_gemm_mxfp8",
     "quant_act_group", "quant_act_group_pow2", "rmsnorm_quant_pow2", "quant_act_static", "quant_act_mx", "rmsnorm_quant", "add_rmsnorm_quant",
     "quant_weight_block", "quant_weight_block_pow2", "requant_weight_pow2", "quant_weight_mx", "quant_weight_tensor",
-    "gemm_blockscale", "gemm_blockscale_pow2", "gemm_pertensor", "gemm_mxfp8",
+    "gemm_blockscale", "gemm_blockscale_pow2", "gemm_grouped_blockscale", "gemm_pertensor", "gemm_mxfp8",
     "SCALE_F32", "SCALE_UE8M0", "SCALE_F32_POW2", "ROW_MAJOR", "COL_MAJOR", "GRAN_BLOCK128", "GRAN_PER_TENSOR",
     "GRAN_BLOCK128_POW2",
 ]
@@ -49,6 +49,8 @@ SIGNATURES = {
     "fp8q_requant_weight_pow2": (ctypes.c_int, [_P, _I64, _P, _I64, _I64, _P, _I64, _P, _P]),
     "fp8q_quant_weight_block": (ctypes.c_int, [_P, _I64, _I64, _I64, _I32, _I32, _I32, _P, _I64, _P, _P]),
     "fp8q_gemm_blockscale": (ctypes.c_int, [_P, _I64, _P, _I32, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _P]),
+    "fp8q_gemm_grouped_blockscale": (ctypes.c_int, [_P, _I64, _P, _I32, _P, _I32, _P, _I64, _I64, _P, _I64, _P, _I64,
+                                                    _I64, _I64, _I64, _I32, _P]),
     "fp8q_gemm_mxfp8": (ctypes.c_int, [_P, _I64, _P, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _I64, _P]),
 }
 
@@ -196,6 +198,30 @@ def fp8q_gemm_blockscale(a, a_scales, a_layout, w, w_scale_inv, bias, y, gran, s
     _check(load_library().fp8q_gemm_blockscale(_ptr(a), lda, _ptr(a_scales), a_layout, _ptr(w), ldw,
                                                _ptr(w_scale_inv), _ptr(bias), _ptr(y), ldy, M, N, K,
                                                gran, _stream(stream)), "fp8q_gemm_blockscale")
+
+
+def fp8q_gemm_grouped_blockscale(a, a_scales, a_layout, expert_offsets, w, w_scale_inv, y, shard=0,
+                                 gran=GRAN_BLOCK128, stream=None):
+    """a [M, K] expert-sorted rows; expert_offsets int32 [E+1] (device);
+    w [E, N, K] (uint8 / float8 view, rows 16-byte aligned); w_scale_inv fp32
+    [E, NBs, ceil(K/128)]; y bf16 [M, N]."""
+    a, w = _u8(a), _u8(w)
+    M, K, lda = _rows(a, torch.uint8, "a")
+    if w.dim() != 3 or w.stride(2) != 1 or w.size(2) != K:
+        raise ValueError("w must be [E, N, K] with unit column stride")
+    E, N = w.size(0), w.size(1)
+    ldw, w_stride = w.stride(1), w.stride(0)
+    My, Ny, ldy = _rows(y, torch.bfloat16, "y")
+    if (My, Ny) != (M, N):
+        raise ValueError("y must be [M, N]")
+    if expert_offsets.dtype != torch.int32 or expert_offsets.numel() != E + 1 or not expert_offsets.is_cuda:
+        raise ValueError("expert_offsets must be a device int32 tensor of E + 1 entries")
+    if w_scale_inv.dtype != torch.float32 or not w_scale_inv.is_contiguous() or w_scale_inv.size(0) != E:
+        raise ValueError("w_scale_inv must be a contiguous float32 [E, NBs, ceil(K/128)] tensor")
+    _check(load_library().fp8q_gemm_grouped_blockscale(_ptr(a), lda, _ptr(a_scales), a_layout, _ptr(expert_offsets),
+                                                       E, _ptr(w), ldw, w_stride, _ptr(w_scale_inv), shard, _ptr(y),
+                                                       ldy, M, N, K, gran, _stream(stream)),
+           "fp8q_gemm_grouped_blockscale")
 
 
 def fp8q_gemm_mxfp8(a, a_scales, w, w_scales, bias, y, stream=None):
@@ -354,6 +380,14 @@ def gemm_blockscale_pow2(a, a_scales, w, w_scale_inv, bias=None, a_layout: int =
     """Block GEMM on power-of-two scales, applied by the scaled MFMA."""
     y = _y(a.shape[0], w.shape[0], a.device)
     fp8q_gemm_blockscale(a, a_scales, a_layout, w, w_scale_inv, bias, y, GRAN_BLOCK128_POW2, stream)
+    return y
+
+
+def gemm_grouped_blockscale(a, a_scales, expert_offsets, w, w_scale_inv, shard=0, a_layout: int = ROW_MAJOR,
+                            gran=GRAN_BLOCK128, stream=None):
+    """MoE expert GEMMs over expert-sorted rows; returns y bf16 [M, N]."""
+    y = _y(a.shape[0], w.shape[1], a.device)
+    fp8q_gemm_grouped_blockscale(a, a_scales, a_layout, expert_offsets, w, w_scale_inv, y, shard, gran, stream)
     return y
 
 

@@ -266,6 +266,36 @@ fp8q_status_t fp8q_gemm_blockscale(const uint8_t* a, int64_t lda, const float* a
                                                      gran, static_cast<hipStream_t>(stream)));
 }
 
+fp8q_status_t fp8q_gemm_grouped_blockscale(const uint8_t* a, int64_t lda, const float* a_scales,
+                                           int32_t a_layout, const int32_t* expert_offsets, int32_t E,
+                                           const uint8_t* w, int64_t ldw, int64_t w_expert_stride,
+                                           const float* w_scale_inv, int64_t shard, uint16_t* y,
+                                           int64_t ldy, int64_t M, int64_t N, int64_t K, int32_t gran,
+                                           void* stream) {
+  if (M < 0 || N < 0 || K <= 0 || M > kMaxRows || N > kMaxRows || K > kMaxK) return FP8Q_ERR_SHAPE;
+  if (E < 1 || E > 1024 || shard < 0) return FP8Q_ERR_SHAPE;
+  if (gran != FP8Q_GRAN_BLOCK128 && gran != FP8Q_GRAN_BLOCK128_POW2) return FP8Q_ERR_UNSUPPORTED;
+  if (a_layout != FP8Q_SCALES_ROW_MAJOR && a_layout != FP8Q_SCALES_COL_MAJOR) return FP8Q_ERR_UNSUPPORTED;
+  if (K % 128 != 0) return FP8Q_ERR_UNSUPPORTED;
+  if (shard > 0 && (N % shard != 0 || shard % 64 != 0)) return FP8Q_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return FP8Q_OK;
+  FP8Q_TRY(check_matrix(a, K, lda, 1));
+  FP8Q_TRY(check_matrix(w, K, ldw, 1));
+  FP8Q_TRY(check_matrix(y, N, ldy, 2));
+  if (a_scales == nullptr || w_scale_inv == nullptr || expert_offsets == nullptr) return FP8Q_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(a_scales) & 3u) || (reinterpret_cast<uintptr_t>(w_scale_inv) & 3u) ||
+      (reinterpret_cast<uintptr_t>(expert_offsets) & 3u))
+    return FP8Q_ERR_MISALIGNED;
+  if (w_expert_stride < N * ldw) return FP8Q_ERR_SHAPE;
+  if (w_expert_stride % 16 != 0) return FP8Q_ERR_MISALIGNED;
+  FP8Q_TRY(check_device());
+  const hipError_t e = fp8q::launch_gemm_grouped_blockscale(
+      a, lda, a_scales, a_layout == FP8Q_SCALES_COL_MAJOR, expert_offsets, E, w, ldw, w_expert_stride,
+      w_scale_inv, shard, y, ldy, M, N, K, gran == FP8Q_GRAN_BLOCK128_POW2, static_cast<hipStream_t>(stream));
+  if (e == hipErrorInvalidValue) return FP8Q_ERR_SHAPE;     // beyond the kernel's offset limits
+  return launch_status(e);
+}
+
 fp8q_status_t fp8q_gemm_mxfp8(const uint8_t* a, int64_t lda, const uint8_t* a_scales,
                               const uint8_t* w, int64_t ldw, const uint8_t* w_scales,
                               const uint16_t* bias, uint16_t* y, int64_t ldy, int64_t M,

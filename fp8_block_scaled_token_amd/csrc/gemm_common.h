@@ -33,9 +33,18 @@ struct GemmArgs {
   int M, N, K;
   int KB;               // number of 128-wide K blocks
   int KB32;             // number of 32-wide K blocks (MX scale columns)
-  int NB;               // number of 128-row weight blocks
+  int NB;               // number of weight scale rows
   int tiles_m, tiles_n;
+  int m_end;            // output rows at or past m_end are not stored (M, or an expert's end)
+  int shard;            // stacked weight shards of `shard` rows each (0: one shard), see below
+  int shard_blocks;     // ceil(shard / 128)
 };
+
+// Weight scale row of output channel j: j / 128, or with stacked shards
+// (j / shard) * ceil(shard / 128) + (j % shard) / 128.
+__host__ __device__ __forceinline__ int weight_scale_row(const GemmArgs& p, int j) {
+  return p.shard ? (j / p.shard) * p.shard_blocks + (j % p.shard) / 128 : j / 128;
+}
 
 union Frag {
   v8i v;
@@ -111,6 +120,12 @@ __device__ __forceinline__ void store_tile_bf16(const GemmArgs& p, const v4f& ac
 // Fast prefill path (gemm_fast.hip): shapes it accepts, and its launcher.
 bool gemm_fast_eligible(const GemmArgs& p, int mode);
 hipError_t launch_gemm_fast(GemmArgs p, int mode, hipStream_t stream);
+
+// Grouped (MoE) path on the fast kernel's tiles: expert-sorted rows,
+// offsets [E + 1] on the device, expert weights w_stride bytes apart.
+bool gemm_grouped_eligible(const GemmArgs& p, int E, int64_t w_stride);
+hipError_t launch_gemm_grouped(GemmArgs p, const int32_t* offsets, int E, int64_t w_stride, int mode,
+                               hipStream_t stream);
 
 // Decode path (gemm_decode.hip): shapes it accepts, and its launcher.
 bool gemm_decode_eligible(const GemmArgs& p);

@@ -128,8 +128,10 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
   // Scale words: lane l of wave w fetches word q = 64w + l of the stage's
   // scale area.  Activation words are ordered [wm][row % 16][row tile] so a
   // lane reads the TM scales of its rows as consecutive words; MX weight
-  // words likewise [wn][row % 16][row tile].  Block mode: weight word b is
-  // the scale of 128-column block n0/128 + b.
+  // words likewise [wn][row % 16][row tile].  Block mode: weight word b
+  // (b < WN) is the scale of the 128-row weight block that holds wave
+  // column b's channels n0 + b*WTN .. +WTN (one block: WTN divides 128 and
+  // the shard size).
   // L2 prefetch rows: tiles running together on one XCD share operand rows:
   // the NTN tiles of a tile row read the same A rows, the 8 tiles of a tile
   // column (group_walk's group height) the same W rows.  Every workgroup
@@ -166,8 +168,8 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
       } else {
         const int qw = q - BM;
         if (FP32S) {
-          const int blk = tn0 / 128 + qw;
-          o.s = (qw < (BN + 127) / 128 && blk < p.NB) ? (uint32_t)(blk * p.KB * 4) : OOB;
+          const int col = tn0 + qw * WTN;
+          o.s = (qw < WN && col < p.N) ? (uint32_t)(weight_scale_row(p, col) * p.KB * 4) : OOB;
         } else {
           const int g = qw / WTN, rem = qw % WTN;
           const int row = tn0 + g * WTN + 16 * (rem % TN) + rem / TN;
@@ -317,9 +319,9 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
       read_words(reinterpret_cast<const uint32_t*>(a + SA_OFF) + wm * WTM + l16 * TM, sav,
                  std::integral_constant<int, TM>{});
     if constexpr (MODE == MODE_BLOCK)
-      swv = __uint_as_float(reinterpret_cast<const uint32_t*>(a + SW_OFF)[(wn * WTN) / 128]);
+      swv = __uint_as_float(reinterpret_cast<const uint32_t*>(a + SW_OFF)[wn]);
     if constexpr (MODE == MODE_BMX)
-      swe = (int)((reinterpret_cast<const uint32_t*>(a + SW_OFF)[(wn * WTN) / 128] >> 23) & 0xFFu);
+      swe = (int)((reinterpret_cast<const uint32_t*>(a + SW_OFF)[wn] >> 23) & 0xFFu);
     if constexpr (MODE == MODE_MX)
       read_words(reinterpret_cast<const uint32_t*>(a + SW_OFF) + wn * WTN + l16 * TN, swb,
                  std::integral_constant<int, TN>{});
@@ -490,7 +492,7 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
       e[3][h] = t23[1];
     }
     const int row = m0 + wm * WTM + 16 * i + l16;
-    if (row >= p.M) continue;
+    if (row >= p.m_end) continue;
     uint16_t* yr = p.y + (int64_t)row * p.ldy;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -551,6 +553,97 @@ __global__ __launch_bounds__(T::NW * 64) void gemm_fast_kernel(GemmArgs p, int f
   }
   // the last touches and past-the-end loads still write the LDS sink: let
   // them land before the workgroup ends
+  wait_vmcnt<0>();
+}
+
+// Grouped GEMM over expert-sorted rows (MoE experts): rows offsets[e] ..
+// offsets[e+1] of A multiply expert e's weight w + e * w_stride with its
+// scales sw + e * sw_stride.  Items are the tiles of every expert, expert
+// after expert (an expert's tiles in group_walk order), counted on the device
+// from the offsets: each workgroup sums the per-expert tile counts in LDS
+// (a scan) and finds an item's expert by binary search.  Offsets are clamped
+// to [0, M] and made non-decreasing, so any offsets keep every access inside
+// the operands (outputs are then unspecified).  A tile's rows past its
+// expert's end are computed from the next expert's rows and not stored.  The
+// next tile's first K block is issued early only when it belongs to the same
+// expert (its weight descriptor is the same).
+struct GroupArgs {
+  const int32_t* offsets;   // [E + 1]
+  int E;
+  int64_t w_stride;         // bytes between experts' weights
+  int64_t sw_stride;        // scale words between experts' scale grids
+};
+
+constexpr int kMaxExperts = 1024;
+
+template <class T>
+__global__ __launch_bounds__(T::NW * 64) void gemm_grouped_kernel(GemmArgs p, GroupArgs g) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES];
+  __shared__ int tiles_before[kMaxExperts];    // inclusive scan of per-expert tile counts
+  constexpr int NT = T::NW * 64, PER = (kMaxExperts + NT - 1) / NT;
+  const int E = g.E;
+  // expert e's rows [row_begin(e), row_end(e)), clamped into [0, M]; e may
+  // differ between lanes (the counting loop below), so nothing here assumes
+  // a wave-uniform e
+  auto clampM = [&](int o) { return o < 0 ? 0 : (o > p.M ? p.M : o); };
+  auto row_begin = [&](int e) { return clampM(g.offsets[e]); };
+  auto row_end = [&](int e) {
+    const int b = clampM(g.offsets[e]), x = clampM(g.offsets[e + 1]);
+    return x < b ? b : x;
+  };
+  for (int t = threadIdx.x; t < E; t += NT)
+    tiles_before[t] = (row_end(t) - row_begin(t) + T::BM - 1) / T::BM * p.tiles_n;
+  __syncthreads();
+  for (int d = 1; d < E; d <<= 1) {
+    int v[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int t = threadIdx.x + i * NT;
+      v[i] = (t < E && t >= d) ? tiles_before[t - d] : 0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int t = threadIdx.x + i * NT;
+      if (t < E) tiles_before[t] += v[i];
+    }
+    __syncthreads();
+  }
+  const int items = __builtin_amdgcn_readfirstlane(tiles_before[E - 1]);
+  // item -> expert (first e with tiles_before[e] > x) and tile origin
+  auto decode = [&](int x, int& e, int& m0, int& n0, int& gm, int& gn) {
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (__builtin_amdgcn_readfirstlane(tiles_before[mid]) > x) hi = mid;
+      else lo = mid + 1;
+    }
+    e = lo;
+    const int li = x - (e ? __builtin_amdgcn_readfirstlane(tiles_before[e - 1]) : 0);
+    // x is wave-uniform, hence e: its rows are made uniform (SGPRs)
+    const int r0 = __builtin_amdgcn_readfirstlane(row_begin(e));
+    const int tiles_m = (__builtin_amdgcn_readfirstlane(row_end(e)) - r0 + T::BM - 1) / T::BM;
+    int tm, tn;
+    group_walk(li, tiles_m, p.tiles_n, tm, tn);
+    m0 = r0 + tm * T::BM;
+    n0 = tn * T::BN;
+    gm = tm % 8;
+    gn = tn % T::NTN;
+  };
+  bool preloaded = false;
+  for (int b = blockIdx.x; b < items; b += gridDim.x) {
+    int e, m0, n0, gm, gn, ne = -1, nm0 = 0, nn0 = 0, ngm = 0, ngn = 0;
+    decode(b, e, m0, n0, gm, gn);
+    const int nb = b + gridDim.x;
+    if (nb < items) decode(nb, ne, nm0, nn0, ngm, ngn);
+    const bool has_next = ne == e;
+    GemmArgs pe = p;
+    pe.w = p.w + e * g.w_stride;
+    pe.sw = static_cast<const float*>(p.sw) + e * g.sw_stride;
+    pe.m_end = __builtin_amdgcn_readfirstlane(row_end(e));
+    fast_tile<T, false>(pe, smem, m0, n0, gm, gn, preloaded, has_next, nm0, nn0, ngm, ngn);
+    preloaded = has_next;
+  }
   wait_vmcnt<0>();
 }
 
@@ -642,6 +735,40 @@ bool gemm_fast_eligible(const GemmArgs& p, int /*mode*/) {
   return p.M > 64 && p.K % 128 == 0 && a_bytes < lim && w_bytes < lim &&
          (int64_t)(p.M + bm) * p.KB * 4 < lim && (int64_t)(p.M + bm) * p.KB32 < lim &&
          (int64_t)(p.N + bn) * p.KB32 < lim && (int64_t)(p.NB + 2) * p.KB * 4 < lim;
+}
+
+bool gemm_grouped_eligible(const GemmArgs& p, int E, int64_t w_stride) {
+  const int64_t lim = (int64_t(1) << 31) - 1;
+  return E >= 1 && E <= kMaxExperts && p.K % 128 == 0 && (int64_t)(p.M + 256) * p.lda < lim &&
+         (int64_t)p.N * p.ldw + 256 * p.ldw < lim && (int64_t)(p.M + 256) * p.KB * 4 < lim &&
+         (int64_t)(p.NB + 2) * p.KB * 4 < lim && (int64_t)(E - 1) * w_stride < (int64_t(1) << 62) &&
+         (p.shard == 0 || p.shard % 64 == 0);
+}
+
+hipError_t launch_gemm_grouped(GemmArgs p, const int32_t* offsets, int E, int64_t w_stride, int mode,
+                               hipStream_t stream) {
+  // tiles of 256 rows when experts average at least 256 rows, else 128
+  const int cfg = env_int("FP8Q_GEMM_CFG", p.M >= 256 * E ? 0 : 1) == 0 ? 0 : 1;
+  const int bm = cfg == 0 ? 256 : 128;
+  p.tiles_n = (p.N + bm - 1) / bm;
+  p.tiles_m = 0;
+  const GroupArgs g{offsets, E, w_stride, (int64_t)p.NB * p.KB};
+  // persistent: one workgroup per slot; the item count is known on the device only
+  const int grid = (cfg == 0 ? 1 : 2) * cu_count();
+#define FP8Q_GROUPED(MODEV)                                                                           \
+  do {                                                                                                \
+    if (cfg == 0) {                                                                                   \
+      using T = FastTile<MODEV, 256, 256, 2, 4, 4>;                                                   \
+      hipLaunchKernelGGL(gemm_grouped_kernel<T>, dim3(grid), dim3(T::NW * 64), 0, stream, p, g);      \
+    } else {                                                                                          \
+      using T = FastTile<MODEV, 128, 128, 2, 2, 8>;                                                   \
+      hipLaunchKernelGGL(gemm_grouped_kernel<T>, dim3(grid), dim3(T::NW * 64), 0, stream, p, g);      \
+    }                                                                                                 \
+  } while (0)
+  if (mode == MODE_BMX) FP8Q_GROUPED(MODE_BMX);
+  else FP8Q_GROUPED(MODE_BLOCK);
+#undef FP8Q_GROUPED
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_fast(GemmArgs p, int mode, hipStream_t stream) {

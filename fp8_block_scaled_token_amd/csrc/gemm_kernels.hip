@@ -383,9 +383,28 @@ hipError_t launch_gemm_blockscale(const uint8_t* a, int64_t lda, const float* sa
   p.w = w; p.ldw = ldw; p.sw = sw; p.bias = bias; p.y = y; p.ldy = ldy;
   p.M = (int)M; p.N = (int)N; p.K = (int)K;
   p.KB = cdiv(K, 128); p.KB32 = cdiv(K, 32); p.NB = cdiv(N, 128);
+  p.m_end = p.M;
   if (gran == 1) return launch_mode<MODE_TENSOR>(p, stream);
   if (gran == 2 && p.M > 64 && gemm_fast_eligible(p, MODE_BMX)) return launch_gemm_fast(p, MODE_BMX, stream);
   return launch_mode<MODE_BLOCK>(p, stream);
+}
+
+hipError_t launch_gemm_grouped_blockscale(const uint8_t* a, int64_t lda, const float* sa, int sa_col_major,
+                                          const int32_t* offsets, int E, const uint8_t* w, int64_t ldw,
+                                          int64_t w_stride, const float* sw, int64_t shard, uint16_t* y,
+                                          int64_t ldy, int64_t M, int64_t N, int64_t K, int pow2,
+                                          hipStream_t stream) {
+  GemmArgs p{};
+  p.a = a; p.lda = lda; p.sa = sa; p.sa_col_major = sa_col_major;
+  p.w = w; p.ldw = ldw; p.sw = sw; p.bias = nullptr; p.y = y; p.ldy = ldy;
+  p.M = (int)M; p.N = (int)N; p.K = (int)K;
+  p.KB = cdiv(K, 128); p.KB32 = cdiv(K, 32);
+  p.shard = (int)shard;
+  p.shard_blocks = cdiv(shard, 128);
+  p.NB = shard ? (int)(N / shard) * p.shard_blocks : cdiv(N, 128);
+  p.m_end = p.M;
+  if (!gemm_grouped_eligible(p, E, w_stride)) return hipErrorInvalidValue;
+  return launch_gemm_grouped(p, offsets, E, w_stride, pow2 ? MODE_BMX : MODE_BLOCK, stream);
 }
 
 hipError_t launch_gemm_mxfp8(const uint8_t* a, int64_t lda, const uint8_t* sa, const uint8_t* w,
@@ -396,6 +415,7 @@ hipError_t launch_gemm_mxfp8(const uint8_t* a, int64_t lda, const uint8_t* sa, c
   p.w = w; p.ldw = ldw; p.sw = sw; p.bias = bias; p.y = y; p.ldy = ldy;
   p.M = (int)M; p.N = (int)N; p.K = (int)K;
   p.KB = cdiv(K, 128); p.KB32 = cdiv(K, 32); p.NB = cdiv(N, 128);
+  p.m_end = p.M;
   return launch_mode<MODE_MX>(p, stream);
 }
 

@@ -44,6 +44,13 @@ hipError_t launch_gemm_blockscale(const uint8_t* a, int64_t lda, const float* sa
                                   const uint8_t* w, int64_t ldw, const float* sw,
                                   const uint16_t* bias, uint16_t* y, int64_t ldy, int64_t M,
                                   int64_t N, int64_t K, int gran, hipStream_t stream);
+// Grouped (MoE) block GEMM over expert-sorted rows; hipErrorInvalidValue when
+// the sizes exceed the kernel's 32-bit offsets (nothing is launched then).
+hipError_t launch_gemm_grouped_blockscale(const uint8_t* a, int64_t lda, const float* sa, int sa_col_major,
+                                          const int32_t* offsets, int E, const uint8_t* w, int64_t ldw,
+                                          int64_t w_stride, const float* sw, int64_t shard, uint16_t* y,
+                                          int64_t ldy, int64_t M, int64_t N, int64_t K, int pow2,
+                                          hipStream_t stream);
 hipError_t launch_gemm_mxfp8(const uint8_t* a, int64_t lda, const uint8_t* sa, const uint8_t* w,
                              int64_t ldw, const uint8_t* sw, const uint16_t* bias, uint16_t* y,
                              int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t stream);

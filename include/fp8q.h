@@ -245,6 +245,44 @@ fp8q_status_t fp8q_gemm_blockscale(const uint8_t* a, int64_t lda, const float* a
                                    int32_t gran, void* stream);
 
 /*
+ * fp8q_gemm_grouped_blockscale -- MoE expert GEMMs over expert-sorted rows.
+ *
+ * [SGL19] "MoE:专家权重多一个维度": expert weights carry one more dimension
+ * (w13 [E, 2 I_p, H] with gate and up stacked, w2 [E, H, I_p]) and one scale
+ * grid per expert; a grouped GEMM takes the activations sorted by expert into
+ * one contiguous run per expert (the dispatch stage sorts them).  For each
+ * expert e, rows offsets[e] .. offsets[e+1] - 1 of A:
+ *   Y[i, j] = bf16( sum_b P_b[i,j] * s_a[i,b] * s_w[e][r(j), b] ),
+ * the FP8Q_GRAN_BLOCK128 formula with expert e's weight and scales, where the
+ * weight scale row r(j) = j / 128, or with stacked shards of `shard` rows
+ * (w13: shard = I_p) r(j) = (j / shard) * ceil(shard/128) + (j % shard) / 128:
+ * each shard has its own ceil grid, 2 * ceil(I_p/128) scale rows rather than
+ * ceil(2 I_p / 128) (same section).
+ *
+ *   a E4M3 [M, lda] (expert-sorted rows);  a_scales float, [M, ceil(K/128)]
+ *     (ROW_MAJOR) or [ceil(K/128), M] (COL_MAJOR).
+ *   expert_offsets  device int32 [E + 1]: 0 = offsets[0] <= ... <=
+ *     offsets[E] = M (rows of expert e are offsets[e] .. offsets[e+1] - 1;
+ *     empty experts allowed).  Offsets outside [0, M] or decreasing give
+ *     unspecified outputs but no access outside the operands.  1 <= E <= 1024.
+ *   w E4M3: expert e's [N, ldw] matrix starts w_expert_stride bytes after
+ *     expert e-1's (w_expert_stride >= N * ldw, a multiple of 16).
+ *   w_scale_inv float [E, NBs, ceil(K/128)], NBs = ceil(N/128), or
+ *     (N / shard) * ceil(shard/128) with shards; contiguous.
+ *   shard  0 (one shard) or a divisor of N that is a multiple of 64.
+ *   gran   FP8Q_GRAN_BLOCK128 or FP8Q_GRAN_BLOCK128_POW2 (power-of-two scales
+ *     applied inside the MFMA, as in fp8q_gemm_blockscale).
+ *   y bf16 [M, ldy].
+ * K must be a multiple of 128 (FP8Q_ERR_UNSUPPORTED otherwise).
+ */
+fp8q_status_t fp8q_gemm_grouped_blockscale(const uint8_t* a, int64_t lda, const float* a_scales,
+                                           int32_t a_layout, const int32_t* expert_offsets, int32_t E,
+                                           const uint8_t* w, int64_t ldw, int64_t w_expert_stride,
+                                           const float* w_scale_inv, int64_t shard, uint16_t* y,
+                                           int64_t ldy, int64_t M, int64_t N, int64_t K, int32_t gran,
+                                           void* stream);
+
+/*
  * fp8q_gemm_mxfp8 -- MXFP8 GEMM: 1x32 blocks on both operands.
  *
  * [SGLFP8] "4. 블록 양자화 스케일 관리" (uint8 UE8M0 scales) and [SGL19]

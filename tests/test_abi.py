@@ -144,6 +144,36 @@ def test_requant_weight_pow2_validation(lib):
     assert f(A, 256, C, 256, 256, Q2, 256, ctypes.c_void_p(0x100000), None) == 7        # s_out over q_in
 
 
+def test_gemm_grouped_validation(lib):
+    f = lib.fp8q_gemm_grouped_blockscale
+    O = ctypes.c_void_p(0x600000)
+    ok = [A, 256, C, 0, O, 4, B, 256, 256 * 256, C, 0, ctypes.c_void_p(0x700000), 256, 100, 256, 256, 0, None]
+
+    def call(**kw):
+        names = ["a", "lda", "sa", "layout", "off", "E", "w", "ldw", "wstride", "sw", "shard", "y", "ldy", "M", "N",
+                 "K", "gran", "stream"]
+        args = list(ok)
+        for k, v in kw.items():
+            args[names.index(k)] = v
+        return f(*args)
+
+    assert call(M=-1) == 2
+    assert call(E=0) == 2 and call(E=1025) == 2
+    assert call(shard=-64) == 2
+    assert call(gran=1) == 3                                   # per-tensor is not grouped
+    assert call(layout=2) == 3
+    assert call(K=200, lda=208, ldw=208) == 3                  # K % 128
+    assert call(shard=100) == 3                                # not a multiple of 64
+    assert call(shard=192) == 3                                # does not divide N = 256
+    assert call(M=0) == 0
+    assert call(off=None) == 1
+    assert call(sw=None) == 1
+    assert call(off=ctypes.c_void_p(0x600002)) == 4
+    assert call(wstride=256 * 255) == 2                        # experts overlap
+    assert call(wstride=256 * 256 + 8) == 4
+    assert call(ldy=200) == 2
+
+
 def test_quant_weight_block_validation(lib):
     f = lib.fp8q_quant_weight_block
     assert f(A, 256, 256, 256, 64, 64, 0, B, 256, C, None) == 3          # 64x64 blocks
@@ -189,6 +219,9 @@ def test_device_check_without_gpu(lib):
     assert lib.fp8q_quant_weight_block(A, 256, 256, 256, 128, 128, 2, B, 256, C, None) == 5
     assert lib.fp8q_requant_weight_pow2(A, 256, C, 256, 256, A, 256, C, None) == 5          # in place
     assert lib.fp8q_gemm_blockscale(A, 128, C, 0, B, 128, C, None, C, 256, 4, 256, 128, 2, None) == 5
+    # the grouped GEMM with shards (and the power-of-two format)
+    assert lib.fp8q_gemm_grouped_blockscale(A, 256, C, 1, ctypes.c_void_p(0x600000), 4, B, 256, 512 * 256, C, 256,
+                                            ctypes.c_void_p(0x700000), 512, 100, 512, 256, 2, None) == 5
 
 
 @pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")

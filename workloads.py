@@ -20,7 +20,13 @@ with round-to-nearest-even):
 * weights ~ N(0, std) with std = 1/sqrt(K) unless stated;
 * RMSNorm gain g ~ U(0.5, 1.5);
 * sublayer output added to the residual stream: activations of their own
-  seed (outlier channels included) times 0.25, an exact power-of-two scaling.
+  seed (outlier channels included) times 0.25, an exact power-of-two scaling;
+* MoE routing (synthetic, the GEMM's input layout only): every token picks
+  top_k distinct experts uniformly at random (the top_k largest of uniform
+  draws); the (token, expert) pairs whose expert is local are sorted by
+  expert, then token, and the token rows are gathered in that order.  Expert
+  weights are drawn per expert from seed + expert, so any expert can be
+  regenerated alone.
 """
 from __future__ import annotations
 
@@ -32,6 +38,9 @@ import torch
 __all__ = [
     "Workload",
     "WORKLOADS",
+    "MoeWorkload",
+    "MOE_WORKLOADS",
+    "moe_routing",
     "activations",
     "weights",
     "gamma",
@@ -119,4 +128,70 @@ WORKLOADS = {
     "large": Workload("large", 8192, 18432, 7168, seed=3, outlier_frac=0.001),
     # MXFP8 / per-tensor: A [2048,7168], W [7168,7168], both N(0,1)
     "mx": Workload("mx", 2048, 7168, 7168, seed=4, w_std=1.0, mx=True),
+}
+
+
+def moe_routing(tokens: int, top_k: int, n_experts: int, local_experts: int, seed: int):
+    """(token index of each dispatched row [M], offsets [local_experts + 1]).
+
+    Rows are sorted by expert, then by token; rows offsets[e] .. offsets[e+1]
+    go to local expert e (experts 0 .. local_experts - 1 are local).
+    """
+    gen = make_generator(seed)
+    picks = torch.rand(tokens, n_experts, generator=gen).topk(top_k, dim=1).indices   # [T, top_k]
+    tok = torch.arange(tokens).repeat_interleave(top_k)
+    exp = picks.reshape(-1)
+    keep = exp < local_experts
+    tok, exp = tok[keep], exp[keep]
+    order = torch.argsort(exp * tokens + tok)
+    tok, exp = tok[order], exp[order]
+    counts = torch.bincount(exp, minlength=local_experts)
+    offsets = torch.zeros(local_experts + 1, dtype=torch.int64)
+    offsets[1:] = torch.cumsum(counts, 0)
+    return tok, offsets
+
+
+@dataclass(frozen=True)
+class MoeWorkload:
+    """Expert GEMMs of one MoE layer on one GPU's share of the experts."""
+    name: str
+    tokens: int
+    top_k: int
+    n_experts: int       # routed experts of the layer
+    local_experts: int   # experts held by this GPU
+    hidden: int          # H
+    inter: int           # I_p
+    proj: str            # "up" (w13: N = 2 I_p, K = H, gate/up shards) or "down" (w2: N = H, K = I_p)
+    seed: int
+
+    @property
+    def N(self) -> int:
+        return 2 * self.inter if self.proj == "up" else self.hidden
+
+    @property
+    def K(self) -> int:
+        return self.hidden if self.proj == "up" else self.inter
+
+    @property
+    def shard(self) -> int:
+        return self.inter if self.proj == "up" else 0
+
+    def routing(self):
+        return moe_routing(self.tokens, self.top_k, self.n_experts, self.local_experts, self.seed * 10 + 5)
+
+    def activations(self, device: str = "cpu") -> torch.Tensor:
+        """Dispatched (expert-sorted) input rows [M, K]."""
+        tok, _ = self.routing()
+        x = activations(self.tokens, self.K, self.seed * 10 + 1, 0.001, device="cpu")
+        return x[tok].to(device)
+
+    def expert_weight(self, e: int, device: str = "cpu") -> torch.Tensor:
+        return weights(self.N, self.K, self.seed * 1000 + e, device=device)
+
+
+MOE_WORKLOADS = {
+    # the pages' example layer (H 7168, I_p 2048, 256 experts, top-8) with
+    # experts split over 8 GPUs: 32 local experts, 4096 tokens
+    "moe_up": MoeWorkload("moe_up", 4096, 8, 256, 32, 7168, 2048, "up", seed=7),
+    "moe_down": MoeWorkload("moe_down", 4096, 8, 256, 32, 7168, 2048, "down", seed=8),
 }
