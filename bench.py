@@ -6,7 +6,9 @@ activations already resident in HBM: the activation quantizer (fused with
 RMSNorm for the prefill-with-norm workload, and with the residual add in front
 of it for the add-norm workload, which updates the stream in place) followed
 by the scaled GEMM (`*_pow2` workloads: the same with power-of-two scales
--- block FP8 as an MXFP8 view -- applied inside the MFMA).  The
+-- block FP8 as an MXFP8 view -- applied inside the MFMA; `moe_*`: the
+expert-sorted rows of one GPU's share of a MoE layer through the grouped
+GEMM).  The
 weight is quantized once before timing (it is offline preparation).  Inputs
 and outputs rotate over several buffer sets whose total exceeds the 256 MB
 Infinity Cache, so HBM rates are not inflated by cache hits.
@@ -47,7 +49,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="prefill_norm",
                     choices=["tiny", "decode", "prefill_norm", "prefill_addnorm", "large", "mx", "pertensor",
-                             "prefill_norm_pow2", "large_pow2"])
+                             "prefill_norm_pow2", "large_pow2", "moe_up", "moe_down"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample (0 = skip)")
     return ap.parse_args()
@@ -95,6 +97,8 @@ def main() -> int:
     fq.load_library()
 
     name = args.workload
+    if name in workloads.MOE_WORKLOADS:
+        return moe_main(args, workloads.MOE_WORKLOADS[name])
     pow2 = name.endswith("_pow2")
     wl = workloads.WORKLOADS["mx" if name == "pertensor" else name[:-5] if pow2 else name]
     M, N, K = wl.M, wl.N, wl.K
@@ -263,6 +267,140 @@ def main() -> int:
         out["cpu_baseline"] = cpu_baseline(name, wl, d, args.cpu_seconds, pow2)
     print(json.dumps(out), flush=True)
     return 0
+
+
+def moe_main(args, wl) -> int:
+    """One GPU's share of a MoE layer: group-quantize the expert-sorted rows,
+    then the grouped block GEMM over the local experts (weights quantized
+    beforehand, untimed)."""
+    import numpy as np
+    import torch
+
+    import fp8_block_scaled_token_amd as fq
+
+    _, off = wl.routing()
+    M, N, K, E = int(off[-1]), wl.N, wl.K, wl.local_experts
+    KB = K // 128
+    x = wl.activations().cuda()
+    offd = off.to(torch.int32).cuda()
+    shard = wl.shard
+    nbs = (N // shard) * math.ceil(shard / 128) if shard else math.ceil(N / 128)
+    qw = torch.empty(E, N, K, dtype=torch.uint8, device="cuda")
+    sw = torch.empty(E, nbs, KB, dtype=torch.float32, device="cuda")
+    for e in range(E):
+        wd = wl.expert_weight(e, device="cuda")      # seeded per expert on the device
+        if shard:
+            nb = math.ceil(shard / 128)
+            for i in range(N // shard):
+                fq.fp8q_quant_weight_block(wd[i * shard:(i + 1) * shard], 128, 128, fq.SCALE_F32,
+                                           qw[e, i * shard:(i + 1) * shard], sw[e, i * nb:(i + 1) * nb])
+        else:
+            fq.fp8q_quant_weight_block(wd, 128, 128, fq.SCALE_F32, qw[e], sw[e])
+        del wd
+    set_bytes = M * K * 3 + M * KB * 4 + M * N * 2
+    nsets = max(2, min(8, math.ceil(MALL_DEFEAT_BYTES / set_bytes)))
+    sets = [{"x": x.clone(), "q": torch.empty(M, K, dtype=torch.uint8, device="cuda"),
+             "s": torch.empty(KB, M, dtype=torch.float32, device="cuda"),
+             "y": torch.empty(M, N, dtype=torch.bfloat16, device="cuda")} for _ in range(nsets)]
+
+    def quant(s):
+        fq.fp8q_quant_act_group(s["x"], 128, fq.SCALE_F32, fq.COL_MAJOR, None, s["q"], s["s"])
+
+    def gemm(s):
+        fq.fp8q_gemm_grouped_blockscale(s["q"], s["s"], fq.COL_MAJOR, offd, qw, sw, s["y"], shard, fq.GRAN_BLOCK128)
+
+    for i in range(args.warmup):
+        quant(sets[i % nsets])
+        gemm(sets[i % nsets])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        quant(sets[i % nsets])
+        gemm(sets[i % nsets])
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    def timed(fn, reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for i in range(min(reps, nsets)):
+            fn(sets[i % nsets])
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(reps):
+            fn(sets[i % nsets])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    reps = max(args.steps, 2 * nsets)
+    quant_ms = timed(quant, reps)
+    gemm_ms = timed(gemm, reps)
+    flops = 2.0 * M * N * K
+    g_bytes = E * N * K + M * K + 4 * M * KB + 4 * E * nbs * KB + 2 * M * N
+    q_bytes = M * K * 3 + 4 * M * KB
+    gemm_gbps = g_bytes / (gemm_ms * 1e-3) / 1e9
+    gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
+    quant_gbps = q_bytes / (quant_ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC, "value": round(flops / (ms_per_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate)", "data": "synthetic",
+        "config": {"workload": wl.name, "M": M, "N": N, "K": K, "experts": E, "tokens": wl.tokens,
+                   "top_k": wl.top_k, "routed_experts": wl.n_experts, "shard": shard,
+                   "scales": "group128 + 128x128 fp32 per expert", "rotating_buffer_sets": nsets},
+        # weight streaming dominates: 2 flops per weight byte per routed row
+        # (about 2 * 129 here) is below the chip's 625 flop/byte balance
+        "roofline": {"bound": "hbm", "achieved": round(gemm_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(gemm_gbps / PEAK_HBM_GBPS, 4), "traffic": None},
+        "gemm": {"us": round(gemm_ms * 1e3, 2), "TFLOP/s": round(gemm_tflops, 1),
+                 "frac_fp8_peak": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "GB/s": round(gemm_gbps, 1),
+                 "algorithmic_bytes": g_bytes},
+        "quant": {"kernel": "quant_group128", "us": round(quant_ms * 1e3, 2), "GB/s": round(quant_gbps, 1),
+                  "frac_hbm": round(quant_gbps / PEAK_HBM_GBPS, 4), "algorithmic_bytes": q_bytes},
+        "cpu_baseline": None,
+    }
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = moe_cpu_baseline(wl, x.cpu(), off, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def moe_cpu_baseline(wl, x, off, target_s):
+    """The oracle's group quantizer and grouped GEMM on the rows of the first
+    experts (growing until about target_s of CPU time)."""
+    import numpy as np
+    from oracle import gemm as og
+    from oracle import quant as oq
+    off = off.numpy()
+    xh = x.float().numpy()
+    cache = {}
+
+    def weight(e):
+        if e not in cache:
+            wh = wl.expert_weight(e, device="cuda").float().cpu().numpy()
+            cache[e] = oq.quant_weight_block_sharded(wh, wl.shard) if wl.shard else oq.quant_weight_block(wh)
+        return cache[e]
+
+    n_exp = 1
+    while True:
+        for e in range(n_exp):
+            weight(e)                                    # weight preparation is untimed
+        rows = int(off[n_exp])
+        t0 = time.perf_counter()
+        qa, sa = oq.quant_group(xh[:rows])
+        og.gemm_grouped_blockscale(qa, sa, lambda e: weight(e)[0], lambda e: weight(e)[1], off[:n_exp + 1],
+                                   shard=wl.shard)
+        t = time.perf_counter() - t0
+        if t >= 0.5 * target_s or n_exp >= wl.local_experts or n_exp >= 8:
+            break
+        n_exp = min(wl.local_experts, 8, max(n_exp + 1, int(n_exp * 0.8 * target_s / max(t, 1e-3))))
+    return {"value": 2.0 * rows * wl.N * wl.K / t / 1e12, "unit": "TFLOP/s",
+            "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"rows of the first {n_exp} of {wl.local_experts} experts ({rows} rows, {t:.1f} s; "
+                      f"weights quantized beforehand, untimed)",
+            "host_cpus": len(os.sched_getaffinity(0))}
 
 
 def cpu_baseline(name, wl, d, target_s, pow2=False):
