@@ -20,10 +20,12 @@ import torch
 __all__ = [
     "load_library", "FP8QError", "abi_version",
     "fp8q_quant_act_group", "fp8q_rmsnorm_quant", "fp8q_add_rmsnorm_quant", "fp8q_quant_weight_block",
-    "fp8q_requant_weight_pow2", "fp8q_gemm_blockscale", "fp8q_gemm_grouped_blockscale", "fp8q_gemm_mxfp8",
+    "fp8q_requant_weight_pow2", "fp8q_gemm_blockscale", "fp8q_gemm_blockscale_splitk",
+    "fp8q_gemm_splitk_workspace_size", "fp8q_gemm_grouped_blockscale", "fp8q_gemm_mxfp8",
     "quant_act_group", "quant_act_group_pow2", "rmsnorm_quant_pow2", "quant_act_static", "quant_act_mx", "rmsnorm_quant", "add_rmsnorm_quant",
     "quant_weight_block", "quant_weight_block_pow2", "requant_weight_pow2", "quant_weight_mx", "quant_weight_tensor",
-    "gemm_blockscale", "gemm_blockscale_pow2", "gemm_grouped_blockscale", "gemm_pertensor", "gemm_mxfp8",
+    "gemm_blockscale", "gemm_blockscale_pow2", "gemm_blockscale_splitk", "gemm_grouped_blockscale",
+    "gemm_pertensor", "gemm_mxfp8",
     "SCALE_F32", "SCALE_UE8M0", "SCALE_F32_POW2", "ROW_MAJOR", "COL_MAJOR", "GRAN_BLOCK128", "GRAN_PER_TENSOR",
     "GRAN_BLOCK128_POW2",
 ]
@@ -49,6 +51,9 @@ SIGNATURES = {
     "fp8q_requant_weight_pow2": (ctypes.c_int, [_P, _I64, _P, _I64, _I64, _P, _I64, _P, _P]),
     "fp8q_quant_weight_block": (ctypes.c_int, [_P, _I64, _I64, _I64, _I32, _I32, _I32, _P, _I64, _P, _P]),
     "fp8q_gemm_blockscale": (ctypes.c_int, [_P, _I64, _P, _I32, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _P]),
+    "fp8q_gemm_splitk_workspace_size": (ctypes.c_size_t, [_I64, _I64, _I64]),
+    "fp8q_gemm_blockscale_splitk": (ctypes.c_int, [_P, _I64, _P, _I32, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _I64,
+                                                   _I32, _P, ctypes.c_size_t, _P]),
     "fp8q_gemm_grouped_blockscale": (ctypes.c_int, [_P, _I64, _P, _I32, _P, _I32, _P, _I64, _I64, _P, _I64, _P, _I64,
                                                     _I64, _I64, _I64, _I32, _P]),
     "fp8q_gemm_mxfp8": (ctypes.c_int, [_P, _I64, _P, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _I64, _P]),
@@ -198,6 +203,26 @@ def fp8q_gemm_blockscale(a, a_scales, a_layout, w, w_scale_inv, bias, y, gran, s
     _check(load_library().fp8q_gemm_blockscale(_ptr(a), lda, _ptr(a_scales), a_layout, _ptr(w), ldw,
                                                _ptr(w_scale_inv), _ptr(bias), _ptr(y), ldy, M, N, K,
                                                gran, _stream(stream)), "fp8q_gemm_blockscale")
+
+
+def fp8q_gemm_splitk_workspace_size(M: int, N: int, K: int) -> int:
+    return int(load_library().fp8q_gemm_splitk_workspace_size(M, N, K))
+
+
+def fp8q_gemm_blockscale_splitk(a, a_scales, a_layout, w, w_scale_inv, bias, y, gran, workspace, stream=None):
+    """fp8q_gemm_blockscale with K split over idle CUs; workspace: a device
+    tensor (its whole size is offered) or None."""
+    a, w = _u8(a), _u8(w)
+    M, K, lda = _rows(a, torch.uint8, "a")
+    N, Kw, ldw = _rows(w, torch.uint8, "w")
+    My, Ny, ldy = _rows(y, torch.bfloat16, "y")
+    if Kw != K or (My, Ny) != (M, N):
+        raise ValueError("shape mismatch")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().fp8q_gemm_blockscale_splitk(_ptr(a), lda, _ptr(a_scales), a_layout, _ptr(w), ldw,
+                                                      _ptr(w_scale_inv), _ptr(bias), _ptr(y), ldy, M, N, K, gran,
+                                                      _ptr(workspace), ws_bytes, _stream(stream)),
+           "fp8q_gemm_blockscale_splitk")
 
 
 def fp8q_gemm_grouped_blockscale(a, a_scales, a_layout, expert_offsets, w, w_scale_inv, y, shard=0,
@@ -380,6 +405,19 @@ def gemm_blockscale_pow2(a, a_scales, w, w_scale_inv, bias=None, a_layout: int =
     """Block GEMM on power-of-two scales, applied by the scaled MFMA."""
     y = _y(a.shape[0], w.shape[0], a.device)
     fp8q_gemm_blockscale(a, a_scales, a_layout, w, w_scale_inv, bias, y, GRAN_BLOCK128_POW2, stream)
+    return y
+
+
+def gemm_blockscale_splitk(a, a_scales, w, w_scale_inv, bias=None, a_layout: int = ROW_MAJOR, gran=GRAN_BLOCK128,
+                           workspace=None, stream=None):
+    """Block GEMM with split-K on decode shapes; allocates the workspace
+    (torch) when none is given."""
+    M, N, K = a.shape[0], w.shape[0], a.shape[1]
+    if workspace is None:
+        nbytes = fp8q_gemm_splitk_workspace_size(M, N, K)
+        workspace = torch.empty(max(nbytes, 4) // 4, dtype=torch.float32, device=a.device) if nbytes else None
+    y = _y(M, N, a.device)
+    fp8q_gemm_blockscale_splitk(a, a_scales, a_layout, w, w_scale_inv, bias, y, gran, workspace, stream)
     return y
 
 

@@ -266,6 +266,39 @@ fp8q_status_t fp8q_gemm_blockscale(const uint8_t* a, int64_t lda, const float* a
                                                      gran, static_cast<hipStream_t>(stream)));
 }
 
+size_t fp8q_gemm_splitk_workspace_size(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || N < 1 || K < 1 || M > kMaxRows || N > kMaxRows || K > kMaxK) return 0;
+  if (check_device() != FP8Q_OK) return 0;
+  return fp8q::gemm_splitk_workspace(M, N, K);
+}
+
+fp8q_status_t fp8q_gemm_blockscale_splitk(const uint8_t* a, int64_t lda, const float* a_scales,
+                                          int32_t a_layout, const uint8_t* w, int64_t ldw,
+                                          const float* w_scale_inv, const uint16_t* bias,
+                                          uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                                          int32_t gran, void* workspace, size_t workspace_bytes,
+                                          void* stream) {
+  if (M < 0 || N < 0 || K <= 0 || M > kMaxRows || N > kMaxRows || K > kMaxK) return FP8Q_ERR_SHAPE;
+  if ((M / 128 + 1) * (N / 128 + 1) >= (int64_t(1) << 24)) return FP8Q_ERR_SHAPE;
+  if (gran != FP8Q_GRAN_BLOCK128 && gran != FP8Q_GRAN_PER_TENSOR && gran != FP8Q_GRAN_BLOCK128_POW2)
+    return FP8Q_ERR_UNSUPPORTED;
+  if (a_layout != FP8Q_SCALES_ROW_MAJOR && a_layout != FP8Q_SCALES_COL_MAJOR) return FP8Q_ERR_UNSUPPORTED;
+  if (workspace == nullptr && workspace_bytes != 0) return FP8Q_ERR_NULL;
+  if (M == 0 || N == 0) return FP8Q_OK;
+  FP8Q_TRY(check_matrix(a, K, lda, 1));
+  FP8Q_TRY(check_matrix(w, K, ldw, 1));
+  FP8Q_TRY(check_matrix(y, N, ldy, 2));
+  if (a_scales == nullptr || w_scale_inv == nullptr) return FP8Q_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(a_scales) & 3u) || (reinterpret_cast<uintptr_t>(w_scale_inv) & 3u) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 3u))
+    return FP8Q_ERR_MISALIGNED;
+  if (bias != nullptr && (reinterpret_cast<uintptr_t>(bias) & 1u)) return FP8Q_ERR_MISALIGNED;
+  FP8Q_TRY(check_device());
+  return launch_status(fp8q::launch_gemm_blockscale_splitk(
+      a, lda, a_scales, a_layout == FP8Q_SCALES_COL_MAJOR, w, ldw, w_scale_inv, bias, y, ldy, M, N, K, gran,
+      workspace, workspace_bytes, static_cast<hipStream_t>(stream)));
+}
+
 fp8q_status_t fp8q_gemm_grouped_blockscale(const uint8_t* a, int64_t lda, const float* a_scales,
                                            int32_t a_layout, const int32_t* expert_offsets, int32_t E,
                                            const uint8_t* w, int64_t ldw, int64_t w_expert_stride,

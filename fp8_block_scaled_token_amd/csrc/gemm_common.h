@@ -38,6 +38,8 @@ struct GemmArgs {
   int m_end;            // output rows at or past m_end are not stored (M, or an expert's end)
   int shard;            // stacked weight shards of `shard` rows each (0: one shard), see below
   int shard_blocks;     // ceil(shard / 128)
+  int split_kb;         // split-K: K blocks per split (0: no split); split s = blockIdx.y
+  float* partial;       // split-K: fp32 partial sums [splits][M][N] (row stride N)
 };
 
 // Weight scale row of output channel j: j / 128, or with stacked shards
@@ -130,5 +132,11 @@ hipError_t launch_gemm_grouped(GemmArgs p, const int32_t* offsets, int E, int64_
 // Decode path (gemm_decode.hip): shapes it accepts, and its launcher.
 bool gemm_decode_eligible(const GemmArgs& p);
 hipError_t launch_gemm_decode(GemmArgs p, int mode, hipStream_t stream);
+// Split-K decode: the K blocks are cut into `splits` runs of p.split_kb, one
+// grid row each, whose fp32 partial sums go to p.partial; a second kernel adds
+// them in split order and applies the epilogue.  decode_splits() is the
+// split count launch_gemm_decode_split uses for a shape (1: no split).
+int decode_splits(const GemmArgs& p);
+hipError_t launch_gemm_decode_split(GemmArgs p, int mode, int splits, hipStream_t stream);
 
 }  // namespace fp8q

@@ -17,6 +17,12 @@
 //  * Fragments sit in LDS in the XOR-swizzled layout of the prefill kernel:
 //    a 1 KB load covers eight 128-byte K-block rows, lane i fetching chunk
 //    (i % 8) ^ (i / 8) of row i / 8.
+//  * Split-K (when the column tiles alone leave CUs idle): grid row s takes
+//    K blocks [s * split_kb, (s + 1) * split_kb) and writes its fp32 partial
+//    sums instead of the output; splitk_reduce_kernel adds the splits in
+//    order s = 0, 1, ... (fixed, so repeated calls give the same bits; the
+//    order differs from the unsplit kernel's, so the bits may differ from
+//    it) and applies the epilogue.
 // Arithmetic per K block is that of the other kernels: one
 // v_mfma_scale_f32_16x16x128_f8f6f4 per 16x16 tile and K block, then the
 // block rescale (block mode), nothing (per-tensor, scaled in the epilogue)
@@ -68,7 +74,9 @@ __global__ __launch_bounds__(256) void gemm_decode_dma_kernel(GemmArgs p) {
   const int lane = threadIdx.x & 63, l16 = lane & 15, lq = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n0 = blockIdx.x * (16 * TN);
-  const int KB = p.KB;
+  // this grid row's K blocks [kb0, KB)
+  const int kb0 = p.split_kb ? (int)blockIdx.y * p.split_kb : 0;
+  const int KB = p.split_kb ? min(p.KB, kb0 + p.split_kb) : p.KB;
 
   const i32x4 rA = rsrc(p.a, (int64_t)p.M * p.lda);
   const i32x4 rW = rsrc(p.w, (int64_t)p.N * p.ldw);
@@ -229,12 +237,13 @@ __global__ __launch_bounds__(256) void gemm_decode_dma_kernel(GemmArgs p) {
   // (whose LDS reads are waited for) is refilled with block t + S - 1; then
   // the wave waits until only the loads of blocks t + 1 .. t + S - 1 are in
   // flight, i.e. block t has landed, and multiplies it.
-  const int T = KB > wave ? (KB - wave + 3) / 4 : 0;
+  const int kw = kb0 + wave;                 // this wave's first block
+  const int T = KB > kw ? (KB - kw + 3) / 4 : 0;
 #pragma unroll
-  for (int s = 0; s < S - 1; ++s) issue(s, wave + 4 * s);
+  for (int s = 0; s < S - 1; ++s) issue(s, kw + 4 * s);
   for (int t = 0; t < T; ++t) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    issue((t + S - 1) % S, wave + 4 * (t + S - 1));
+    issue((t + S - 1) % S, kw + 4 * (t + S - 1));
     wait_vmcnt<LOADS * (S - 1)>();
     compute(t % S);
   }
@@ -265,6 +274,24 @@ __global__ __launch_bounds__(256) void gemm_decode_dma_kernel(GemmArgs p) {
         for (int r = 0; r < 4; ++r) acc[i][j][r] = acc[i][j][r] + o[r];
       }
 
+  if (p.split_kb) {
+    // fp32 partial sums of this split: element (row, col) at
+    // partial[(split * M + row) * N + col]; lane holds rows 16i + 4*(lane/16) + r
+    float* part = p.partial + (int64_t)blockIdx.y * p.M * p.N;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = n0 + 16 * j + l16;
+      if (col >= p.N) continue;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * i + 4 * lq + r;
+          if (row < p.M) part[(int64_t)row * p.N + col] = acc[i][j][r];
+        }
+    }
+    return;
+  }
   float mul = 1.0f;
   if (MODE == MODE_TENSOR)
     mul = static_cast<const float*>(p.sa)[0] * static_cast<const float*>(p.sw)[0];
@@ -277,12 +304,35 @@ __global__ __launch_bounds__(256) void gemm_decode_dma_kernel(GemmArgs p) {
   }
 }
 
+// y = bf16(sum over splits s = 0, 1, ... of partial[s] (in that order),
+// times the per-tensor scale product if any, plus bias).  Thread t handles
+// four consecutive columns of one row.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs p, int splits, int per_tensor) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int cols4 = (p.N + 3) / 4;
+  const int64_t row = q / cols4;
+  const int c0 = (int)(q % cols4) * 4;
+  if (row >= p.M) return;
+  float mul = 1.0f;
+  if (per_tensor) mul = static_cast<const float*>(p.sa)[0] * static_cast<const float*>(p.sw)[0];
+  const int64_t plane = (int64_t)p.M * p.N;
+  for (int c = c0; c < c0 + 4 && c < p.N; ++c) {
+    const float* src = p.partial + row * p.N + c;
+    float v = src[0];
+    for (int s = 1; s < splits; ++s) v = v + src[s * plane];
+    if (per_tensor) v = v * mul;
+    const float b = p.bias != nullptr ? __uint_as_float((uint32_t)p.bias[c] << 16) : 0.0f;
+    p.y[row * p.ldy + c] = (uint16_t)f32_to_bf16_bits(v + b);
+  }
+}
+
 namespace {
 
 template <int MODE, int TM, int TN, int S>
-void launch_dec(const GemmArgs& p, hipStream_t stream) {
+void launch_dec(const GemmArgs& p, hipStream_t stream, int splits = 1) {
   using D = DecTile<TM, TN, S, MODE>;
-  hipLaunchKernelGGL(gemm_decode_dma_kernel<D>, dim3((p.N + 16 * TN - 1) / (16 * TN)), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(gemm_decode_dma_kernel<D>, dim3((p.N + 16 * TN - 1) / (16 * TN), splits), dim3(256), 0, stream,
+                     p);
 }
 
 // Column tiles per workgroup and ring depth: six column tiles (96
@@ -319,6 +369,43 @@ bool gemm_decode_eligible(const GemmArgs& p) {
   return p.M >= 1 && p.M <= 64 && p.K % 128 == 0 && (int64_t)(p.N + 96) * p.ldw < lim &&
          (int64_t)64 * p.lda < lim && (int64_t)p.M * p.KB * 4 < lim && (int64_t)(p.NB + 2) * p.KB * 4 < lim &&
          (int64_t)(p.N + 96) * p.KB32 < lim;
+}
+
+// Split count of the split-K path: as many K runs as keep every CU busy
+// with the narrow (two column tiles, 32 channels) configuration, at least
+// eight K blocks per run, at most 8 runs -- and no split below 96 K blocks:
+// the reduction kernel and its launch cost about as much as a short K loop
+// saves (measured at M = 32: K 7168 loses 2 us of 12; K 14336 gains 5 of
+// 18, K 28672 gains 23 of 44).
+int decode_splits(const GemmArgs& p) {
+  if (!gemm_decode_eligible(p) || p.KB < 96) return 1;
+  const int cus = device_cu_count();
+  const int wgs = (p.N + 31) / 32;
+  int s = cus / (wgs > 0 ? wgs : 1);
+  s = s < p.KB / 8 ? s : p.KB / 8;
+  s = s < 8 ? s : 8;
+  return s < 1 ? 1 : s;
+}
+
+template <int MODE>
+void launch_dec_split(const GemmArgs& p, int splits, hipStream_t stream) {
+  const int tm = (p.M + 15) / 16;
+  if (tm == 1) launch_dec<MODE, 1, 2, 4>(p, stream, splits);
+  else if (tm == 2) launch_dec<MODE, 2, 2, 4>(p, stream, splits);
+  else if (tm == 3) launch_dec<MODE, 3, 2, 3>(p, stream, splits);
+  else launch_dec<MODE, 4, 2, 3>(p, stream, splits);
+}
+
+hipError_t launch_gemm_decode_split(GemmArgs p, int mode, int splits, hipStream_t stream) {
+  p.split_kb = (p.KB + splits - 1) / splits;
+  splits = (p.KB + p.split_kb - 1) / p.split_kb;            // no empty split
+  if (mode == MODE_BLOCK) launch_dec_split<MODE_BLOCK>(p, splits, stream);
+  else if (mode == MODE_TENSOR) launch_dec_split<MODE_TENSOR>(p, splits, stream);
+  else launch_dec_split<MODE_MX>(p, splits, stream);
+  const int64_t threads = (int64_t)p.M * ((p.N + 3) / 4);
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, p, splits,
+                     mode == MODE_TENSOR ? 1 : 0);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_decode(GemmArgs p, int mode, hipStream_t stream) {

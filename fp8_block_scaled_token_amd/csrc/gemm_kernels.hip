@@ -389,6 +389,46 @@ hipError_t launch_gemm_blockscale(const uint8_t* a, int64_t lda, const float* sa
   return launch_mode<MODE_BLOCK>(p, stream);
 }
 
+namespace {
+
+GemmArgs block_args(const uint8_t* a, int64_t lda, const float* sa, int sa_col_major, const uint8_t* w,
+                    int64_t ldw, const float* sw, const uint16_t* bias, uint16_t* y, int64_t ldy, int64_t M,
+                    int64_t N, int64_t K) {
+  GemmArgs p{};
+  p.a = a; p.lda = lda; p.sa = sa; p.sa_col_major = sa_col_major;
+  p.w = w; p.ldw = ldw; p.sw = sw; p.bias = bias; p.y = y; p.ldy = ldy;
+  p.M = (int)M; p.N = (int)N; p.K = (int)K;
+  p.KB = cdiv(K, 128); p.KB32 = cdiv(K, 32); p.NB = cdiv(N, 128);
+  p.m_end = p.M;
+  return p;
+}
+
+}  // namespace
+
+size_t gemm_splitk_workspace(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || M > 64 || N < 1 || K < 1) return 0;
+  const GemmArgs p = block_args(nullptr, K, nullptr, 0, nullptr, K, nullptr, nullptr, nullptr, N, M, N, K);
+  const int s = decode_splits(p);
+  return s > 1 ? (size_t)s * (size_t)M * (size_t)N * 4u : 0u;
+}
+
+hipError_t launch_gemm_blockscale_splitk(const uint8_t* a, int64_t lda, const float* sa, int sa_col_major,
+                                         const uint8_t* w, int64_t ldw, const float* sw, const uint16_t* bias,
+                                         uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, int gran,
+                                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  GemmArgs p = block_args(a, lda, sa, sa_col_major, w, ldw, sw, bias, y, ldy, M, N, K);
+  if (p.M <= 64 && workspace != nullptr && gemm_decode_eligible(p)) {
+    int s = decode_splits(p);
+    const int64_t fit = (int64_t)(workspace_bytes / ((size_t)M * (size_t)N * 4u));
+    if (s > fit) s = (int)fit;
+    if (s >= 2) {
+      p.partial = static_cast<float*>(workspace);
+      return launch_gemm_decode_split(p, gran == 1 ? MODE_TENSOR : MODE_BLOCK, s, stream);
+    }
+  }
+  return launch_gemm_blockscale(a, lda, sa, sa_col_major, w, ldw, sw, bias, y, ldy, M, N, K, gran, stream);
+}
+
 hipError_t launch_gemm_grouped_blockscale(const uint8_t* a, int64_t lda, const float* sa, int sa_col_major,
                                           const int32_t* offsets, int E, const uint8_t* w, int64_t ldw,
                                           int64_t w_stride, const float* sw, int64_t shard, uint16_t* y,

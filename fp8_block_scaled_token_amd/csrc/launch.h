@@ -44,6 +44,14 @@ hipError_t launch_gemm_blockscale(const uint8_t* a, int64_t lda, const float* sa
                                   const uint8_t* w, int64_t ldw, const float* sw,
                                   const uint16_t* bias, uint16_t* y, int64_t ldy, int64_t M,
                                   int64_t N, int64_t K, int gran, hipStream_t stream);
+// Split-K variant of launch_gemm_blockscale: fp32 partials in `workspace`
+// (decode shapes whose column tiles leave CUs idle); otherwise, or when the
+// workspace is too small for two splits, the unsplit kernels.
+size_t gemm_splitk_workspace(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_blockscale_splitk(const uint8_t* a, int64_t lda, const float* sa, int sa_col_major,
+                                         const uint8_t* w, int64_t ldw, const float* sw, const uint16_t* bias,
+                                         uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, int gran,
+                                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 // Grouped (MoE) block GEMM over expert-sorted rows; hipErrorInvalidValue when
 // the sizes exceed the kernel's 32-bit offsets (nothing is launched then).
 hipError_t launch_gemm_grouped_blockscale(const uint8_t* a, int64_t lda, const float* sa, int sa_col_major,

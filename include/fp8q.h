@@ -45,6 +45,7 @@
 #ifndef FP8Q_H
 #define FP8Q_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -243,6 +244,35 @@ fp8q_status_t fp8q_gemm_blockscale(const uint8_t* a, int64_t lda, const float* a
                                    const float* w_scale_inv, const uint16_t* bias,
                                    uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K,
                                    int32_t gran, void* stream);
+
+/*
+ * fp8q_gemm_blockscale_splitk -- fp8q_gemm_blockscale with K split into segments.
+ *
+ * [SGL19] "Triton 分块内核在做什么": with SPLIT_K > 1 the K dimension is cut
+ * into segments, each accumulated into its own fp32 partial sum, and a
+ * reduction kernel adds them; this changes the order of the floating-point
+ * additions, so the result is not bit-identical to the single-accumulator
+ * kernel (it is the same formula, within the same bound).  Here the split
+ * serves decode shapes (M <= 64, K >= 12288) whose column tiles alone leave
+ * compute units idle: each of S segments streams its share of the weight on
+ * otherwise idle CUs; the partials are added in segment order 0, 1, ..., S-1 (fixed: repeated
+ * calls give identical bits).  Other shapes, or a workspace too small for two
+ * segments, run the unsplit kernels.
+ *
+ *   Arguments as fp8q_gemm_blockscale (all three granularities), plus
+ *   workspace  device memory for S * M * N fp32 partials (4-byte aligned),
+ *              owned by the caller, contents ignored and overwritten; NULL
+ *              with workspace_bytes 0 means: never split.
+ * fp8q_gemm_splitk_workspace_size returns the bytes the current device's
+ * split choice uses for an M x N x K problem (0: it would not split).
+ */
+size_t fp8q_gemm_splitk_workspace_size(int64_t M, int64_t N, int64_t K);
+fp8q_status_t fp8q_gemm_blockscale_splitk(const uint8_t* a, int64_t lda, const float* a_scales,
+                                          int32_t a_layout, const uint8_t* w, int64_t ldw,
+                                          const float* w_scale_inv, const uint16_t* bias,
+                                          uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                                          int32_t gran, void* workspace, size_t workspace_bytes,
+                                          void* stream);
 
 /*
  * fp8q_gemm_grouped_blockscale -- MoE expert GEMMs over expert-sorted rows.

@@ -144,6 +144,17 @@ def test_requant_weight_pow2_validation(lib):
     assert f(A, 256, C, 256, 256, Q2, 256, ctypes.c_void_p(0x100000), None) == 7        # s_out over q_in
 
 
+def test_gemm_splitk_validation(lib):
+    f = lib.fp8q_gemm_blockscale_splitk
+    W = ctypes.c_void_p(0x800000)
+    assert f(A, 128, C, 0, B, 128, C, None, C, 256, -1, 256, 128, 0, W, 1 << 20, None) == 2
+    assert f(A, 128, C, 0, B, 128, C, None, C, 256, 4, 256, 128, 5, W, 1 << 20, None) == 3
+    assert f(A, 128, C, 0, B, 128, C, None, C, 256, 4, 256, 128, 0, None, 64, None) == 1   # bytes, no buffer
+    assert f(A, 128, C, 0, B, 128, C, None, C, 256, 4, 256, 128, 0, ctypes.c_void_p(0x800002), 64, None) == 4
+    assert f(A, 128, C, 0, B, 128, C, None, C, 256, 0, 256, 128, 0, W, 64, None) == 0      # M == 0
+    assert lib.fp8q_gemm_splitk_workspace_size(0, 256, 128) == 0
+
+
 def test_gemm_grouped_validation(lib):
     f = lib.fp8q_gemm_grouped_blockscale
     O = ctypes.c_void_p(0x600000)
@@ -219,6 +230,8 @@ def test_device_check_without_gpu(lib):
     assert lib.fp8q_quant_weight_block(A, 256, 256, 256, 128, 128, 2, B, 256, C, None) == 5
     assert lib.fp8q_requant_weight_pow2(A, 256, C, 256, 256, A, 256, C, None) == 5          # in place
     assert lib.fp8q_gemm_blockscale(A, 128, C, 0, B, 128, C, None, C, 256, 4, 256, 128, 2, None) == 5
+    assert lib.fp8q_gemm_blockscale_splitk(A, 128, C, 0, B, 128, C, None, C, 256, 4, 256, 128, 0, None, 0, None) == 5
+    assert lib.fp8q_gemm_splitk_workspace_size(32, 2048, 7168) == 0          # no device: no split
     # the grouped GEMM with shards (and the power-of-two format)
     assert lib.fp8q_gemm_grouped_blockscale(A, 256, C, 1, ctypes.c_void_p(0x600000), 4, B, 256, 512 * 256, C, 256,
                                             ctypes.c_void_p(0x700000), 512, 100, 512, 256, 2, None) == 5

@@ -1,0 +1,105 @@
+"""GPU parity of the split-K GEMM entry point (fp32 partial sums per K
+segment, added in segment order by a second kernel): decode shapes whose
+column tiles leave CUs idle, all three scale granularities, ragged M and N,
+against the oracle (the method's per-row bound); repeated calls give the
+same bits; a workspace too small for two segments, and shapes the split does
+not serve (M > 64, or K below 96 blocks), give exactly the unsplit kernels'
+bits."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import bf16 as obf16
+from oracle import gemm as og
+from oracle import quant as oq
+from tests.gpu_helpers import CANARY_BF16, bf16_bits, bf16_host, canary_intact, check_gemm_rows, log, padded
+
+pytestmark = pytest.mark.gpu
+
+REL = 1e-2
+# the split serves K >= 12288 (96 blocks); (5, 300, 4096) runs unsplit
+SHAPES = [(1, 2048, 14336), (16, 1024, 16384), (32, 4096, 12288), (64, 2048, 14336), (33, 1000, 12800), (5, 300, 4096)]
+
+
+def fq():
+    import fp8_block_scaled_token_amd as m
+    return m
+
+
+def _dev_u8(a, K):
+    ld = -(-K // 16) * 16 + 16
+    buf = torch.zeros(a.shape[0], ld, dtype=torch.uint8, device="cuda")
+    buf[:, :K] = torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    return buf[:, :K]
+
+
+def _operands(M, N, K, gran, seed):
+    m = fq()
+    x = bf16_host(workloads.activations(M, K, seed, 0.001))
+    w = bf16_host(workloads.weights(N, K, seed + 1))
+    if gran == m.GRAN_PER_TENSOR:
+        sx = np.float32(np.float32(np.abs(x).max()) / np.float32(448.0))
+        qa = oq.quant_static(x, sx)
+        qw, sw = oq.quant_tensor(w)
+        sa, sw = np.array([sx], np.float32), np.array([sw], np.float32)
+        ref = lambda: og.gemm_pertensor(qa, sx, qw, sw[0])[0]
+    elif gran == m.GRAN_BLOCK128_POW2:
+        qa, sa = oq.quant_group_pow2(x)
+        qw, sw = oq.requant_weight_pow2(*oq.quant_weight_block(w))
+        ref = lambda: og.gemm_blockscale(qa, sa, qw, sw)[0]
+    else:
+        qa, sa = oq.quant_group(x)
+        qw, sw = oq.quant_weight_block(w)
+        ref = lambda: og.gemm_blockscale(qa, sa, qw, sw)[0]
+    return qa, sa, qw, sw, ref
+
+
+def _call(qa, sa, qw, sw, gran, ws):
+    m = fq()
+    M, K = qa.shape
+    N = qw.shape[0]
+    yb, y = padded(M, N, torch.bfloat16, 8, CANARY_BF16)
+    m.fp8q_gemm_blockscale_splitk(_dev_u8(qa, K), torch.from_numpy(sa).cuda(), 0, _dev_u8(qw, K),
+                                  torch.from_numpy(np.ascontiguousarray(sw)).cuda(), None, y, gran, ws)
+    torch.cuda.synchronize()
+    assert canary_intact(yb, N, CANARY_BF16)
+    return bf16_bits(y)
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+@pytest.mark.parametrize("gran", [0, 1, 2])
+def test_splitk_parity(M, N, K, gran):
+    m = fq()
+    nbytes = m.fp8q_gemm_splitk_workspace_size(M, N, K)
+    log(f"splitk M={M} N={N} K={K} gran={gran} workspace={nbytes}")
+    if (M, N, K) != (5, 300, 4096):
+        assert nbytes > 0, "these shapes leave CUs idle without a split"
+    ws = torch.full((max(nbytes, 4) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    qa, sa, qw, sw, ref = _operands(M, N, K, gran, M + N + K + gran)
+    y = _call(qa, sa, qw, sw, gran, ws)
+    check_gemm_rows(y, ref(), f"splitk M={M} N={N} K={K} gran={gran}", REL)
+    np.testing.assert_array_equal(_call(qa, sa, qw, sw, gran, ws), y)      # fixed reduction order
+
+
+def test_splitk_small_workspace_and_other_shapes_run_unsplit():
+    m = fq()
+    for (M, N, K, ws_elems) in [(16, 1024, 16384, 16 * 1024), (200, 1024, 2048, 1 << 22), (32, 2048, 7168, 1 << 22)]:
+        qa, sa, qw, sw, _ = _operands(M, N, K, 0, 7)
+        ws = torch.zeros(ws_elems, dtype=torch.float32, device="cuda")    # one segment at most
+        y = _call(qa, sa, qw, sw, 0, ws)
+        ref = bf16_bits(m.gemm_blockscale(_dev_u8(qa, K), torch.from_numpy(sa).cuda(), _dev_u8(qw, K),
+                                          torch.from_numpy(sw).cuda()))
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(y, ref)
+
+
+def test_splitk_decode_workload_full_size():
+    # the decode workload's row count with a narrow, long weight (N 2048, K 28672)
+    m = fq()
+    M, N, K = 32, 2048, 28672
+    qa, sa, qw, sw, ref = _operands(M, N, K, 0, 99)
+    nbytes = m.fp8q_gemm_splitk_workspace_size(M, N, K)
+    ws = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    y = _call(qa, sa, qw, sw, 0, ws)
+    check_gemm_rows(y, ref(), "splitk 32x2048x7168", REL)
