@@ -6,7 +6,8 @@ activations already resident in HBM: the activation quantizer (fused with
 RMSNorm for the prefill-with-norm workload, and with the residual add in front
 of it for the add-norm workload, which updates the stream in place) followed
 by the scaled GEMM (`*_pow2` workloads: the same with power-of-two scales
--- block FP8 as an MXFP8 view -- applied inside the MFMA; `moe_*`: the
+-- block FP8 as an MXFP8 view -- applied inside the MFMA; `decode_splitk`:
+the split-K entry point with its workspace; `moe_*`: the
 expert-sorted rows of one GPU's share of a MoE layer through the grouped
 GEMM).  The
 weight is quantized once before timing (it is offline preparation).  Inputs
@@ -49,7 +50,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="prefill_norm",
                     choices=["tiny", "decode", "prefill_norm", "prefill_addnorm", "large", "mx", "pertensor",
-                             "prefill_norm_pow2", "large_pow2", "moe_up", "moe_down"])
+                             "prefill_norm_pow2", "large_pow2", "moe_up", "moe_down", "decode_splitk"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample (0 = skip)")
     return ap.parse_args()
@@ -165,8 +166,15 @@ def main() -> int:
         else:
             fq.fp8q_quant_act_group(s["x"], 128, fq.SCALE_F32, fq.COL_MAJOR, None, s["q"], s["s"])
 
+    ws = None
+    if name == "decode_splitk":
+        ws = torch.empty(max(fq.fp8q_gemm_splitk_workspace_size(M, N, K), 4) // 4, dtype=torch.float32,
+                         device="cuda")
+
     def gemm(s):
-        if name == "mx":
+        if name == "decode_splitk":
+            fq.fp8q_gemm_blockscale_splitk(s["q"], s["s"], fq.COL_MAJOR, qw, sw, None, s["y"], fq.GRAN_BLOCK128, ws)
+        elif name == "mx":
             fq.fp8q_gemm_mxfp8(s["q"], s["s"], qw, sw, None, s["y"])
         elif name == "pertensor":
             fq.fp8q_gemm_blockscale(s["q"], s["s"], fq.ROW_MAJOR, qw, sw, None, s["y"], fq.GRAN_PER_TENSOR)

@@ -126,6 +126,8 @@ WORKLOADS = {
                                 outlier_frac=0.001, norm=True, residual=True),
     # large prefill: A [8192,7168] with outliers, W [18432,7168]
     "large": Workload("large", 8192, 18432, 7168, seed=3, outlier_frac=0.001),
+    # narrow, long weight at decode batch size (the split-K case): A [32,28672], W [2048,28672]
+    "decode_splitk": Workload("decode_splitk", 32, 2048, 28672, seed=5, outlier_frac=0.001),
     # MXFP8 / per-tensor: A [2048,7168], W [7168,7168], both N(0,1)
     "mx": Workload("mx", 2048, 7168, 7168, seed=4, w_std=1.0, mx=True),
 }
