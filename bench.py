@@ -166,14 +166,19 @@ def main() -> int:
         else:
             fq.fp8q_quant_act_group(s["x"], 128, fq.SCALE_F32, fq.COL_MAJOR, None, s["q"], s["s"])
 
+    # the split entry with its workspace (allocated once by the caller):
+    # decode shapes that leave CUs idle split K; prefill shapes split the
+    # leftover tiles of their last round along K
     ws = None
-    if name == "decode_splitk":
-        ws = torch.empty(max(fq.fp8q_gemm_splitk_workspace_size(M, N, K), 4) // 4, dtype=torch.float32,
-                         device="cuda")
+    ws_bytes = fq.fp8q_gemm_splitk_workspace_size(M, N, K) if name != "mx" else 0
+    if ws_bytes:
+        ws = torch.empty(ws_bytes // 4, dtype=torch.float32, device="cuda")
 
     def gemm(s):
-        if name == "decode_splitk":
-            fq.fp8q_gemm_blockscale_splitk(s["q"], s["s"], fq.COL_MAJOR, qw, sw, None, s["y"], fq.GRAN_BLOCK128, ws)
+        if ws is not None:
+            gran = {"pertensor": fq.GRAN_PER_TENSOR}.get(name, fq.GRAN_BLOCK128_POW2 if pow2 else fq.GRAN_BLOCK128)
+            layout = fq.ROW_MAJOR if name == "pertensor" else fq.COL_MAJOR
+            fq.fp8q_gemm_blockscale_splitk(s["q"], s["s"], layout, qw, sw, None, s["y"], gran, ws)
         elif name == "mx":
             fq.fp8q_gemm_mxfp8(s["q"], s["s"], qw, sw, None, s["y"])
         elif name == "pertensor":
@@ -261,7 +266,7 @@ def main() -> int:
         "config": {"workload": name, "M": M, "N": N, "K": K, "norm": wl.norm, "residual_add": wl.residual,
                    "scales": {"mx": "1x32 ue8m0", "pertensor": "per-tensor fp32"}.get(
                        name, "group128 + 128x128 power-of-two fp32 (in-MFMA)" if pow2 else "group128 + 128x128 fp32"),
-                   "rotating_buffer_sets": nsets},
+                   "rotating_buffer_sets": nsets, "splitk_workspace_bytes": ws_bytes},
         "roofline": roof,
         "gemm": {"us": round(gemm_ms * 1e3, 2), "TFLOP/s": round(gemm_tflops, 1),
                  "frac_fp8_peak": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "GB/s": round(gemm_gbps, 1),

@@ -18,6 +18,7 @@ constexpr float kAmaxFloor = 1e-10f;
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------- bf16 <-> f32
 

@@ -39,7 +39,9 @@ struct GemmArgs {
   int shard;            // stacked weight shards of `shard` rows each (0: one shard), see below
   int shard_blocks;     // ceil(shard / 128)
   int split_kb;         // split-K: K blocks per split (0: no split); split s = blockIdx.y
-  float* partial;       // split-K: fp32 partial sums [splits][M][N] (row stride N)
+  float* partial;       // split-K: fp32 partial sums [splits][M][N] (row stride N); split
+                        // tail tiles: 256 KB per leftover tile, then a flag word each
+  uint32_t nonce;       // split tail tiles: this launch's flag value
 };
 
 // Weight scale row of output channel j: j / 128, or with stacked shards
@@ -121,6 +123,10 @@ __device__ __forceinline__ void store_tile_bf16(const GemmArgs& p, const v4f& ac
 
 // Fast prefill path (gemm_fast.hip): shapes it accepts, and its launcher.
 bool gemm_fast_eligible(const GemmArgs& p, int mode);
+// With p.partial set (at least gemm_fast_tail_workspace(p) bytes), the
+// leftover tiles of the last round are split along K between two
+// workgroups instead of into half-height tiles.
+size_t gemm_fast_tail_workspace(const GemmArgs& p);
 hipError_t launch_gemm_fast(GemmArgs p, int mode, hipStream_t stream);
 
 // Grouped (MoE) path on the fast kernel's tiles: expert-sorted rows,

@@ -39,6 +39,8 @@
 #include <cstdlib>
 #include <utility>
 
+#include <atomic>
+
 #include "dma.h"
 #include "gemm_common.h"
 #include "launch.h"
@@ -101,9 +103,29 @@ struct FastTile {
 // first K block (and its touches) before its epilogue.  `has_next`: issue the
 // first K block of the next tile (nm0, nn0, ngm, ngn; same kind) before this
 // tile's epilogue, so that its latency overlaps the output stores.
+// K range of a tile and, for the two K halves of a split tail tile, how the
+// halves meet: the producer stores its fp32 accumulators to `part` and raises
+// `flag` to `nonce`; the consumer waits for that (bounded), adds the partial
+// as first half + second half (a fixed order whichever workgroup consumes)
+// and writes the output.
+// Cache policy bits of a buffer access (SC0 | SC1): system scope, i.e. a
+// store writes through to memory and a load misses the caches.
+constexpr int kCacheSystem = 1 | 16;
+
+struct TileK {
+  int kb0, kb1;        // K blocks [kb0, kb1)
+  int next_kb0;        // first K block of the next tile (issued early when has_next)
+  int role;            // 0: whole tile, 1: producer, 2: consumer
+  int first;           // this workgroup holds the first K half
+  float* part;         // 256 KB slot of the pair
+  uint32_t* flag;
+  uint32_t nonce;
+};
+
 template <class T, bool HALF>
 __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int m0, int n0, int gm, int gn,
-                                          bool preloaded, bool has_next, int nm0, int nn0, int ngm, int ngn) {
+                                          bool preloaded, bool has_next, int nm0, int nn0, int ngm, int ngn,
+                                          const TileK& tk) {
   constexpr int MODE = T::MODE, BM = T::BM, BN = T::BN, WN = T::WN, NW = T::NW;
   constexpr bool FP32S = T::FP32S;
   constexpr int RM = HALF ? T::BM / 2 : T::BM;
@@ -210,7 +232,7 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
   // Past the last block the descriptors cover nothing: the loads are still
   // issued (every block issues the same number) but read nothing and write
   // zeros into this wave's sink.
-  const int KB = p.KB;
+  const int KB = tk.kb1;                     // loads of blocks at or past it read nothing
   constexpr int NLD = A_PER + W_PER + T::SCALE_LOADS;
   auto issue_load = [&](auto L, int st, int kb, const Offs& o) {
     constexpr int l = decltype(L)::value;
@@ -237,7 +259,7 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
   // issued after the operand loads of a step and may stay in flight until
   // the next step's wait.
   auto prefetch = [&](int kb, const Offs& o) {
-    const bool valid = PFD > 0 && kb < p.KB;
+    const bool valid = PFD > 0 && kb < KB;
     i32x4 ra = rA, rw = rW;
     ra.z = valid ? ra.z : 0;
     rw.z = valid ? rw.z : 0;
@@ -397,18 +419,19 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
     static_for<NLD>([&](auto L) { issue_load(L, st, kb, o); });
     prefetch(kb + PFD - 1, o);
   };
+  const int kb0 = tk.kb0;
   if (preloaded) {
-    // block 0 was issued before the previous tile's output stores: wait for
-    // everything (the stores have had the loads' latency to drain)
+    // block kb0 was issued before the previous tile's output stores: wait
+    // for everything (the stores have had the loads' latency to drain)
     wait_vmcnt_barrier<0>();
   } else {
-    issue_all(0, 0, cur);
+    issue_all(0, kb0, cur);
     wait_vmcnt_barrier<2>();
   }
-  static_for<SLOTS>([&](auto S) { if constexpr (decltype(S)::value == 0) issue_slot(S, 1, 1); });
+  static_for<SLOTS>([&](auto S) { if constexpr (decltype(S)::value == 0) issue_slot(S, 1, kb0 + 1); });
   load_regs(0);
-  for (int kb = 0; kb < KB; ++kb) {
-    const int st = kb & 1;
+  for (int kb = kb0; kb < KB; ++kb) {
+    const int st = (kb - kb0) & 1;
     static_for<TM>([&](auto I) {
       constexpr int i = decltype(I)::value;
       // the rest of block kb + 1's loads (its slot 0 was issued at the
@@ -433,12 +456,58 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
   if (has_next) {
     int ln = lane;
     asm volatile("" : "+v"(ln));
-    issue_all(0, 0, make_offs(nm0, nn0, ngm, ngn, ln));
+    issue_all(0, tk.next_kb0, make_offs(nm0, nn0, ngm, ngn, ln));
   }
   if constexpr (MODE == MODE_BLOCK) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) fold_one(std::integral_constant<int, TM - 1>{}, j);
   }
+
+  // Split tail tile: the two K halves meet here.  Partial layout: float4
+  // ((wave * TM + i) * TN + j) * 64 + lane, i.e. every store and load of a
+  // wave is 1 KB contiguous.
+  // The accumulators are not modified here (an update inside a branch made
+  // the register allocator keep two copies of them): the partner's partial
+  // is added in the epilogue, to every tile (-0, an identity, outside the
+  // consumer).
+  const bool producer = tk.role == 1, consumer = tk.role == 2;
+  const int vo = (wave * TM * TN * 64 + lane) * 16;
+  int m_end = p.m_end;
+  if (tk.role != 0) {
+    // The partial and the flag are written through to memory (system-scope
+    // cache policy) and read back with loads that miss the caches, so the
+    // two workgroups (on different XCDs, whose L2s are not coherent) meet
+    // without an L2 write-back.  Every wave waits for its own stores to
+    // complete before the barrier; thread 0 raises the flag after it.
+    if (producer) {
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(tk.part, 0, T::BM * T::BN * 4, 0x00020000);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), rs, vo, (i * TN + j) * 1024,
+                                                 kCacheSystem);
+      wait_vmcnt<0>();
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      if (producer) {
+        __hip_atomic_store(tk.flag, tk.nonce, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      } else {
+        // bounded wait: the producer runs in the same round and never waits
+        // itself; past the limit the tile is finished without its partner
+        for (int n = 0; n < (1 << 22); ++n) {
+          if (__hip_atomic_load(tk.flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == tk.nonce) break;
+          __builtin_amdgcn_s_sleep(2);
+        }
+      }
+    }
+    __syncthreads();
+    if (producer) m_end = 0;              // the consumer writes the output
+  }
+  // the consumer's partner partial, read in the epilogue one 16-row tile at
+  // a time; -0 is added instead elsewhere
+  const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(tk.part, 0, T::BM * T::BN * 4, 0x00020000);
 
   // Epilogue.  After the MFMAs, lane (r16, q) = (lane % 16, lane / 16) holds
   // for column tile j the four columns 16j + 4q + 0..3 of row r16 (+16i).
@@ -462,6 +531,18 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
   const int col0 = n0 + wn * WTN + 16 * lq;           // this lane's columns after the exchange
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
+    // split tail tile: first K half + second K half
+    // (loads only in the consumer: an issued load, even one reading
+    // nothing, would make this wait for the next tile's loads in flight)
+    v4f o[TN];
+    if (consumer) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        o[j] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rl, vo, (i * TN + j) * 1024, kCacheSystem));
+    } else {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) o[j] = v4f{-0.f, -0.f, -0.f, -0.f};
+    }
     // D[j][h]: bf16 pair h (columns 16j + 4q + 2h, +1) of column tile j
     uint32_t d[TN][2];
 #pragma unroll
@@ -469,7 +550,7 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
       float v[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        v[r] = acc[i][j][r];
+        v[r] = tk.first ? acc[i][j][r] + o[j][r] : o[j][r] + acc[i][j][r];
         if (MODE == MODE_TENSOR) v[r] = v[r] * mul;
         v[r] = v[r] + bias[j][r];
       }
@@ -492,7 +573,7 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
       e[3][h] = t23[1];
     }
     const int row = m0 + wm * WTM + 16 * i + l16;
-    if (row >= p.m_end) continue;
+    if (row >= m_end) continue;
     uint16_t* yr = p.y + (int64_t)row * p.ldy;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -512,43 +593,74 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
 
 // Work items [0, full) are whole tiles (in XCD-contiguous group order); the
 // remaining tiles of that order are split into two half-height tiles, items
-// [full, items).  The kernel is persistent: workgroup g takes items g,
-// g + G, g + 2G, ... (G = gridDim.x, at most one workgroup per slot), so the
-// workgroups of a round start together and keep their XCD (item % 8), and no
-// workgroup is launched per tile.  Between two tiles no barrier is needed: a
-// wave issues the next tile's first LDS writes only after the last K-loop
-// barrier of the previous tile, after which nobody reads a stage, and the
-// next tile's first barrier waits for every wave.
+// [full, items) -- or, with `ksplit` (a workspace in p.partial), into their
+// two K halves: items full + 2t and full + 2t + 1 are the first and second
+// K half of leftover tile t, and the workgroup with the lower index of the
+// pair hands its partial sums to the other (see TileK).  The kernel is
+// persistent: workgroup g takes items g, g + G, g + 2G, ... (G = gridDim.x,
+// at most one workgroup per slot), so the workgroups of a round start
+// together and keep their XCD (item % 8), and no workgroup is launched per
+// tile.  Between two tiles no barrier is needed: a wave issues the next
+// tile's first LDS writes only after the last K-loop barrier of the previous
+// tile, after which nobody reads a stage, and the next tile's first barrier
+// waits for every wave.  A split pair's items are the last of their
+// workgroups (the tail is one round), and the lower-index workgroup of a
+// pair never waits, so the waits cannot form a cycle.
 template <class T>
-__global__ __launch_bounds__(T::NW * 64) void gemm_fast_kernel(GemmArgs p, int full, int items) {
+__global__ __launch_bounds__(T::NW * 64) void gemm_fast_kernel(GemmArgs p, int full, int items, int ksplit) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES];
   const int total = p.tiles_m * p.tiles_n;
-  // item -> tile origin and prefetch group coordinates; true for a half tile
+  const int G = gridDim.x;
+  // item -> tile origin and prefetch group coordinates; the kind: 0 whole
+  // tile, 1 half-height tile, 2 K half
   auto decode = [&](int x, int& m0, int& n0, int& gm, int& gn) {
-    int tm, tn;
+    int tm, tn, kind = 0;
     if (x < full) {
       group_walk(xcd_contiguous(x, full), p.tiles_m, p.tiles_n, tm, tn);
       m0 = tm * T::BM;
+    } else if (ksplit) {
+      group_walk(full + ((x - full) >> 1), p.tiles_m, p.tiles_n, tm, tn);
+      m0 = tm * T::BM;
+      kind = 2;
     } else {
       const int h = xcd_contiguous(x - full, 2 * (total - full));
       group_walk(full + (h >> 1), p.tiles_m, p.tiles_n, tm, tn);
       m0 = tm * T::BM + (h & 1) * (T::BM / 2);
+      kind = 1;
     }
     n0 = tn * T::BN;
     gm = tm % 8;
     gn = tn % T::NTN;
-    return x >= full;
+    return kind;
   };
+  const int half_kb = p.KB / 2;
+  const int tails = (items - full) / 2;
   bool preloaded = false;
-  for (int b = blockIdx.x; b < items; b += gridDim.x) {
+  for (int b = blockIdx.x; b < items; b += G) {
     int m0, n0, gm, gn, nm0 = 0, nn0 = 0, ngm = 0, ngn = 0;
-    const bool half = decode(b, m0, n0, gm, gn);
-    const int nb = b + gridDim.x;
-    const bool has_next = nb < items && decode(nb, nm0, nn0, ngm, ngn) == half;
-    if (!half)
-      fast_tile<T, false>(p, smem, m0, n0, gm, gn, preloaded, has_next, nm0, nn0, ngm, ngn);
+    const int kind = decode(b, m0, n0, gm, gn);
+    const int nb = b + G;
+    // the next tile's first block is issued early between tiles of one
+    // kind, and from a whole tile to a K half (at that half's first block)
+    const int nkind = nb < items ? decode(nb, nm0, nn0, ngm, ngn) : -1;
+    const bool has_next = nkind >= 0 && (nkind == kind || (kind == 0 && nkind == 2));
+    TileK tk{0, p.KB, 0, 0, 0, nullptr, nullptr, 0u};
+    if (nkind == 2) tk.next_kb0 = ((nb - full) & 1) ? half_kb : 0;
+    if (kind == 2) {
+      const int t = (b - full) >> 1, second = (b - full) & 1;
+      const int partner = second ? b - 1 : b + 1;
+      tk.kb0 = second ? half_kb : 0;
+      tk.kb1 = second ? p.KB : half_kb;
+      tk.first = !second;
+      tk.role = (int)blockIdx.x < partner % G ? 1 : 2;
+      tk.part = p.partial + (int64_t)t * (T::BM * T::BN);
+      tk.flag = reinterpret_cast<uint32_t*>(p.partial + (int64_t)tails * (T::BM * T::BN)) + t;
+      tk.nonce = p.nonce;
+    }
+    if (kind == 1)
+      fast_tile<T, true>(p, smem, m0, n0, gm, gn, preloaded, has_next, nm0, nn0, ngm, ngn, tk);
     else
-      fast_tile<T, true>(p, smem, m0, n0, gm, gn, preloaded, has_next, nm0, nn0, ngm, ngn);
+      fast_tile<T, false>(p, smem, m0, n0, gm, gn, preloaded, has_next, nm0, nn0, ngm, ngn, tk);
     preloaded = has_next;
   }
   // the last touches and past-the-end loads still write the LDS sink: let
@@ -641,7 +753,8 @@ __global__ __launch_bounds__(T::NW * 64) void gemm_grouped_kernel(GemmArgs p, Gr
     pe.w = p.w + e * g.w_stride;
     pe.sw = static_cast<const float*>(p.sw) + e * g.sw_stride;
     pe.m_end = __builtin_amdgcn_readfirstlane(row_end(e));
-    fast_tile<T, false>(pe, smem, m0, n0, gm, gn, preloaded, has_next, nm0, nn0, ngm, ngn);
+    const TileK tk{0, p.KB, 0, 0, 0, nullptr, nullptr, 0u};
+    fast_tile<T, false>(pe, smem, m0, n0, gm, gn, preloaded, has_next, nm0, nn0, ngm, ngn, tk);
     preloaded = has_next;
   }
   wait_vmcnt<0>();
@@ -708,6 +821,19 @@ Plan choose_plan(const GemmArgs& p) {
   return plan_cost(big, cus) <= plan_cost(small, cus) ? big : small;
 }
 
+// Workspace of the split tail (configuration 0 only): 256 x 256 fp32 per
+// leftover tile, then one flag word each; 0 when the plan has no tail, or
+// when K is below 32 blocks: the exchange of a 256 KB partial costs about
+// what half of a short K loop saves (measured: 4096x6144x6144 158 -> 146 us,
+// 2560x7168x2048 55 -> 58 us).
+size_t tail_workspace(const Plan& pl, const GemmArgs& p) {
+  const int tail = pl.tiles_m * pl.tiles_n - pl.full;
+  if (pl.cfg != 0 || tail <= 0 || p.KB < 32) return 0;
+  return (size_t)tail * (256u * 256u * 4u + 4u);
+}
+
+std::atomic<uint32_t> g_nonce{0};
+
 template <int MODE>
 void launch_plan(GemmArgs p, const Plan& pl, hipStream_t stream) {
   p.tiles_m = pl.tiles_m;
@@ -716,12 +842,20 @@ void launch_plan(GemmArgs p, const Plan& pl, hipStream_t stream) {
   // workgroup per CU, configuration 1 two), never more than the items
   const int slots = (pl.cfg == 0 ? 1 : 2) * cu_count();
   const int grid = pl.grid < slots ? pl.grid : slots;
+  // with a workspace, the leftover tiles are split along K instead of in
+  // half-height tiles; a fresh nonce per launch marks its flags
+  const int ksplit = p.partial != nullptr && tail_workspace(pl, p) > 0;
+  if (ksplit) {
+    uint32_t n = ++g_nonce;
+    if (n == 0) n = ++g_nonce;
+    p.nonce = n;
+  }
   if (pl.cfg == 0) {
     using T = FastTile<MODE, 256, 256, 2, 4, 4>;
-    hipLaunchKernelGGL(gemm_fast_kernel<T>, dim3(grid), dim3(T::NW * 64), 0, stream, p, pl.full, pl.grid);
+    hipLaunchKernelGGL(gemm_fast_kernel<T>, dim3(grid), dim3(T::NW * 64), 0, stream, p, pl.full, pl.grid, ksplit);
   } else {
     using T = FastTile<MODE, 128, 128, 2, 2, 8>;
-    hipLaunchKernelGGL(gemm_fast_kernel<T>, dim3(grid), dim3(T::NW * 64), 0, stream, p, pl.full, pl.grid);
+    hipLaunchKernelGGL(gemm_fast_kernel<T>, dim3(grid), dim3(T::NW * 64), 0, stream, p, pl.full, pl.grid, 0);
   }
 }
 
@@ -773,6 +907,8 @@ hipError_t launch_gemm_grouped(GemmArgs p, const int32_t* offsets, int E, int64_
 #undef FP8Q_GROUPED
   return hipGetLastError();
 }
+
+size_t gemm_fast_tail_workspace(const GemmArgs& p) { return tail_workspace(choose_plan(p), p); }
 
 hipError_t launch_gemm_fast(GemmArgs p, int mode, hipStream_t stream) {
   const Plan pl = choose_plan(p);

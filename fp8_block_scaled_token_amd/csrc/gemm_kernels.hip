@@ -406,8 +406,9 @@ GemmArgs block_args(const uint8_t* a, int64_t lda, const float* sa, int sa_col_m
 }  // namespace
 
 size_t gemm_splitk_workspace(int64_t M, int64_t N, int64_t K) {
-  if (M < 1 || M > 64 || N < 1 || K < 1) return 0;
+  if (M < 1 || N < 1 || K < 1) return 0;
   const GemmArgs p = block_args(nullptr, K, nullptr, 0, nullptr, K, nullptr, nullptr, nullptr, N, M, N, K);
+  if (M > 64) return gemm_fast_eligible(p, MODE_BLOCK) ? gemm_fast_tail_workspace(p) : 0u;
   const int s = decode_splits(p);
   return s > 1 ? (size_t)s * (size_t)M * (size_t)N * 4u : 0u;
 }
@@ -417,6 +418,14 @@ hipError_t launch_gemm_blockscale_splitk(const uint8_t* a, int64_t lda, const fl
                                          uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K, int gran,
                                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
   GemmArgs p = block_args(a, lda, sa, sa_col_major, w, ldw, sw, bias, y, ldy, M, N, K);
+  if (p.M > 64 && workspace != nullptr && gemm_fast_eligible(p, MODE_BLOCK)) {
+    // prefill: the last round's leftover tiles split along K
+    const size_t need = gemm_fast_tail_workspace(p);
+    if (need > 0 && workspace_bytes >= need) {
+      p.partial = static_cast<float*>(workspace);
+      return launch_gemm_fast(p, gran == 1 ? MODE_TENSOR : gran == 2 ? MODE_BMX : MODE_BLOCK, stream);
+    }
+  }
   if (p.M <= 64 && workspace != nullptr && gemm_decode_eligible(p)) {
     int s = decode_splits(p);
     const int64_t fit = (int64_t)(workspace_bytes / ((size_t)M * (size_t)N * 4u));

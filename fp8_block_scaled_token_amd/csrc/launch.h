@@ -45,8 +45,9 @@ hipError_t launch_gemm_blockscale(const uint8_t* a, int64_t lda, const float* sa
                                   const uint16_t* bias, uint16_t* y, int64_t ldy, int64_t M,
                                   int64_t N, int64_t K, int gran, hipStream_t stream);
 // Split-K variant of launch_gemm_blockscale: fp32 partials in `workspace`
-// (decode shapes whose column tiles leave CUs idle); otherwise, or when the
-// workspace is too small for two splits, the unsplit kernels.
+// (decode shapes whose column tiles leave CUs idle, and the leftover tiles
+// of a prefill GEMM's last round); otherwise, or when the workspace is too
+// small, the unsplit kernels.
 size_t gemm_splitk_workspace(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_blockscale_splitk(const uint8_t* a, int64_t lda, const float* sa, int sa_col_major,
                                          const uint8_t* w, int64_t ldw, const float* sw, const uint16_t* bias,

@@ -253,11 +253,17 @@ fp8q_status_t fp8q_gemm_blockscale(const uint8_t* a, int64_t lda, const float* a
  * reduction kernel adds them; this changes the order of the floating-point
  * additions, so the result is not bit-identical to the single-accumulator
  * kernel (it is the same formula, within the same bound).  Here the split
- * serves decode shapes (M <= 64, K >= 12288) whose column tiles alone leave
- * compute units idle: each of S segments streams its share of the weight on
- * otherwise idle CUs; the partials are added in segment order 0, 1, ..., S-1 (fixed: repeated
- * calls give identical bits).  Other shapes, or a workspace too small for two
- * segments, run the unsplit kernels.
+ * serves two cases, both where whole tiles leave compute units idle:
+ *  - decode shapes (M <= 64, K >= 12288): each of S segments streams its
+ *    share of the weight on otherwise idle CUs; a second kernel adds the
+ *    partials in segment order 0, 1, ..., S-1;
+ *  - prefill shapes whose last round of 256 x 256 tiles is at most half
+ *    full: each leftover tile is computed as two K halves by two workgroups,
+ *    one of which adds the other's fp32 partial (first half + second half)
+ *    before the epilogue (it waits for it, bounded; the other never waits).
+ * Both orders are fixed: repeated calls give identical bits.  Other shapes,
+ * or a workspace too small, run the unsplit kernels (a prefill launch keeps
+ * a launch counter for the flags it leaves in the workspace).
  *
  *   Arguments as fp8q_gemm_blockscale (all three granularities), plus
  *   workspace  device memory for S * M * N fp32 partials (4-byte aligned),

@@ -84,7 +84,8 @@ def test_splitk_parity(M, N, K, gran):
 
 def test_splitk_small_workspace_and_other_shapes_run_unsplit():
     m = fq()
-    for (M, N, K, ws_elems) in [(16, 1024, 16384, 16 * 1024), (200, 1024, 2048, 1 << 22), (32, 2048, 7168, 1 << 22)]:
+    for (M, N, K, ws_elems) in [(16, 1024, 16384, 16 * 1024), (200, 1024, 2048, 1 << 22), (32, 2048, 7168, 1 << 22),
+                                (2304, 8192, 2048, 1 << 24), (2304, 8192, 4096, 1 << 10)]:
         qa, sa, qw, sw, _ = _operands(M, N, K, 0, 7)
         ws = torch.zeros(ws_elems, dtype=torch.float32, device="cuda")    # one segment at most
         y = _call(qa, sa, qw, sw, 0, ws)
@@ -103,3 +104,30 @@ def test_splitk_decode_workload_full_size():
     ws = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
     y = _call(qa, sa, qw, sw, 0, ws)
     check_gemm_rows(y, ref(), "splitk 32x2048x7168", REL)
+
+
+# Prefill shapes whose last round of 256 x 256 tiles is at most half full
+# (more tiles than the 256 CUs): the leftover tiles run as two K halves
+# (odd block counts included) that meet in the workspace.
+# (at least 32 K blocks; 37 is odd)
+PREFILL = [(2304, 8192, 4096), (2304, 8192, 4736), (2560, 7168, 6144), (4096, 6144, 6144)]
+
+
+@pytest.mark.parametrize("M,N,K", PREFILL)
+@pytest.mark.parametrize("gran", [0, 1, 2])
+def test_prefill_tail_split_parity(M, N, K, gran):
+    m = fq()
+    nbytes = m.fp8q_gemm_splitk_workspace_size(M, N, K)
+    log(f"prefill tail split M={M} N={N} K={K} gran={gran} workspace={nbytes}")
+    assert nbytes > 0
+    ws = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    qa, sa, qw, sw, ref = _operands(M, N, K, gran, M + N + K + 3 * gran)
+    y = _call(qa, sa, qw, sw, gran, ws)
+    rows = np.unique(np.r_[0, M - 1, np.arange(M - 256, M, 37), np.random.default_rng(5).integers(0, M, 12)])
+    if gran == 1:
+        yr = og.gemm_pertensor(qa, sa[0], qw, sw[0], rows=rows)[0]
+    else:
+        yr = og.gemm_blockscale(qa, sa, qw, sw, rows=rows)[0]
+    check_gemm_rows(y[rows], yr, f"prefill split M={M} N={N} K={K}", REL)
+    # fixed order, and the flags of the previous launch do not confuse the next
+    np.testing.assert_array_equal(_call(qa, sa, qw, sw, gran, ws), y)
