@@ -122,7 +122,7 @@ struct TileK {
   uint32_t nonce;
 };
 
-template <class T, bool HALF>
+template <class T, bool HALF, bool SPLIT>
 __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int m0, int n0, int gm, int gn,
                                           bool preloaded, bool has_next, int nm0, int nn0, int ngm, int ngn,
                                           const TileK& tk) {
@@ -470,10 +470,12 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
   // the register allocator keep two copies of them): the partner's partial
   // is added in the epilogue, to every tile (-0, an identity, outside the
   // consumer).
-  const bool producer = tk.role == 1, consumer = tk.role == 2;
+  // (SPLIT: only the kernel that may split its tail carries this code, so
+  // the others keep their registers.)
+  const bool producer = SPLIT && tk.role == 1, consumer = SPLIT && tk.role == 2;
   const int vo = (wave * TM * TN * 64 + lane) * 16;
   int m_end = p.m_end;
-  if (tk.role != 0) {
+  if (SPLIT && tk.role != 0) {
     // The partial and the flag are written through to memory (system-scope
     // cache policy) and read back with loads that miss the caches, so the
     // two workgroups (on different XCDs, whose L2s are not coherent) meet
@@ -535,7 +537,10 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
     // (loads only in the consumer: an issued load, even one reading
     // nothing, would make this wait for the next tile's loads in flight)
     v4f o[TN];
-    if (consumer) {
+    if constexpr (!SPLIT) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) o[j] = v4f{-0.f, -0.f, -0.f, -0.f};
+    } else if (consumer) {
 #pragma unroll
       for (int j = 0; j < TN; ++j)
         o[j] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rl, vo, (i * TN + j) * 1024, kCacheSystem));
@@ -606,8 +611,9 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
 // waits for every wave.  A split pair's items are the last of their
 // workgroups (the tail is one round), and the lower-index workgroup of a
 // pair never waits, so the waits cannot form a cycle.
-template <class T>
-__global__ __launch_bounds__(T::NW * 64) void gemm_fast_kernel(GemmArgs p, int full, int items, int ksplit) {
+template <class T, bool KSPLIT>
+__global__ __launch_bounds__(T::NW * 64) void gemm_fast_kernel(GemmArgs p, int full, int items) {
+  constexpr bool ksplit = KSPLIT;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES];
   const int total = p.tiles_m * p.tiles_n;
   const int G = gridDim.x;
@@ -658,9 +664,9 @@ __global__ __launch_bounds__(T::NW * 64) void gemm_fast_kernel(GemmArgs p, int f
       tk.nonce = p.nonce;
     }
     if (kind == 1)
-      fast_tile<T, true>(p, smem, m0, n0, gm, gn, preloaded, has_next, nm0, nn0, ngm, ngn, tk);
+      fast_tile<T, true, KSPLIT>(p, smem, m0, n0, gm, gn, preloaded, has_next, nm0, nn0, ngm, ngn, tk);
     else
-      fast_tile<T, false>(p, smem, m0, n0, gm, gn, preloaded, has_next, nm0, nn0, ngm, ngn, tk);
+      fast_tile<T, false, KSPLIT>(p, smem, m0, n0, gm, gn, preloaded, has_next, nm0, nn0, ngm, ngn, tk);
     preloaded = has_next;
   }
   // the last touches and past-the-end loads still write the LDS sink: let
@@ -722,40 +728,56 @@ __global__ __launch_bounds__(T::NW * 64) void gemm_grouped_kernel(GemmArgs p, Gr
     __syncthreads();
   }
   const int items = __builtin_amdgcn_readfirstlane(tiles_before[E - 1]);
-  // item -> expert (first e with tiles_before[e] > x) and tile origin
+  // item -> expert (first e with tiles_before[e] > x), tile origin, and
+  // whether it is a half-height tile: an expert's last row tile holding at
+  // most BM/2 rows computes only those (it loads half the activation rows)
   auto decode = [&](int x, int& e, int& m0, int& n0, int& gm, int& gn) {
-    int lo = 0, hi = E - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (__builtin_amdgcn_readfirstlane(tiles_before[mid]) > x) hi = mid;
-      else lo = mid + 1;
+    // branch-free binary search (straight-line code: a loop here made the
+    // register allocator spill around the tile bodies); e = the number of
+    // experts whose inclusive count is <= x
+    int lo = 0;
+#pragma unroll
+    for (int step = kMaxExperts / 2; step > 0; step >>= 1) {
+      const int c = lo + step;
+      const int v = __builtin_amdgcn_readfirstlane(tiles_before[c <= E ? c - 1 : 0]);
+      lo = (c <= E && v <= x) ? c : lo;
     }
     e = lo;
     const int li = x - (e ? __builtin_amdgcn_readfirstlane(tiles_before[e - 1]) : 0);
     // x is wave-uniform, hence e: its rows are made uniform (SGPRs)
     const int r0 = __builtin_amdgcn_readfirstlane(row_begin(e));
-    const int tiles_m = (__builtin_amdgcn_readfirstlane(row_end(e)) - r0 + T::BM - 1) / T::BM;
+    const int cnt = __builtin_amdgcn_readfirstlane(row_end(e)) - r0;
+    const int tiles_m = (cnt + T::BM - 1) / T::BM;
     int tm, tn;
     group_walk(li, tiles_m, p.tiles_n, tm, tn);
     m0 = r0 + tm * T::BM;
     n0 = tn * T::BN;
     gm = tm % 8;
     gn = tn % T::NTN;
+    return cnt - tm * T::BM <= T::BM / 2;
   };
   bool preloaded = false;
+  // the next item's decode is carried into the next iteration
+  int e = 0, m0 = 0, n0 = 0, gm = 0, gn = 0;
+  bool half = false;
+  if ((int)blockIdx.x < items) half = decode(blockIdx.x, e, m0, n0, gm, gn);
   for (int b = blockIdx.x; b < items; b += gridDim.x) {
-    int e, m0, n0, gm, gn, ne = -1, nm0 = 0, nn0 = 0, ngm = 0, ngn = 0;
-    decode(b, e, m0, n0, gm, gn);
+    int ne = -1, nm0 = 0, nn0 = 0, ngm = 0, ngn = 0;
     const int nb = b + gridDim.x;
-    if (nb < items) decode(nb, ne, nm0, nn0, ngm, ngn);
-    const bool has_next = ne == e;
+    bool nhalf = false;
+    if (nb < items) nhalf = decode(nb, ne, nm0, nn0, ngm, ngn);
+    const bool has_next = ne == e && nhalf == half;
     GemmArgs pe = p;
     pe.w = p.w + e * g.w_stride;
     pe.sw = static_cast<const float*>(p.sw) + e * g.sw_stride;
     pe.m_end = __builtin_amdgcn_readfirstlane(row_end(e));
     const TileK tk{0, p.KB, 0, 0, 0, nullptr, nullptr, 0u};
-    fast_tile<T, false>(pe, smem, m0, n0, gm, gn, preloaded, has_next, nm0, nn0, ngm, ngn, tk);
+    if (half)
+      fast_tile<T, true, false>(pe, smem, m0, n0, gm, gn, preloaded, has_next, nm0, nn0, ngm, ngn, tk);
+    else
+      fast_tile<T, false, false>(pe, smem, m0, n0, gm, gn, preloaded, has_next, nm0, nn0, ngm, ngn, tk);
     preloaded = has_next;
+    e = ne; m0 = nm0; n0 = nn0; gm = ngm; gn = ngn; half = nhalf;
   }
   wait_vmcnt<0>();
 }
@@ -852,10 +874,13 @@ void launch_plan(GemmArgs p, const Plan& pl, hipStream_t stream) {
   }
   if (pl.cfg == 0) {
     using T = FastTile<MODE, 256, 256, 2, 4, 4>;
-    hipLaunchKernelGGL(gemm_fast_kernel<T>, dim3(grid), dim3(T::NW * 64), 0, stream, p, pl.full, pl.grid, ksplit);
+    if (ksplit)
+      hipLaunchKernelGGL((gemm_fast_kernel<T, true>), dim3(grid), dim3(T::NW * 64), 0, stream, p, pl.full, pl.grid);
+    else
+      hipLaunchKernelGGL((gemm_fast_kernel<T, false>), dim3(grid), dim3(T::NW * 64), 0, stream, p, pl.full, pl.grid);
   } else {
     using T = FastTile<MODE, 128, 128, 2, 2, 8>;
-    hipLaunchKernelGGL(gemm_fast_kernel<T>, dim3(grid), dim3(T::NW * 64), 0, stream, p, pl.full, pl.grid, 0);
+    hipLaunchKernelGGL((gemm_fast_kernel<T, false>), dim3(grid), dim3(T::NW * 64), 0, stream, p, pl.full, pl.grid);
   }
 }
 
