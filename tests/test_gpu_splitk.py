@@ -55,13 +55,15 @@ def _operands(M, N, K, gran, seed):
     return qa, sa, qw, sw, ref
 
 
-def _call(qa, sa, qw, sw, gran, ws):
+def _call(qa, sa, qw, sw, gran, ws, bias=None, a_layout=0):
     m = fq()
     M, K = qa.shape
     N = qw.shape[0]
     yb, y = padded(M, N, torch.bfloat16, 8, CANARY_BF16)
-    m.fp8q_gemm_blockscale_splitk(_dev_u8(qa, K), torch.from_numpy(sa).cuda(), 0, _dev_u8(qw, K),
-                                  torch.from_numpy(np.ascontiguousarray(sw)).cuda(), None, y, gran, ws)
+    b_d = None if bias is None else torch.from_numpy(bias.astype(np.float32)).to(torch.bfloat16).cuda()
+    sa_d = torch.from_numpy(np.ascontiguousarray(sa.T if a_layout else sa)).cuda()
+    m.fp8q_gemm_blockscale_splitk(_dev_u8(qa, K), sa_d, a_layout, _dev_u8(qw, K),
+                                  torch.from_numpy(np.ascontiguousarray(sw)).cuda(), b_d, y, gran, ws)
     torch.cuda.synchronize()
     assert canary_intact(yb, N, CANARY_BF16)
     return bf16_bits(y)
@@ -122,12 +124,16 @@ def test_prefill_tail_split_parity(M, N, K, gran):
     assert nbytes > 0
     ws = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device="cuda")
     qa, sa, qw, sw, ref = _operands(M, N, K, gran, M + N + K + 3 * gran)
-    y = _call(qa, sa, qw, sw, gran, ws)
+    # a bias (added once, by the workgroup that writes the tile) and the
+    # bench's column-major activation scales for the block granularities
+    bias = obf16.to_f64(obf16.round_from_f64(np.linspace(-3.0, 3.0, N)))
+    layout = 0 if gran == 1 else 1
+    y = _call(qa, sa, qw, sw, gran, ws, bias, layout)
     rows = np.unique(np.r_[0, M - 1, np.arange(M - 256, M, 37), np.random.default_rng(5).integers(0, M, 12)])
     if gran == 1:
-        yr = og.gemm_pertensor(qa, sa[0], qw, sw[0], rows=rows)[0]
+        yr = og.gemm_pertensor(qa, sa[0], qw, sw[0], bias=bias, rows=rows)[0]
     else:
-        yr = og.gemm_blockscale(qa, sa, qw, sw, rows=rows)[0]
+        yr = og.gemm_blockscale(qa, sa, qw, sw, bias=bias, rows=rows)[0]
     check_gemm_rows(y[rows], yr, f"prefill split M={M} N={N} K={K}", REL)
     # fixed order, and the flags of the previous launch do not confuse the next
-    np.testing.assert_array_equal(_call(qa, sa, qw, sw, gran, ws), y)
+    np.testing.assert_array_equal(_call(qa, sa, qw, sw, gran, ws, bias, layout), y)
