@@ -110,7 +110,9 @@ def main() -> int:
     # ---- weights: quantized once (offline preparation, not timed)
     wd = w_cpu.cuda()
     if name == "mx":
-        qw, sw = fq.quant_weight_mx(wd)
+        # MX scales column-major ([K/32, rows]), the layout the GEMM reads as
+        # contiguous runs; the weight's rows are quantized like activations
+        qw, sw = fq.quant_act_mx(wd, layout=fq.COL_MAJOR)
     elif name == "pertensor":
         qw, sw = fq.quant_weight_tensor(wd)
     elif pow2:
@@ -136,7 +138,7 @@ def main() -> int:
         if wl.residual:
             s["h"] = hg.clone()
         if name == "mx":
-            s["s"] = torch.empty(M, math.ceil(K / 32), dtype=torch.uint8, device="cuda")
+            s["s"] = torch.empty(math.ceil(K / 32), M, dtype=torch.uint8, device="cuda")
         elif name == "pertensor":
             s["s"] = sx_static
         else:
@@ -160,7 +162,7 @@ def main() -> int:
         elif wl.norm:
             fq.fp8q_rmsnorm_quant(s["x"], gamma, d["eps"], fq.COL_MAJOR, s["q"], s["s"])
         elif name == "mx":
-            fq.fp8q_quant_act_group(s["x"], 32, fq.SCALE_UE8M0, fq.ROW_MAJOR, None, s["q"], s["s"])
+            fq.fp8q_quant_act_group(s["x"], 32, fq.SCALE_UE8M0, fq.COL_MAJOR, None, s["q"], s["s"])
         elif name == "pertensor":
             fq.fp8q_quant_act_group(s["x"], 128, fq.SCALE_F32, fq.ROW_MAJOR, sx_static, s["q"], None)
         else:
@@ -180,7 +182,7 @@ def main() -> int:
             layout = fq.ROW_MAJOR if name == "pertensor" else fq.COL_MAJOR
             fq.fp8q_gemm_blockscale_splitk(s["q"], s["s"], layout, qw, sw, None, s["y"], gran, ws)
         elif name == "mx":
-            fq.fp8q_gemm_mxfp8(s["q"], s["s"], qw, sw, None, s["y"])
+            fq.fp8q_gemm_mxfp8(s["q"], s["s"], qw, sw, None, s["y"], fq.COL_MAJOR)
         elif name == "pertensor":
             fq.fp8q_gemm_blockscale(s["q"], s["s"], fq.ROW_MAJOR, qw, sw, None, s["y"], fq.GRAN_PER_TENSOR)
         else:
@@ -264,7 +266,7 @@ def main() -> int:
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8_e4m3 (fp32 accumulate)", "data": "synthetic",
         "config": {"workload": name, "M": M, "N": N, "K": K, "norm": wl.norm, "residual_add": wl.residual,
-                   "scales": {"mx": "1x32 ue8m0", "pertensor": "per-tensor fp32"}.get(
+                   "scales": {"mx": "1x32 ue8m0, [K/32, rows]", "pertensor": "per-tensor fp32"}.get(
                        name, "group128 + 128x128 power-of-two fp32 (in-MFMA)" if pow2 else "group128 + 128x128 fp32"),
                    "rotating_buffer_sets": nsets, "splitk_workspace_bytes": ws_bytes},
         "roofline": roof,

@@ -56,7 +56,7 @@ SIGNATURES = {
                                                    _I32, _P, ctypes.c_size_t, _P]),
     "fp8q_gemm_grouped_blockscale": (ctypes.c_int, [_P, _I64, _P, _I32, _P, _I32, _P, _I64, _I64, _P, _I64, _P, _I64,
                                                     _I64, _I64, _I64, _I32, _P]),
-    "fp8q_gemm_mxfp8": (ctypes.c_int, [_P, _I64, _P, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _I64, _P]),
+    "fp8q_gemm_mxfp8": (ctypes.c_int, [_P, _I64, _P, _P, _I64, _P, _I32, _P, _P, _I64, _I64, _I64, _I64, _P]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -249,7 +249,7 @@ def fp8q_gemm_grouped_blockscale(a, a_scales, a_layout, expert_offsets, w, w_sca
            "fp8q_gemm_grouped_blockscale")
 
 
-def fp8q_gemm_mxfp8(a, a_scales, w, w_scales, bias, y, stream=None):
+def fp8q_gemm_mxfp8(a, a_scales, w, w_scales, bias, y, scale_layout=ROW_MAJOR, stream=None):
     a, w = _u8(a), _u8(w)
     M, K, lda = _rows(a, torch.uint8, "a")
     N, Kw, ldw = _rows(w, torch.uint8, "w")
@@ -257,7 +257,7 @@ def fp8q_gemm_mxfp8(a, a_scales, w, w_scales, bias, y, stream=None):
     if Kw != K or (My, Ny) != (M, N):
         raise ValueError("shape mismatch between a, w and y")
     _check(load_library().fp8q_gemm_mxfp8(_ptr(a), lda, _ptr(a_scales), _ptr(w), ldw, _ptr(w_scales),
-                                          _ptr(bias), _ptr(y), ldy, M, N, K, _stream(stream)),
+                                          scale_layout, _ptr(bias), _ptr(y), ldy, M, N, K, _stream(stream)),
            "fp8q_gemm_mxfp8")
 
 
@@ -295,12 +295,14 @@ def quant_act_group_pow2(x: torch.Tensor, layout: int = ROW_MAJOR, stream=None):
     return q, s
 
 
-def quant_act_mx(x: torch.Tensor, stream=None):
-    """(q uint8 [M,K], UE8M0 scale bytes uint8 [M, ceil(K/32)])."""
+def quant_act_mx(x: torch.Tensor, layout: int = ROW_MAJOR, stream=None):
+    """(q uint8 [M,K], UE8M0 scale bytes uint8 [M, ceil(K/32)] or [ceil(K/32), M]).
+    Also the MX quantizer of weight rows (any layout)."""
     M, K = x.shape
     q = _q_like(M, K, x.device)
-    s = torch.empty(M, _cdiv(K, 32), dtype=torch.uint8, device=x.device)
-    fp8q_quant_act_group(x, 32, SCALE_UE8M0, ROW_MAJOR, None, q, s, stream)
+    G = _cdiv(K, 32)
+    s = torch.empty((G, M) if layout == COL_MAJOR else (M, G), dtype=torch.uint8, device=x.device)
+    fp8q_quant_act_group(x, 32, SCALE_UE8M0, layout, None, q, s, stream)
     return q, s
 
 
@@ -435,7 +437,7 @@ def gemm_pertensor(a, a_scale, w, w_scale, bias=None, stream=None):
     return y
 
 
-def gemm_mxfp8(a, a_scales, w, w_scales, bias=None, stream=None):
+def gemm_mxfp8(a, a_scales, w, w_scales, bias=None, scale_layout=ROW_MAJOR, stream=None):
     y = _y(a.shape[0], w.shape[0], a.device)
-    fp8q_gemm_mxfp8(a, a_scales, w, w_scales, bias, y, stream)
+    fp8q_gemm_mxfp8(a, a_scales, w, w_scales, bias, y, scale_layout, stream)
     return y

@@ -331,19 +331,28 @@ fp8q_status_t fp8q_gemm_grouped_blockscale(const uint8_t* a, int64_t lda, const 
 
 fp8q_status_t fp8q_gemm_mxfp8(const uint8_t* a, int64_t lda, const uint8_t* a_scales,
                               const uint8_t* w, int64_t ldw, const uint8_t* w_scales,
-                              const uint16_t* bias, uint16_t* y, int64_t ldy, int64_t M,
-                              int64_t N, int64_t K, void* stream) {
+                              int32_t scale_layout, const uint16_t* bias, uint16_t* y, int64_t ldy,
+                              int64_t M, int64_t N, int64_t K, void* stream) {
   if (M < 0 || N < 0 || K <= 0 || M > kMaxRows || N > kMaxRows || K > kMaxK) return FP8Q_ERR_SHAPE;
   if ((M / 128 + 1) * (N / 128 + 1) >= (int64_t(1) << 24)) return FP8Q_ERR_SHAPE;   // tile grid
+  if (scale_layout != FP8Q_SCALES_ROW_MAJOR && scale_layout != FP8Q_SCALES_COL_MAJOR) return FP8Q_ERR_UNSUPPORTED;
+  if (scale_layout == FP8Q_SCALES_COL_MAJOR && (M <= 64 || K % 128 != 0 || M % 4 != 0 || N % 4 != 0))
+    return FP8Q_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) return FP8Q_OK;
   FP8Q_TRY(check_matrix(a, K, lda, 1));
   FP8Q_TRY(check_matrix(w, K, ldw, 1));
   FP8Q_TRY(check_matrix(y, N, ldy, 2));
   if (a_scales == nullptr || w_scales == nullptr) return FP8Q_ERR_NULL;
+  if (scale_layout == FP8Q_SCALES_COL_MAJOR &&
+      ((reinterpret_cast<uintptr_t>(a_scales) & 3u) || (reinterpret_cast<uintptr_t>(w_scales) & 3u)))
+    return FP8Q_ERR_MISALIGNED;
   if (bias != nullptr && (reinterpret_cast<uintptr_t>(bias) & 1u)) return FP8Q_ERR_MISALIGNED;
   FP8Q_TRY(check_device());
-  return launch_status(fp8q::launch_gemm_mxfp8(a, lda, a_scales, w, ldw, w_scales, bias, y, ldy, M,
-                                                N, K, static_cast<hipStream_t>(stream)));
+  const hipError_t e = fp8q::launch_gemm_mxfp8(a, lda, a_scales, w, ldw, w_scales,
+                                               scale_layout == FP8Q_SCALES_COL_MAJOR, bias, y, ldy, M, N, K,
+                                               static_cast<hipStream_t>(stream));
+  if (e == hipErrorInvalidValue) return FP8Q_ERR_UNSUPPORTED;   // column-major beyond the fast kernel's limits
+  return launch_status(e);
 }
 
 }  // extern "C"

@@ -17,7 +17,7 @@
 
 namespace fp8q {
 
-enum { MODE_BLOCK = 0, MODE_TENSOR = 1, MODE_MX = 2, MODE_BMX = 3 };
+enum { MODE_BLOCK = 0, MODE_TENSOR = 1, MODE_MX = 2, MODE_BMX = 3, MODE_MXC = 4 };  // MXC: MX, scales [K/32][rows]
 
 struct GemmArgs {
   const uint8_t* a;

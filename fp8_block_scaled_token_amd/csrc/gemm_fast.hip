@@ -73,6 +73,8 @@ struct FastTile {
   static constexpr int MODE = MODE_, BM = BM_, BN = BN_, WM = WM_, WN = WN_;
   // fp32 scale words (block mode, and its power-of-two view)
   static constexpr bool FP32S = MODE == MODE_BLOCK || MODE == MODE_BMX;
+  // MX scale bytes, row-major ([rows][K/32]) or column-major ([K/32][rows])
+  static constexpr bool MXS = MODE == MODE_MX || MODE == MODE_MXC;
   // tile columns of one XCD's concurrently running group of tiles (the XCD's
   // workgroup slots divided by the group height of group_walk)
   static constexpr int NTN = NTN_;
@@ -127,7 +129,7 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
                                           bool preloaded, bool has_next, int nm0, int nn0, int ngm, int ngn,
                                           const TileK& tk) {
   constexpr int MODE = T::MODE, BM = T::BM, BN = T::BN, WN = T::WN, NW = T::NW;
-  constexpr bool FP32S = T::FP32S;
+  constexpr bool FP32S = T::FP32S, MXC = MODE == MODE_MXC;
   constexpr int RM = HALF ? T::BM / 2 : T::BM;
   constexpr int WTM = RM / T::WM, TM = WTM / 16, WTN = T::WTN, TN = T::TN;
   // a half tile's activation rows are spread over all waves too
@@ -183,15 +185,24 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
         const int g = q / WTM, rem = q % WTM;             // q < RM only when g < WM
         const int row = tm0 + g * WTM + 16 * (rem % TM) + rem / TM;
         const bool live = q < RM && row < p.M;
-        if (FP32S)
+        if (FP32S) {
           o.s = live ? (uint32_t)(p.sa_col_major ? row * 4 : row * p.KB * 4) : OOB;
-        else
+        } else if (MXC) {
+          // MX, [K/32][M] bytes: dword q holds rows 4r .. 4r+3 of 32-wide
+          // block qb of the K block (M % 4 == 0: whole dwords in or out)
+          const int qb = q / (BM / 4), r = tm0 + 4 * (q % (BM / 4));
+          o.s = (r < p.M && r < tm0 + RM) ? (uint32_t)(qb * p.M + r) : OOB;
+        } else {
           o.s = live ? (uint32_t)(row * p.KB32) : OOB;
+        }
       } else {
         const int qw = q - BM;
         if (FP32S) {
           const int col = tn0 + qw * WTN;
           o.s = (qw < WN && col < p.N) ? (uint32_t)(weight_scale_row(p, col) * p.KB * 4) : OOB;
+        } else if (MXC) {
+          const int qb = qw / (BN / 4), c = tn0 + 4 * (qw % (BN / 4));
+          o.s = c < p.N ? (uint32_t)(qb * p.N + c) : OOB;
         } else {
           const int g = qw / WTN, rem = qw % WTN;
           const int row = tn0 + g * WTN + 16 * (rem % TN) + rem / TN;
@@ -212,15 +223,15 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
   if constexpr (FP32S) {
     rSA = rsrc(p.sa, (int64_t)p.M * p.KB * 4);
     rSW = rsrc(p.sw, (int64_t)p.NB * p.KB * 4);
-  } else if constexpr (MODE == MODE_MX) {
+  } else if constexpr (T::MXS) {
     rSA = rsrc(p.sa, (int64_t)p.M * p.KB32);
     rSW = rsrc(p.sw, (int64_t)p.N * p.KB32);
   }
   // the scalar offset of a K block: block-mode column-major activation
   // scales advance by M words, every other scale array by one word (block)
   // or four bytes (MX) per K block
-  const uint32_t kstepS =
-      (FP32S && p.sa_col_major && wave_is_a) ? (uint32_t)p.M * 4u : 4u;
+  uint32_t kstepS = (FP32S && p.sa_col_major && wave_is_a) ? (uint32_t)p.M * 4u : 4u;
+  if (MXC) kstepS = wave_is_a ? (uint32_t)p.M * 4u : (uint32_t)p.N * 4u;
   const i32x4 rS = wave_is_a ? rSA : rSW;
   const uint32_t smem_base = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 
@@ -337,16 +348,25 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
     for (int j = 0; j < TN; ++j) fb[j] = read_frag(w, brow + 16 * j);
 #pragma unroll
     for (int i = 0; i < LA; ++i) fr[i] = read_frag(a, arow + 16 * i);
-    if constexpr (MODE != MODE_TENSOR)
+    if constexpr (MXC) {
+      // [sub-block][row] bytes: this lane's sub-block lq, its rows
+#pragma unroll
+      for (int i = 0; i < TM; ++i) sav[i] = a[SA_OFF + lq * BM + arow + 16 * i];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) swb[j] = a[SW_OFF + lq * BN + brow + 16 * j];
+    } else if constexpr (MODE == MODE_MX) {
       read_words(reinterpret_cast<const uint32_t*>(a + SA_OFF) + wm * WTM + l16 * TM, sav,
                  std::integral_constant<int, TM>{});
+      read_words(reinterpret_cast<const uint32_t*>(a + SW_OFF) + wn * WTN + l16 * TN, swb,
+                 std::integral_constant<int, TN>{});
+    } else if constexpr (MODE != MODE_TENSOR) {
+      read_words(reinterpret_cast<const uint32_t*>(a + SA_OFF) + wm * WTM + l16 * TM, sav,
+                 std::integral_constant<int, TM>{});
+    }
     if constexpr (MODE == MODE_BLOCK)
       swv = __uint_as_float(reinterpret_cast<const uint32_t*>(a + SW_OFF)[wn]);
     if constexpr (MODE == MODE_BMX)
       swe = (int)((reinterpret_cast<const uint32_t*>(a + SW_OFF)[wn] >> 23) & 0xFFu);
-    if constexpr (MODE == MODE_MX)
-      read_words(reinterpret_cast<const uint32_t*>(a + SW_OFF) + wn * WTN + l16 * TN, swb,
-                 std::integral_constant<int, TN>{});
   };
 
   // The MFMAs (and block-mode folds) of 16-row tile i of the block in stage
@@ -381,8 +401,9 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[i][j] = mfma_mx(fb[j].v, fa.v, acc[i][j], swe, sab);
     } else {
-      // scale byte of this lane's 32-wide K block (lane / 16) in each word
-      const int sh = 8 * lq;
+      // scale byte of this lane's 32-wide K block (lane / 16): in each word
+      // (row-major scales) or already the byte (column-major)
+      const int sh = MXC ? 0 : 8 * lq;
       const int sab = (int)((sav[i] >> sh) & 0xFF);
 #pragma unroll
       for (int j = 0; j < TN; ++j)
@@ -940,6 +961,7 @@ hipError_t launch_gemm_fast(GemmArgs p, int mode, hipStream_t stream) {
   if (mode == MODE_BLOCK) launch_plan<MODE_BLOCK>(p, pl, stream);
   else if (mode == MODE_TENSOR) launch_plan<MODE_TENSOR>(p, pl, stream);
   else if (mode == MODE_BMX) launch_plan<MODE_BMX>(p, pl, stream);
+  else if (mode == MODE_MXC) launch_plan<MODE_MXC>(p, pl, stream);
   else launch_plan<MODE_MX>(p, pl, stream);
   return hipGetLastError();
 }

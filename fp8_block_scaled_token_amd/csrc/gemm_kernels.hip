@@ -457,14 +457,19 @@ hipError_t launch_gemm_grouped_blockscale(const uint8_t* a, int64_t lda, const f
 }
 
 hipError_t launch_gemm_mxfp8(const uint8_t* a, int64_t lda, const uint8_t* sa, const uint8_t* w,
-                             int64_t ldw, const uint8_t* sw, const uint16_t* bias, uint16_t* y,
+                             int64_t ldw, const uint8_t* sw, int col_major, const uint16_t* bias, uint16_t* y,
                              int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   GemmArgs p{};
-  p.a = a; p.lda = lda; p.sa = sa; p.sa_col_major = 0;
+  p.a = a; p.lda = lda; p.sa = sa; p.sa_col_major = col_major;
   p.w = w; p.ldw = ldw; p.sw = sw; p.bias = bias; p.y = y; p.ldy = ldy;
   p.M = (int)M; p.N = (int)N; p.K = (int)K;
   p.KB = cdiv(K, 128); p.KB32 = cdiv(K, 32); p.NB = cdiv(N, 128);
   p.m_end = p.M;
+  if (col_major) {
+    // [K/32][rows] scales: the fast kernel reads them (whole dwords of four rows)
+    if (!gemm_fast_eligible(p, MODE_MX) || p.M % 4 || p.N % 4) return hipErrorInvalidValue;
+    return launch_gemm_fast(p, MODE_MXC, stream);
+  }
   return launch_mode<MODE_MX>(p, stream);
 }
 

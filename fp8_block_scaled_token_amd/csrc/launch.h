@@ -60,8 +60,10 @@ hipError_t launch_gemm_grouped_blockscale(const uint8_t* a, int64_t lda, const f
                                           int64_t w_stride, const float* sw, int64_t shard, uint16_t* y,
                                           int64_t ldy, int64_t M, int64_t N, int64_t K, int pow2,
                                           hipStream_t stream);
+// MX GEMM; col_major: scales [K/32][rows] (fast kernel only:
+// hipErrorInvalidValue, nothing launched, where it does not apply).
 hipError_t launch_gemm_mxfp8(const uint8_t* a, int64_t lda, const uint8_t* sa, const uint8_t* w,
-                             int64_t ldw, const uint8_t* sw, const uint16_t* bias, uint16_t* y,
+                             int64_t ldw, const uint8_t* sw, int col_major, const uint16_t* bias, uint16_t* y,
                              int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
 }  // namespace fp8q

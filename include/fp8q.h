@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define FP8Q_ABI_VERSION 1
+#define FP8Q_ABI_VERSION 2
 
 typedef enum {
   FP8Q_OK = 0,
@@ -325,13 +325,20 @@ fp8q_status_t fp8q_gemm_grouped_blockscale(const uint8_t* a, int64_t lda, const 
  * "Triton 分块内核在做什么" (the scale multiply becomes an exponent add):
  *   Y[i,j] = bf16( sum_b P_b[i,j] * 2^(ea[i,b]-127) * 2^(ew[j,b]-127) + bias[j] ),
  *   b over 32-wide K blocks.
- *   a E4M3 [M, lda], a_scales uint8 [M, ceil(K/32)] row-major;
- *   w E4M3 [N, ldw], w_scales uint8 [N, ceil(K/32)] row-major;
- *   bias optional bf16 [N];  y bf16 [M, ldy].
+ *   a E4M3 [M, lda];  w E4M3 [N, ldw];  bias optional bf16 [N];  y bf16 [M, ldy].
+ *   scale_layout FP8Q_SCALES_ROW_MAJOR: a_scales uint8 [M, ceil(K/32)],
+ *                w_scales uint8 [N, ceil(K/32)];
+ *                FP8Q_SCALES_COL_MAJOR: a_scales [ceil(K/32), M], w_scales
+ *                [ceil(K/32), N] (the [groups, rows] layout of [GLM17] "第 7
+ *                站:MoE——被排除在 FP8 之外的门控与 dispatch 的量化": a K block's scales
+ *                of consecutive rows are contiguous); requires M > 64,
+ *                K % 128 == 0 and M, N multiples of 4 (FP8Q_ERR_UNSUPPORTED
+ *                otherwise).  fp8q_quant_act_group writes either layout, for
+ *                activations and for weight rows alike.
  */
 fp8q_status_t fp8q_gemm_mxfp8(const uint8_t* a, int64_t lda, const uint8_t* a_scales,
                               const uint8_t* w, int64_t ldw, const uint8_t* w_scales,
-                              const uint16_t* bias, uint16_t* y, int64_t ldy,
+                              int32_t scale_layout, const uint16_t* bias, uint16_t* y, int64_t ldy,
                               int64_t M, int64_t N, int64_t K, void* stream);
 
 #ifdef __cplusplus

@@ -48,7 +48,7 @@ def test_binding_covers_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.fp8q_abi_version() == 1
+    assert lib.fp8q_abi_version() == 2
     for s in range(8):
         assert len(lib.fp8q_status_string(s)) > 0
     assert lib.fp8q_status_string(99) == b"unknown status"
@@ -206,8 +206,13 @@ def test_gemm_validation(lib):
     assert g(A, 128, C, 0, B, 128, C, None, C, 252, 4, 256, 128, 0, None) == 2   # ldy < N
     assert g(A, 128, C, 0, B, 128, C, None, C, 260, 4, 260, 128, 0, None) == 4   # ldy % 8
     m = lib.fp8q_gemm_mxfp8
-    assert m(A, 128, C, B, 128, C, None, C, 256, -1, 256, 128, None) == 2
-    assert m(A, 128, None, B, 128, C, None, C, 256, 4, 256, 128, None) == 1
+    assert m(A, 128, C, B, 128, C, 0, None, C, 256, -1, 256, 128, None) == 2
+    assert m(A, 128, None, B, 128, C, 0, None, C, 256, 4, 256, 128, None) == 1
+    assert m(A, 128, C, B, 128, C, 2, None, C, 256, 128, 256, 128, None) == 3        # layout
+    assert m(A, 128, C, B, 128, C, 1, None, C, 256, 64, 256, 128, None) == 3         # column-major needs M > 64
+    assert m(A, 128, C, B, 128, C, 1, None, C, 256, 130, 256, 128, None) == 3        # ... and M % 4 == 0
+    assert m(A, 200, C, B, 200, C, 1, None, C, 256, 128, 256, 200, None) == 3        # ... and K % 128 == 0
+    assert m(A, 128, ctypes.c_void_p(0x300001), B, 128, C, 1, None, C, 256, 128, 256, 128, None) == 4
 
 
 def test_device_check_without_gpu(lib):

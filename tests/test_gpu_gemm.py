@@ -140,6 +140,30 @@ def test_gemm_mxfp8_parity(M, N, K):
     check_gemm_rows(bf16_bits(y), yr, f"mx M={M} N={N} K={K}", REL)
 
 
+# column-major MX scales ([K/32, rows]): the fast kernel in both tile
+# configurations (and its half-height tail), ragged N and M (multiples of 4)
+@pytest.mark.parametrize("M,N,K", [(100, 640, 7168), (260, 1028, 1024), (2048, 7168, 1024), (516, 2052, 2048),
+                                   (1540, 4096, 512)])
+@pytest.mark.parametrize("cfg", [0, 1])
+def test_gemm_mxfp8_col_major_scales(monkeypatch, M, N, K, cfg):
+    log(f"gemm_mxfp8 col-major M={M} N={N} K={K} cfg={cfg}")
+    monkeypatch.setenv("FP8Q_GEMM_CFG", str(cfg))
+    m = fq()
+    x = workloads.activations(M, K, seed=K + 17, outlier_frac=0.001)
+    w = workloads.weights(N, K, seed=K + 18, std=1.0)
+    qa, ea = oq.quant_mx(bf16_host(x))
+    qw, ew = oq.quant_mx(bf16_host(w))
+    bias = obf16.to_f64(obf16.round_from_f64(np.linspace(-2.0, 2.0, N)))
+    b_d = torch.from_numpy(bias.astype(np.float32)).to(torch.bfloat16).cuda()
+    yb, y = padded(M, N, torch.bfloat16, 8, CANARY_BF16)
+    m.fp8q_gemm_mxfp8(_dev_u8(qa, K), torch.from_numpy(np.ascontiguousarray(ea.T)).cuda(), _dev_u8(qw, K),
+                      torch.from_numpy(np.ascontiguousarray(ew.T)).cuda(), b_d, y, m.COL_MAJOR)
+    torch.cuda.synchronize()
+    assert canary_intact(yb, N, CANARY_BF16)
+    yr, _ = og.gemm_mx(qa, ea, qw, ew, bias=bias)
+    check_gemm_rows(bf16_bits(y), yr, f"mx col-major M={M} N={N} K={K}", REL)
+
+
 def test_gemm_mx_scale_placement():
     # distinct power-of-two scale per 32-block: any mix-up of which block a
     # scale byte applies to changes the result far beyond the tolerance
@@ -216,12 +240,19 @@ def test_full_size_mx_and_pertensor():
     qa, ea = m.quant_act_mx(xd)
     qw, ew = m.quant_weight_mx(wd)
     y = m.gemm_mxfp8(qa, ea, qw, ew)
+    # the bench's configuration: column-major scales from the same quantizer
+    qa_c, ea_c = m.quant_act_mx(xd, layout=m.COL_MAJOR)
+    qw_c, ew_c = m.quant_act_mx(wd, layout=m.COL_MAJOR)
+    y_c = m.gemm_mxfp8(qa_c, ea_c, qw_c, ew_c, scale_layout=m.COL_MAJOR)
     torch.cuda.synchronize()
+    np.testing.assert_array_equal(ea_c.cpu().numpy().T, ea.cpu().numpy())
+    np.testing.assert_array_equal(ew_c.cpu().numpy().T, ew.cpu().numpy())
     rows = np.unique(np.r_[0, wl.M - 1, np.random.default_rng(4).integers(0, wl.M, 6)])
     qa_r, ea_r = oq.quant_mx(bf16_host(d["x"][rows]))
     qw_r, ew_r = oq.quant_mx(bf16_host(d["w"]))
     yr, _ = og.gemm_mx(qa_r, ea_r, qw_r, ew_r)
     check_gemm_rows(bf16_bits(y)[rows], yr, "full mx", REL)
+    check_gemm_rows(bf16_bits(y_c)[rows], yr, "full mx col-major", REL)
     # per-tensor static on the same shapes
     xh = bf16_host(d["x"])
     sx = np.float32(np.float32(np.abs(xh).max()) / np.float32(448.0))
