@@ -523,6 +523,10 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
           if (__hip_atomic_load(tk.flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == tk.nonce) break;
           __builtin_amdgcn_s_sleep(2);
         }
+        // the consumer is the flag's only reader: clear it, so that a launch
+        // replayed with the same nonce (a captured graph) never finds it set
+        // before its own producer has run
+        __hip_atomic_store(tk.flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
       }
     }
     __syncthreads();

@@ -262,8 +262,11 @@ fp8q_status_t fp8q_gemm_blockscale(const uint8_t* a, int64_t lda, const float* a
  *    one of which adds the other's fp32 partial (first half + second half)
  *    before the epilogue (it waits for it, bounded; the other never waits).
  * Both orders are fixed: repeated calls give identical bits.  Other shapes,
- * or a workspace too small, run the unsplit kernels (a prefill launch keeps
- * a launch counter for the flags it leaves in the workspace).
+ * or a workspace too small, run the unsplit kernels.  The prefill split uses
+ * one flag word per leftover tile in the workspace, raised to a per-launch
+ * value and cleared again by the workgroup that reads it, so launches may be
+ * captured in a graph and replayed; a workspace is used by one launch at a
+ * time (launches that overlap on one workspace race).
  *
  *   Arguments as fp8q_gemm_blockscale (all three granularities), plus
  *   workspace  device memory for S * M * N fp32 partials (4-byte aligned),
