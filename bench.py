@@ -46,8 +46,11 @@ MALL_DEFEAT_BYTES = 640 << 20
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # defaults: ~20 ms of warm-up steps (the chip reaches its steady clock
+    # only after some tens of milliseconds of sustained load; 10 warm-up
+    # steps left the first timed steps ~20 % slower) and ~20 ms timed
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="prefill_norm",
                     choices=["tiny", "decode", "prefill_norm", "prefill_addnorm", "large", "mx", "pertensor",
                              "prefill_norm_pow2", "large_pow2", "moe_up", "moe_down", "decode_splitk"])
