@@ -162,7 +162,7 @@ __global__ __launch_bounds__(256) void quant_group128_kernel(
   if (full) {
     const uint16_t* xs = xr + seg0 + 8 * lane;
 #pragma unroll
-    for (int c = 0; c < CH; ++c) raw[c] = ld16(xs + 512 * c);
+    for (int c = 0; c < CH; ++c) raw[c] = ld16_nt(xs + 512 * c);
   } else {
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(256) void quant_group32mx_kernel(
   if (full) {
     const uint16_t* xs = xr + seg0 + 8 * lane;
 #pragma unroll
-    for (int c = 0; c < CH; ++c) raw[c] = ld16(xs + 512 * c);
+    for (int c = 0; c < CH; ++c) raw[c] = ld16_nt(xs + 512 * c);
   } else {
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
@@ -256,7 +256,7 @@ __global__ __launch_bounds__(256) void quant_static_kernel(
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int64_t k0 = seg0 + 512 * c + 8 * lane;
-    raw[c] = full ? ld16(xr + k0) : (k0 < K) ? load8_bf16_masked(xr, k0, K) : make_uint4(0, 0, 0, 0);
+    raw[c] = full ? ld16_nt(xr + k0) : (k0 < K) ? load8_bf16_masked(xr, k0, K) : make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
@@ -309,12 +309,17 @@ struct RmsArgs {
   const float* static_scale; // EXIT_STATIC: per-tensor scale
 };
 
-template <int CH>
+// STREAM: the row is read once (activations, the sublayer output); the norm
+// weight, which every workgroup reads, is loaded without the streaming hint.
+template <int CH, bool STREAM = true>
 __device__ __forceinline__ void load_row_seg(uint4 (&raw)[CH], const uint16_t* xr, int64_t seg0, int64_t K) {
   const int lane = threadIdx.x & 63;
   if (seg0 + 512 * CH <= K) {
 #pragma unroll
-    for (int c = 0; c < CH; ++c) raw[c] = ld16(xr + seg0 + 512 * c + 8 * lane);
+    for (int c = 0; c < CH; ++c) {
+      const uint16_t* p = xr + seg0 + 512 * c + 8 * lane;
+      raw[c] = STREAM ? ld16_nt(p) : ld16(p);
+    }
   } else {
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
@@ -434,7 +439,7 @@ __device__ __forceinline__ void norm_quant_seg(const RmsArgs& a, uint4 (&raw)[CH
 #pragma unroll
       for (int e = 0; e < 8; ++e) t[e] = clamp448(v[e] / s_stat);   // IEEE division
       const uint2 o = encode8(t);
-      if (full) st8(qr + k0, o);
+      if (full) st8_nt(qr + k0, o);
       else if (k0 < K) store8_masked(qr, k0, K, o);
     }
     return;
@@ -447,7 +452,7 @@ __device__ __forceinline__ void norm_quant_seg(const RmsArgs& a, uint4 (&raw)[CH
   for (int c = 0; c < CH; ++c) {
     const int64_t k0 = seg0 + 512 * c + 8 * lane;
     const uint2 o = EXIT == EXIT_POW2 ? quant8_mx(raw[c], byte[c]) : quant8(raw[c], s[c], r[c]);
-    if (full) st8(qr + k0, o);
+    if (full) st8_nt(qr + k0, o);
     else if (k0 < K) store8_masked(qr, k0, K, o);
   }
   store_group_scales<CH>(a.scales, s_mine, seg0 / 128, (K + 127) >> 7, a.M, row, a.col_major);
@@ -467,7 +472,7 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_rows_kernel(RmsArgs a, int 
   float gf[CH][8];          // gamma of this wave's segment, unpacked once
   {
     uint4 gr[CH];
-    load_row_seg<CH>(gr, a.gamma, seg0, a.K);
+    load_row_seg<CH, false>(gr, a.gamma, seg0, a.K);
 #pragma unroll
     for (int c = 0; c < CH; ++c) unpack8(gr[c], gf[c]);
   }
@@ -510,9 +515,10 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(RmsArgs a) {
   uint4 raw[CH], gr[CH];
   double ss = 0.0;
   for (int64_t it = 0; it < npass; ++it) {
-    load_row_seg<CH>(raw, xr, (4 * it + wave) * SEG, a.K);
+    // first of two reads: keep the lines cached for the second
+    load_row_seg<CH, false>(raw, xr, (4 * it + wave) * SEG, a.K);
     if constexpr (ADD) {
-      load_row_seg<CH>(gr, hr, (4 * it + wave) * SEG, a.K);
+      load_row_seg<CH, false>(gr, hr, (4 * it + wave) * SEG, a.K);
       add_seg<CH>(raw, gr);
     }
     ss = sumsq_seg<CH>(raw, ss);
@@ -527,7 +533,7 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(RmsArgs a) {
       add_seg<CH>(raw, gr);
       store_row_seg<CH>(a.z_out + row * a.ldz, raw, seg0, a.K);
     }
-    load_row_seg<CH>(gr, a.gamma, seg0, a.K);
+    load_row_seg<CH, false>(gr, a.gamma, seg0, a.K);
     float gf[CH][8];
 #pragma unroll
     for (int c = 0; c < CH; ++c) unpack8(gr[c], gf[c]);
