@@ -10,9 +10,9 @@ by the scaled GEMM (`*_pow2` workloads: the same with power-of-two scales
 the split-K entry point with its workspace; `moe_*`: the
 expert-sorted rows of one GPU's share of a MoE layer through the grouped
 GEMM).  The
-weight is quantized once before timing (it is offline preparation).  Inputs
-and outputs rotate over several buffer sets whose total exceeds the 256 MB
-Infinity Cache, so HBM rates are not inflated by cache hits.
+weight is quantized once before timing (it is offline preparation).  Inputs,
+outputs and weight copies rotate over several buffer sets whose total exceeds
+the 256 MB Infinity Cache, so HBM rates are not inflated by cache hits.
 
 Prints ONE JSON line.  `value` = 2*M*N*K per step / step time (whole layer,
 quantizer included); `roofline` is for the dominant kernel (the GEMM): its
@@ -150,6 +150,15 @@ def main() -> int:
         sets.append(s)
     del xg, hg
 
+    # ---- weight copies: a weight must not stay in the Infinity Cache between
+    # its uses either (a decode weight is 151 MB), so the sets rotate over
+    # enough copies that several hundred MB lie between two uses of one copy
+    w_bytes = qw.numel() * qw.element_size() + sw.numel() * sw.element_size()
+    nw = max(1, min(nsets, math.ceil(MALL_DEFEAT_BYTES / w_bytes)))
+    wcopies = [(qw, sw)] + [(qw.clone(), sw.clone()) for _ in range(nw - 1)]
+    for i, s in enumerate(sets):
+        s["qw"], s["sw"] = wcopies[i % nw]
+
     # activation group scales travel column-major ([K/128, M]): a K block's
     # scales for consecutive rows are contiguous, one cache line per 32 rows
     # for the GEMM (the row-major form costs a line per row)
@@ -183,13 +192,13 @@ def main() -> int:
         if ws is not None:
             gran = {"pertensor": fq.GRAN_PER_TENSOR}.get(name, fq.GRAN_BLOCK128_POW2 if pow2 else fq.GRAN_BLOCK128)
             layout = fq.ROW_MAJOR if name == "pertensor" else fq.COL_MAJOR
-            fq.fp8q_gemm_blockscale_splitk(s["q"], s["s"], layout, qw, sw, None, s["y"], gran, ws)
+            fq.fp8q_gemm_blockscale_splitk(s["q"], s["s"], layout, s["qw"], s["sw"], None, s["y"], gran, ws)
         elif name == "mx":
-            fq.fp8q_gemm_mxfp8(s["q"], s["s"], qw, sw, None, s["y"], fq.COL_MAJOR)
+            fq.fp8q_gemm_mxfp8(s["q"], s["s"], s["qw"], s["sw"], None, s["y"], fq.COL_MAJOR)
         elif name == "pertensor":
-            fq.fp8q_gemm_blockscale(s["q"], s["s"], fq.ROW_MAJOR, qw, sw, None, s["y"], fq.GRAN_PER_TENSOR)
+            fq.fp8q_gemm_blockscale(s["q"], s["s"], fq.ROW_MAJOR, s["qw"], s["sw"], None, s["y"], fq.GRAN_PER_TENSOR)
         else:
-            fq.fp8q_gemm_blockscale(s["q"], s["s"], fq.COL_MAJOR, qw, sw, None, s["y"],
+            fq.fp8q_gemm_blockscale(s["q"], s["s"], fq.COL_MAJOR, s["qw"], s["sw"], None, s["y"],
                                     fq.GRAN_BLOCK128_POW2 if pow2 else fq.GRAN_BLOCK128)
 
     for i in range(args.warmup):
@@ -271,7 +280,7 @@ def main() -> int:
         "config": {"workload": name, "M": M, "N": N, "K": K, "norm": wl.norm, "residual_add": wl.residual,
                    "scales": {"mx": "1x32 ue8m0, [K/32, rows]", "pertensor": "per-tensor fp32"}.get(
                        name, "group128 + 128x128 power-of-two fp32 (in-MFMA)" if pow2 else "group128 + 128x128 fp32"),
-                   "rotating_buffer_sets": nsets, "splitk_workspace_bytes": ws_bytes},
+                   "rotating_buffer_sets": nsets, "weight_copies": nw, "splitk_workspace_bytes": ws_bytes},
         "roofline": roof,
         "gemm": {"us": round(gemm_ms * 1e3, 2), "TFLOP/s": round(gemm_tflops, 1),
                  "frac_fp8_peak": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "GB/s": round(gemm_gbps, 1),

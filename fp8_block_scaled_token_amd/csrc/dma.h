@@ -46,6 +46,15 @@ __device__ __forceinline__ void dma16(const i32x4& r, uint32_t lds, uint32_t vof
                : "v"(voffset), "s"(r), "s"(lds), "s"(soffset)
                : "memory", "m0");
 }
+// The same with the non-temporal hint, for operand bytes a launch reads once
+// (a decode GEMM's weights, an expert's weights in the grouped GEMM): they
+// stream through the caches instead of displacing lines that are re-read.
+__device__ __forceinline__ void dma16_nt(const i32x4& r, uint32_t lds, uint32_t voffset, uint32_t soffset) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, %3 offen nt lds"
+               :
+               : "v"(voffset), "s"(r), "s"(lds), "s"(soffset)
+               : "memory", "m0");
+}
 __device__ __forceinline__ void dma4(const i32x4& r, uint32_t lds, uint32_t voffset, uint32_t soffset) {
   asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, %3 offen lds"
                :

@@ -157,7 +157,8 @@ __global__ __launch_bounds__(256) void gemm_decode_dma_kernel(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) dma16(rw, valid ? stage + (2 * j + h) * 1024 : sink, offW[j][h], kofs);
+      // weights are read once per launch: streamed
+      for (int h = 0; h < 2; ++h) dma16_nt(rw, valid ? stage + (2 * j + h) * 1024 : sink, offW[j][h], kofs);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll

@@ -124,7 +124,9 @@ struct TileK {
   uint32_t nonce;
 };
 
-template <class T, bool HALF, bool SPLIT>
+// NTW: weight loads carry the non-temporal hint (the grouped GEMM, whose
+// expert weights are read once per launch; the dense kernel re-reads them).
+template <class T, bool HALF, bool SPLIT, bool NTW = false>
 __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int m0, int n0, int gm, int gn,
                                           bool preloaded, bool has_next, int nm0, int nn0, int ngm, int ngn,
                                           const TileK& tk) {
@@ -257,8 +259,9 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
     } else if constexpr (l < A_PER + W_PER) {
       i32x4 r = rW;
       r.z = valid ? r.z : 0;
-      dma16(r, valid ? base + ABYTES + (wave * W_PER + l - A_PER) * 1024 : sink, o.w[l - A_PER],
-            (uint32_t)kbv * 128u);
+      const uint32_t dst = valid ? base + ABYTES + (wave * W_PER + l - A_PER) * 1024 : sink;
+      if constexpr (NTW) dma16_nt(r, dst, o.w[l - A_PER], (uint32_t)kbv * 128u);
+      else dma16(r, dst, o.w[l - A_PER], (uint32_t)kbv * 128u);
     } else {
       i32x4 r = rS;
       r.z = valid ? r.z : 0;
@@ -798,9 +801,9 @@ __global__ __launch_bounds__(T::NW * 64) void gemm_grouped_kernel(GemmArgs p, Gr
     pe.m_end = __builtin_amdgcn_readfirstlane(row_end(e));
     const TileK tk{0, p.KB, 0, 0, 0, nullptr, nullptr, 0u};
     if (half)
-      fast_tile<T, true, false>(pe, smem, m0, n0, gm, gn, preloaded, has_next, nm0, nn0, ngm, ngn, tk);
+      fast_tile<T, true, false, true>(pe, smem, m0, n0, gm, gn, preloaded, has_next, nm0, nn0, ngm, ngn, tk);
     else
-      fast_tile<T, false, false>(pe, smem, m0, n0, gm, gn, preloaded, has_next, nm0, nn0, ngm, ngn, tk);
+      fast_tile<T, false, false, true>(pe, smem, m0, n0, gm, gn, preloaded, has_next, nm0, nn0, ngm, ngn, tk);
     preloaded = has_next;
     e = ne; m0 = nm0; n0 = nn0; gm = ngm; gn = ngn; half = nhalf;
   }
