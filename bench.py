@@ -18,8 +18,10 @@ Prints ONE JSON line.  `value` = 2*M*N*K per step / step time (whole layer,
 quantizer included); `roofline` is for the dominant kernel (the GEMM): its
 average launch duration over back-to-back launches after the timed steps,
 from HIP events recorded on the stream it runs on (`us_in_step` is the same
-kernel timed inside the steps, dispatch gaps included); `cpu_baseline` is the
-CPU oracle timed on a bounded sample of the same workload on this host.
+kernel timed inside the steps, dispatch gaps included); for workloads with
+the RMSNorm front end, `quant_group` is the group quantizer alone over the
+same activations (not part of a step); `cpu_baseline` is the CPU oracle timed
+on a bounded sample of the same workload on this host.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
 """
@@ -290,6 +292,16 @@ def main() -> int:
                   "us_in_step": round(step_quant_ms * 1e3, 2)},
         "cpu_baseline": None,
     }
+    if wl.norm and not pow2:
+        # the group quantizer on its own (no norm in front) over the same
+        # activations, for its HBM fraction on this shape; not part of a step
+        def quant_plain(s):
+            fq.fp8q_quant_act_group(s["x"], 128, fq.SCALE_F32, fq.COL_MAJOR, None, s["q"], s["s"])
+        qp_ms = timed(quant_plain, reps)
+        qp_bytes = M * K * 2 + M * K + 4 * M * KB
+        qp_gbps = qp_bytes / (qp_ms * 1e-3) / 1e9
+        out["quant_group"] = {"kernel": "quant_group128", "us": round(qp_ms * 1e3, 2), "GB/s": round(qp_gbps, 1),
+                              "frac_hbm": round(qp_gbps / PEAK_HBM_GBPS, 4), "algorithmic_bytes": qp_bytes}
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(name, wl, d, args.cpu_seconds, pow2)
     print(json.dumps(out), flush=True)
