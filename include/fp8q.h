@@ -40,7 +40,10 @@
  *   memory-safe) outputs.
  * Determinism.  No atomics on floating-point data and fixed reduction
  *   orders: repeated calls give identical bits.  Calls are re-entrant across
- *   streams (no mutable global state except a per-device architecture cache).
+ *   streams and host threads: the only process-wide mutable state is a
+ *   per-device cache of the architecture and of kernel occupancies (filled
+ *   once) and an atomic launch counter that numbers split-K launches; the
+ *   split-K workspace is the caller's and serves one launch at a time.
  */
 #ifndef FP8Q_H
 #define FP8Q_H
