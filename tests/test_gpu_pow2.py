@@ -33,7 +33,8 @@ def _dev_u8(a: np.ndarray, K: int) -> torch.Tensor:
     return buf[:, :K]
 
 
-@pytest.mark.parametrize("M,K", [(16, 512), (5, 520), (3, 1001), (33, 6144), (2, 8), (1, 7168), (70, 300)])
+@pytest.mark.parametrize("M,K", [(16, 512), (5, 520), (3, 1001), (33, 6144), (2, 8), (1, 7168), (70, 300),
+                                 (7, 2560), (6, 3584)])
 @pytest.mark.parametrize("layout", [0, 1])
 def test_quant_group_pow2_parity(M, K, layout):
     log(f"quant_group pow2 M={M} K={K} layout={layout}")

@@ -50,7 +50,8 @@ def _run_group128(x_cpu, layout):
     return q.cpu().numpy(), s
 
 
-@pytest.mark.parametrize("M,K", [(16, 512), (5, 520), (3, 1001), (33, 6144), (2, 8), (1, 7168), (70, 300)])
+@pytest.mark.parametrize("M,K", [(16, 512), (5, 520), (3, 1001), (33, 6144), (2, 8), (1, 7168), (70, 300),
+                                 (9, 1536), (7, 2560), (6, 3584)])   # 3, 5, 7 chunks per wave
 @pytest.mark.parametrize("layout", [0, 1])
 def test_quant_group128_parity(M, K, layout):
     log(f"quant_group128 M={M} K={K} layout={layout}")
@@ -85,7 +86,7 @@ def test_quant_group128_full_size_sampled_rows(name):
     np.testing.assert_array_equal(q.cpu().numpy()[rows], qr)
 
 
-@pytest.mark.parametrize("M,K", [(16, 512), (5, 200), (3, 1001), (9, 7168)])
+@pytest.mark.parametrize("M,K", [(16, 512), (5, 200), (3, 1001), (9, 7168), (9, 1536), (7, 2560), (6, 3584)])
 def test_quant_mx_parity(M, K):
     log(f"quant_mx M={M} K={K}")
     m = fq()
@@ -113,7 +114,7 @@ def test_quant_mx_special_values():
     np.testing.assert_array_equal(q.cpu().numpy(), qr)
 
 
-@pytest.mark.parametrize("M,K", [(16, 512), (5, 520), (64, 7168)])
+@pytest.mark.parametrize("M,K", [(16, 512), (5, 520), (64, 7168), (9, 1536), (7, 2560), (6, 3584), (3, 9000)])
 def test_quant_static_parity(M, K):
     log(f"quant_static M={M} K={K}")
     m = fq()
