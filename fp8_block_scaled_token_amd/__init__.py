@@ -412,7 +412,8 @@ def gemm_blockscale_pow2(a, a_scales, w, w_scale_inv, bias=None, a_layout: int =
 
 def gemm_blockscale_splitk(a, a_scales, w, w_scale_inv, bias=None, a_layout: int = ROW_MAJOR, gran=GRAN_BLOCK128,
                            workspace=None, stream=None):
-    """Block GEMM with split-K on decode shapes; allocates the workspace
+    """Block GEMM through the split-K entry (decode shapes split K; prefill
+    shapes split their leftover tiles along K); allocates the workspace
     (torch) when none is given."""
     M, N, K = a.shape[0], w.shape[0], a.shape[1]
     if workspace is None:

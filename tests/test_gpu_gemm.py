@@ -206,6 +206,9 @@ def _full_size(name, rows_sample):
     else:
         qa, sa = m.quant_act_group(xd, layout=m.COL_MAJOR)
     y = m.gemm_blockscale(qa, sa, qw, sw, a_layout=m.COL_MAJOR)
+    # and the bench's own call: the split-K entry with the workspace the
+    # library asks for (the prefill shape splits its leftover tiles along K)
+    y_split = m.gemm_blockscale_splitk(qa, sa, qw, sw, a_layout=m.COL_MAJOR)
     torch.cuda.synchronize()
     rows = rows_sample(wl.M)
     xh = bf16_host(d["x"][rows])
@@ -217,6 +220,7 @@ def _full_size(name, rows_sample):
     qw_r, sw_r = oq.quant_weight_block(bf16_host(d["w"]))
     yr, _ = og.gemm_blockscale(qa_r, sa_r, qw_r, sw_r)
     check_gemm_rows(bf16_bits(y)[rows], yr, f"full {name}", REL)
+    check_gemm_rows(bf16_bits(y_split)[rows], yr, f"full {name} (split-K entry)", REL)
 
 
 def test_full_size_decode():
@@ -224,7 +228,9 @@ def test_full_size_decode():
 
 
 def test_full_size_prefill_norm():
-    _full_size("prefill_norm", lambda M: np.unique(np.r_[0, M - 1, np.random.default_rng(2).integers(0, M, 14)]))
+    # sampled rows include the last 256 (the split tail tiles' rows)
+    _full_size("prefill_norm", lambda M: np.unique(np.r_[0, M - 1, np.arange(M - 256, M, 31),
+                                                       np.random.default_rng(2).integers(0, M, 14)]))
 
 
 def test_full_size_large():
