@@ -16,8 +16,10 @@ the 256 MB Infinity Cache, so HBM rates are not inflated by cache hits.
 
 Prints ONE JSON line.  `value` = 2*M*N*K per step / step time (whole layer,
 quantizer included); `roofline` is for the dominant kernel (the GEMM): its
-average launch duration over back-to-back launches after the timed steps,
-from HIP events recorded on the stream it runs on (`us_in_step` is the same
+average launch duration over back-to-back launches after the timed steps
+(captured once in a HIP graph and replayed, so that short kernels are not
+timed at the host's launch rate; `kernel_timing` says so), from HIP events
+recorded on the stream it runs on (`us_in_step` is the same
 kernel timed inside the steps, dispatch gaps included); for workloads with
 the RMSNorm front end, `quant_group` is the group quantizer alone over the
 same activations (not part of a step); `cpu_baseline` is the CPU oracle timed
@@ -82,6 +84,47 @@ def measured_traffic(workload: str):
     rec = t.get("workloads", {}).get(workload)
     return None if rec is None else rec.get("traffic_bytes")
 
+
+
+def launch_ms(fn, sets, reps, stream, record):
+    """Mean duration of one launch of fn over `reps` back-to-back launches
+    (rotating buffer sets), from HIP events recorded on the launch stream.
+    The launches are captured once in a HIP graph and the graph is replayed,
+    so that a kernel shorter than the host's launch interval is timed on the
+    GPU's clock rather than at the host's launch rate; if capture fails the
+    launches are issued eagerly.  `record["kernel_timing"]` says which."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = len(sets)
+    for i in range(min(reps, n)):
+        fn(sets[i % n])
+    torch.cuda.synchronize()
+    try:
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.graph(graph, stream=side):
+            for i in range(reps):
+                fn(sets[i % n])
+        torch.cuda.synchronize()
+        graph.replay()                               # first replay: warm
+        torch.cuda.synchronize()
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        record.setdefault("kernel_timing", "graph replay of back-to-back launches")
+        del graph
+        return e0.elapsed_time(e1) / reps
+    except RuntimeError:
+        torch.cuda.synchronize()
+        record["kernel_timing"] = "eager back-to-back launches (graph capture failed)"
+    e0.record(stream)
+    for i in range(reps):
+        fn(sets[i % n])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
 
 def main() -> int:
     args = parse()
@@ -230,17 +273,9 @@ def main() -> int:
     # timed with HIP events recorded on the stream it runs on; back-to-back
     # launches keep the dispatch gap out of the average, as in a kernel trace.
     def timed(fn, reps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        for i in range(min(reps, nsets)):
-            fn(sets[i % nsets])
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for i in range(reps):
-            fn(sets[i % nsets])
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps
+        return launch_ms(fn, sets, reps, stream, timing)
 
+    timing = {}
     reps = max(args.steps, 2 * nsets)
     quant_ms = timed(quant, reps)
     gemm_ms = timed(gemm, reps)
@@ -292,6 +327,7 @@ def main() -> int:
                   "us_in_step": round(step_quant_ms * 1e3, 2)},
         "cpu_baseline": None,
     }
+    out["kernel_timing"] = timing.get("kernel_timing")
     if wl.norm and not pow2:
         # the group quantizer on its own (no norm in front) over the same
         # activations, for its HBM fraction on this shape; not part of a step
@@ -361,17 +397,9 @@ def moe_main(args, wl) -> int:
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
 
     def timed(fn, reps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        for i in range(min(reps, nsets)):
-            fn(sets[i % nsets])
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for i in range(reps):
-            fn(sets[i % nsets])
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps
+        return launch_ms(fn, sets, reps, stream, timing)
 
+    timing = {}
     reps = max(args.steps, 2 * nsets)
     quant_ms = timed(quant, reps)
     gemm_ms = timed(gemm, reps)
@@ -400,6 +428,7 @@ def moe_main(args, wl) -> int:
                   "frac_hbm": round(quant_gbps / PEAK_HBM_GBPS, 4), "algorithmic_bytes": q_bytes},
         "cpu_baseline": None,
     }
+    out["kernel_timing"] = timing.get("kernel_timing")
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = moe_cpu_baseline(wl, x.cpu(), off, args.cpu_seconds)
     print(json.dumps(out), flush=True)
