@@ -123,10 +123,49 @@ __device__ __forceinline__ float max_wave(float v) {
   return __uint_as_float(u);
 }
 
+// fp64 value of a DPP partner lane (both 32-bit halves moved alike)
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = dpp_u<CTRL>((uint32_t)u), hi = dpp_u<CTRL>((uint32_t)(u >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// v plus the value of the partner lane in the other 16-lane row of a row
+// pair (HALF32 false) or in the other half of the wave (HALF32 true), via
+// the lane-swap instructions (VALU, no LDS round trip)
+template <bool HALF32>
+__device__ __forceinline__ double add_swapped_f64(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)u, hi = (uint32_t)(u >> 32);
+  uint32_t plo, phi;
+  if constexpr (HALF32) {
+    const auto sl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const auto sh = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    const bool upper = (threadIdx.x & 32) != 0;
+    plo = upper ? sl[0] : sl[1];
+    phi = upper ? sh[0] : sh[1];
+  } else {
+    const auto sl = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto sh = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    const bool odd = (threadIdx.x & 16) != 0;
+    plo = odd ? sl[0] : sl[1];
+    phi = odd ? sh[0] : sh[1];
+  }
+  return v + __longlong_as_double((long long)(((uint64_t)phi << 32) | plo));
+}
+
+// Sum over the 64-lane wave, the same bits in every lane: each step adds a
+// lane's value and its partner's (fp64 addition is commutative, so partners
+// compute the same sum): quads, half-rows and rows by DPP, then row pairs
+// and wave halves by lane swaps.
 __device__ __forceinline__ double sum_wave_f64(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v += dpp_f64<0xB1>(v);     // quad_perm [1,0,3,2]
+  v += dpp_f64<0x4E>(v);     // quad_perm [2,3,0,1]
+  v += dpp_f64<0x141>(v);    // row_half_mirror
+  v += dpp_f64<0x140>(v);    // row_mirror
+  v = add_swapped_f64<false>(v);
+  return add_swapped_f64<true>(v);
 }
 
 // ------------------------------------------------------------- work mapping
