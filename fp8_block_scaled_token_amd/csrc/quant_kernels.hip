@@ -43,28 +43,32 @@ __device__ __forceinline__ float absmax8(const uint4& raw) {
 }
 
 // Group scales of a wave segment.  amax[c] holds, in every lane of 16-lane
-// row g, the max of group 4c + g.  Lane j < 4*CH receives group j and computes
-// s = fp32(max(amax, 1e-10) / 448) and r = fp32(1 / s) with IEEE division;
-// s_mine is that value (lane j), s[c] / r[c] the scale of this lane's own
-// group in chunk c.
+// row g, the max of group 4c + g, and every lane computes the scale of that
+// group itself, s = fp32(max(amax, 1e-10) / 448), and its reciprocal
+// r = fp32(1 / s), without a division or a lane exchange:
+//   s0 = RN(a * RN(1/448)), refined by its exact residual a - 448 s0 (FMA);
+//   r from the hardware reciprocal of s, refined by one Newton step (FMAs).
+// amax is a bf16 value or the floor, a set of ~20600 inputs; a host test runs
+// every one of them (with every reciprocal estimate within 2 ulp) and finds
+// both results equal to the IEEE quotients.  s_mine: the scale that lane l
+// stores, that of chunk l % 16 (lanes with l % 16 < CH; see
+// store_group_scales).
 template <int CH>
 __device__ __forceinline__ void group_scales(const float (&amax)[CH], float (&s)[CH],
                                              float (&r)[CH], float& s_mine) {
-  static_assert(4 * CH <= 64, "one lane per group");
-  const int lane = threadIdx.x & 63;
-  float g = 0.0f;
+  static_assert(CH <= 16, "one lane per group");
+  constexpr float kInv448 = 1.0f / kFp8Max;           // RN(1/448), folded at compile time
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
-    const float v = __shfl(amax[c], (lane & 3) << 4);
-    if ((lane >> 2) == c) g = v;
-  }
-  const float sg = fmaxf(g, kAmaxFloor) / kFp8Max;   // IEEE division
-  const float rg = 1.0f / sg;                         // IEEE division
-  s_mine = sg;
-#pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    s[c] = __shfl(sg, 4 * c + (lane >> 4));
-    r[c] = __shfl(rg, 4 * c + (lane >> 4));
+    const float a = fmaxf(amax[c], kAmaxFloor);
+    const float s0 = a * kInv448;
+    const float e = __builtin_fmaf(-s0, kFp8Max, a);
+    s[c] = __builtin_fmaf(e, kInv448, s0);
+    const float r0 = __builtin_amdgcn_rcpf(s[c]);
+    const float t = __builtin_fmaf(-s[c], r0, 1.0f);
+    r[c] = __builtin_fmaf(r0, t, r0);
+    // (selected here, with constant indices, so that s stays in registers)
+    if (c == 0 || (int)(threadIdx.x & 15) == c) s_mine = s[c];
   }
 }
 
@@ -106,27 +110,25 @@ __device__ __forceinline__ uint2 quant8_mx(const uint4& raw, uint32_t byte) {
 
 // Power-of-two group scales (the MX exponent rule on 128-wide groups):
 // amax[c] as in group_scales; byte[c] is the UE8M0 byte of this lane's group
-// in chunk c, s_mine (lane j < 4*CH) the fp32 scale 2^(byte-127) of group j.
+// in chunk c, s_mine the fp32 scale 2^(byte-127) that lane l stores (chunk
+// l % 16, as in group_scales).
 template <int CH>
 __device__ __forceinline__ void pow2_group_scales(const float (&amax)[CH], uint32_t (&byte)[CH], float& s_mine) {
-  const int lane = threadIdx.x & 63;
-  uint32_t b = 127u;
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     byte[c] = ue8m0_byte(amax[c]);
-    const uint32_t v = (uint32_t)__shfl((int)byte[c], (lane & 3) << 4);
-    if ((lane >> 2) == c) b = v;
+    if (c == 0 || (int)(threadIdx.x & 15) == c) s_mine = __uint_as_float(byte[c] << 23);
   }
-  s_mine = __uint_as_float(b << 23);
 }
 
-// Store the wave's group scales: lane j < 4*CH holds group first_group + j.
+// Store the wave's group scales: lane l with c = l % 16 < CH holds the scale
+// of group first_group + 4c + l / 16 (chunk c, 16-lane row l / 16).
 template <int CH>
 __device__ __forceinline__ void store_group_scales(float* scales, float s_mine, int64_t first_group,
                                                    int64_t G, int64_t M, int64_t row, int col_major) {
-  const int lane = threadIdx.x & 63;
-  const int64_t g = first_group + lane;
-  if (lane < 4 * CH && g < G) {
+  const int lane = threadIdx.x & 63, c = lane & 15;
+  const int64_t g = first_group + 4 * c + (lane >> 4);
+  if (c < CH && g < G) {
     if (col_major) scales[g * M + row] = s_mine;
     else scales[row * G + g] = s_mine;
   }

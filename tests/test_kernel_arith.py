@@ -45,3 +45,82 @@ def test_requant_product_round_to_odd_is_exact_rounding():
     ro, rn = _round_odd_product(A, Mm)
     assert np.array_equal(e4m3.encode(ro.astype(np.float64)), exact)
     assert not np.array_equal(e4m3.encode(rn.astype(np.float64)), exact)
+
+
+# --------------------------------------------------------------------------
+# Group scale and its reciprocal without a division.  The quantizers compute,
+# in every lane, s = fp32(max(amax, 1e-10) / 448) and r = fp32(1 / s) for the
+# group whose maximum the lane holds, as
+#     s0 = RN(a * C), C = RN(1/448);  e = RN(a - s0 * 448)  (one FMA);
+#     s  = RN(s0 + e * C)                                    (one FMA);
+#     r0 = hardware reciprocal of s (within an ulp or two);
+#     t  = RN(1 - s * r0) (one FMA);  r = RN(r0 + r0 * t)   (one FMA).
+# amax is a bf16 value (the maximum of bf16 inputs) or the fp32 floor, so
+# the check below covers every input the sequence can see: each positive
+# finite bf16 value >= 1e-10 and the floor, with every reciprocal estimate
+# within 2 ulp of RN(1/s).  Rationals are exact; RN is round-to-nearest-even
+# to fp32.
+
+from fractions import Fraction as _Fr
+import math as _math
+
+
+def _rn32(q: _Fr) -> _Fr:
+    """q rounded to the nearest fp32 value (ties to even), q in the normal range."""
+    if q == 0:
+        return _Fr(0)
+    sign = -1 if q < 0 else 1
+    q = abs(q)
+    e = _math.floor(_math.log2(q.numerator) - _math.log2(q.denominator))
+    while _Fr(2) ** e > q:
+        e -= 1
+    while _Fr(2) ** (e + 1) <= q:
+        e += 1
+    ulp = _Fr(2) ** (e - 23)
+    m = q / ulp
+    lo = _math.floor(m)
+    rem = m - lo
+    if rem > _Fr(1, 2) or (rem == _Fr(1, 2) and lo % 2 == 1):
+        lo += 1
+    return sign * lo * ulp
+
+
+def _amax_values():
+    vals = {np.float32(1e-10)}
+    for e in range(-40, 128):
+        for m in range(128):
+            a = np.float32((1 + m / 128) * 2.0 ** e)
+            if a >= np.float32(1e-10) and np.isfinite(a):
+                vals.add(a)
+    return sorted(vals)
+
+
+def _neighbours(x: np.float32, k: int):
+    out, up, dn = [x], x, x
+    for _ in range(k):
+        up = np.nextafter(up, np.float32(np.inf))
+        dn = np.nextafter(dn, np.float32(0))
+        out += [up, dn]
+    return out
+
+
+def test_group_scale_and_reciprocal_without_division_are_exact():
+    C = _rn32(_Fr(1, 448))
+    vals = _amax_values()
+    assert len(vals) > 20000 and max(vals) == np.float32(3.3895314e38)
+    plain_wrong = 0
+    for a32 in vals:
+        a = _Fr(float(a32))
+        s_ref = _rn32(a / 448)
+        s0 = _rn32(a * C)
+        plain_wrong += s0 != s_ref
+        e = _rn32(a - s0 * 448)
+        s = _rn32(s0 + e * C)
+        assert s == s_ref, float(a32)
+        r_ref = _rn32(1 / s)
+        for r0_32 in _neighbours(np.float32(float(r_ref)), 2):
+            r0 = _Fr(float(r0_32))
+            t = _rn32(1 - s * r0)
+            assert _rn32(r0 + r0 * t) == r_ref, (float(a32), float(r0_32))
+    # the refinement step is needed: the plain product is wrong for many amax
+    assert plain_wrong > 1000
