@@ -10,6 +10,7 @@ import pytest
 import torch
 
 from oracle import e4m3, gemm, quant
+from tests.exact_arith import rn32_quotient
 
 
 def _encode_ties_away(v):
@@ -53,7 +54,7 @@ def _check_group_invariants(qfun):
     dq = np.abs(e4m3.decode(q)).reshape(32, 4, 128).max(axis=2)
     assert np.all(dq == 448.0)
     amax = np.abs(x).reshape(32, 4, 128).max(axis=2)
-    np.testing.assert_allclose(s, amax / 448.0, rtol=2.0 ** -23)
+    np.testing.assert_array_equal(np.asarray(s, np.float64), rn32_quotient(amax, np.float32(448.0)))
     # equivariance under powers of two
     q2, s2 = qfun(np.ldexp(x, 3))
     np.testing.assert_array_equal(q2, q)
@@ -279,3 +280,33 @@ def test_grouped_offset_mistake_is_caught(monkeypatch):
     monkeypatch.setattr(gemm, "gemm_grouped_blockscale", shifted)
     with pytest.raises(AssertionError):
         pins.test_grouped_gemm_against_per_expert_dequantized_products(0)
+
+
+# ------------------------------------------- the two quotients of the quantizer
+
+def _group_scale_reciprocal(amax):
+    # amax * RN32(1/448) instead of the division amax / 448
+    a = np.maximum(np.asarray(amax, np.float32), np.float32(1e-10))
+    return (a * (np.float32(1) / np.float32(448))).astype(np.float32)
+
+
+def _quantize_reciprocal(x, s):
+    # x * RN32(1/s) instead of the division x / s
+    x = np.asarray(x, np.float32)
+    s = np.asarray(s, np.float32)
+    t = (x * (np.float32(1) / s).astype(np.float32)).astype(np.float32)
+    return e4m3.encode(np.clip(t, -448, 448))
+
+
+def test_group_scale_reciprocal_is_caught():
+    from tests.test_oracle_exact import check_group_scale
+    check_group_scale(quant.group_scale)
+    with pytest.raises(AssertionError):
+        check_group_scale(_group_scale_reciprocal)
+
+
+def test_quantize_reciprocal_is_caught():
+    from tests.test_oracle_exact import check_quantize_with_scale
+    check_quantize_with_scale(quant.quantize_with_scale)
+    with pytest.raises(AssertionError):
+        check_quantize_with_scale(_quantize_reciprocal)

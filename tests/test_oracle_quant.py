@@ -13,6 +13,7 @@ import pytest
 import torch
 
 from oracle import bf16, e4m3, quant
+from tests.exact_arith import rn32_quotient
 
 GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_facts.json")))
 
@@ -54,8 +55,9 @@ def test_group_error_bound():
 def test_group_scale_equals_amax_over_448():
     x = _bf16_data((16, 512), 2)
     _, s = quant.quant_group(x)
-    amax = np.abs(x).reshape(16, 4, 128).max(axis=2).astype(np.float64)
-    np.testing.assert_allclose(s, amax / 448.0, rtol=2.0 ** -23)
+    amax = np.abs(x).reshape(16, 4, 128).max(axis=2)
+    # the correctly rounded fp32 quotient, from exact rational arithmetic
+    np.testing.assert_array_equal(s.astype(np.float64), rn32_quotient(amax, np.float32(448.0)))
 
 
 def test_group_identity_on_representable_inputs():
@@ -93,7 +95,7 @@ def test_group_zero_group_uses_floor():
     x = np.zeros((2, 256), np.float32)
     x[1, 200] = 3.0
     q, s = quant.quant_group(x)
-    floor_scale = np.float32(np.float32(1e-10) / np.float32(448))
+    floor_scale = np.float32(rn32_quotient(np.float32(1e-10), np.float32(448.0)))
     assert s[0, 0] == floor_scale and s[0, 1] == floor_scale and s[1, 0] == floor_scale
     assert np.all(q[0] == 0) and np.all(q[1, :128] == 0)
     assert q[1, 200] == 0x7E
