@@ -11,6 +11,7 @@ place of pointers, sizes read from the tensors).  The short-named helpers
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional
@@ -18,7 +19,7 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "load_library", "FP8QError", "abi_version",
+    "load_library", "FP8QError", "abi_version", "fp8q_set_plan_override", "plan_override",
     "fp8q_quant_act_group", "fp8q_rmsnorm_quant", "fp8q_add_rmsnorm_quant", "fp8q_quant_weight_block",
     "fp8q_requant_weight_pow2", "fp8q_gemm_blockscale", "fp8q_gemm_blockscale_splitk",
     "fp8q_gemm_splitk_workspace_size", "fp8q_gemm_grouped_blockscale", "fp8q_gemm_mxfp8",
@@ -44,6 +45,7 @@ _P, _I64, _I32, _F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_f
 SIGNATURES = {
     "fp8q_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "fp8q_abi_version": (ctypes.c_int, []),
+    "fp8q_set_plan_override": (ctypes.c_int, [_I32, _I32, _I32, _I32]),
     "fp8q_quant_act_group": (ctypes.c_int, [_P, _I64, _I64, _I64, _I32, _I32, _I32, _P, _P, _I64, _P, _P]),
     "fp8q_rmsnorm_quant": (ctypes.c_int, [_P, _P, _F, _I64, _I64, _I64, _I32, _P, _I64, _P, _P, _I64, _P]),
     "fp8q_add_rmsnorm_quant": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _I64, _P, _F, _I64, _I64, _I32, _I32, _P, _P,
@@ -85,6 +87,23 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
 
 def abi_version() -> int:
     return load_library().fp8q_abi_version()
+
+
+def fp8q_set_plan_override(gemm_cfg: int = -1, gemm_slots: int = 0, gemm_split: int = 1,
+                           decode_wide: int = -1) -> None:
+    """Force GEMM launch plans process-wide (defaults: automatic plans)."""
+    _check(load_library().fp8q_set_plan_override(gemm_cfg, gemm_slots, gemm_split, decode_wide),
+           "fp8q_set_plan_override")
+
+
+@contextlib.contextmanager
+def plan_override(gemm_cfg: int = -1, gemm_slots: int = 0, gemm_split: int = 1, decode_wide: int = -1):
+    """fp8q_set_plan_override for the duration of a with-block."""
+    fp8q_set_plan_override(gemm_cfg, gemm_slots, gemm_split, decode_wide)
+    try:
+        yield
+    finally:
+        fp8q_set_plan_override()
 
 
 def _ptr(t: Optional[torch.Tensor]):

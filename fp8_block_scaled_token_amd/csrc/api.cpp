@@ -69,6 +69,9 @@ constexpr int64_t kMaxK = int64_t(1) << 30;
 
 std::atomic<int> g_cu_count[kMaxDevices];
 
+// fp8q_set_plan_override's values (automatic plans by default)
+std::atomic<int> g_ov_cfg{-1}, g_ov_slots{0}, g_ov_split{1}, g_ov_wide{-1};
+
 }  // namespace
 
 namespace fp8q {
@@ -85,6 +88,11 @@ int device_cu_count() {
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
   if (dev < kMaxDevices) g_cu_count[dev].store(n, std::memory_order_relaxed);
   return n;
+}
+
+PlanOverride plan_override() {
+  return {g_ov_cfg.load(std::memory_order_relaxed), g_ov_slots.load(std::memory_order_relaxed),
+          g_ov_split.load(std::memory_order_relaxed), g_ov_wide.load(std::memory_order_relaxed)};
 }
 
 }  // namespace fp8q
@@ -106,6 +114,18 @@ const char* fp8q_status_string(fp8q_status_t s) {
 }
 
 int fp8q_abi_version(void) { return FP8Q_ABI_VERSION; }
+
+fp8q_status_t fp8q_set_plan_override(int32_t gemm_cfg, int32_t gemm_slots, int32_t gemm_split,
+                                     int32_t decode_wide) {
+  if (gemm_cfg < -1 || gemm_cfg > 1 || gemm_slots < 0 || gemm_slots > 4096 || gemm_split < 0 ||
+      gemm_split > 1 || decode_wide < -1 || decode_wide > 1)
+    return FP8Q_ERR_VALUE;
+  g_ov_cfg.store(gemm_cfg, std::memory_order_relaxed);
+  g_ov_slots.store(gemm_slots, std::memory_order_relaxed);
+  g_ov_split.store(gemm_split, std::memory_order_relaxed);
+  g_ov_wide.store(decode_wide, std::memory_order_relaxed);
+  return FP8Q_OK;
+}
 
 fp8q_status_t fp8q_quant_act_group(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                    int32_t group_size, int32_t fmt, int32_t layout,

@@ -339,12 +339,12 @@ void launch_dec(const GemmArgs& p, hipStream_t stream, int splits = 1) {
 // Column tiles per workgroup and ring depth: six column tiles (96
 // channels) when that still gives every CU a workgroup, else two (more
 // workgroups, deeper rings); fewer where the rings would not fit in LDS.
-// Test override, read at every call: FP8Q_DECODE_WIDE=1/0 forces the six or
+// plan_override().decode_wide (fp8q_set_plan_override) may force the six or
 // the two column-tile configuration.
 template <int MODE, int TM>
 void launch_dec_tm(const GemmArgs& p, hipStream_t stream) {
-  const char* env = getenv("FP8Q_DECODE_WIDE");
-  const bool wide = env ? atoi(env) != 0 : p.N >= 96 * device_cu_count();
+  const int forced = plan_override().decode_wide;
+  const bool wide = forced >= 0 ? forced != 0 : p.N >= 96 * device_cu_count();
   if (wide) {
     if constexpr (TM <= 3) launch_dec<MODE, TM, 6, 2>(p, stream);
     else launch_dec<MODE, TM, 4, 2>(p, stream);

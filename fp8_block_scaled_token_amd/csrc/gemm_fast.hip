@@ -36,7 +36,6 @@
 //    ahead so that the LDS loads find them in L2.
 // Preconditions (checked by the launcher): K % 128 == 0, every operand and
 // scale array smaller than 2^31 bytes, M > 64.
-#include <cstdlib>
 #include <utility>
 
 #include <atomic>
@@ -814,16 +813,10 @@ namespace {
 
 // Configuration 0: 256 x 256 tiles, 8 waves, one workgroup per CU.
 // Configuration 1: 128 x 128 tiles, 4 waves, two workgroups per CU.
-// Tuning and test overrides, read at every call: FP8Q_GEMM_CFG=0/1 forces a
-// configuration, FP8Q_GEMM_SPLIT=0 disables the half-tile tail balancing,
-// FP8Q_GEMM_SLOTS=n plans for n CUs instead of the device's count.
-int env_int(const char* name, int dflt) {
-  const char* e = getenv(name);
-  return e ? atoi(e) : dflt;
-}
-
+// plan_override() (fp8q_set_plan_override) may force a configuration,
+// disable the tail balancing, or plan for another CU count.
 int cu_count() {
-  const int forced = env_int("FP8Q_GEMM_SLOTS", 0);
+  const int forced = plan_override().gemm_slots;
   return forced > 0 ? forced : device_cu_count();
 }
 
@@ -862,8 +855,9 @@ double plan_cost(const Plan& pl, int cus) {
 }
 
 Plan choose_plan(const GemmArgs& p) {
-  const int forced = env_int("FP8Q_GEMM_CFG", -1);
-  const bool split = env_int("FP8Q_GEMM_SPLIT", 1) != 0;
+  const PlanOverride ov = plan_override();
+  const int forced = ov.gemm_cfg;
+  const bool split = ov.gemm_split != 0;
   const int cus = cu_count();
   const Plan big = plan_cfg(p, 0, cus, split), small = plan_cfg(p, 1, 2 * cus, split);
   if (forced == 0) return big;
@@ -938,7 +932,8 @@ hipError_t launch_gemm_grouped(GemmArgs p, const int32_t* offsets, int E, int64_
   // of c rows takes ceil(c/256) tiles of 256 or ceil(c/128) of 128, and just
   // above 128 rows the second 128-row tile is nearly empty yet re-reads the
   // expert's whole weight (measured: 291 against 333 us at 129 rows).
-  const int cfg = env_int("FP8Q_GEMM_CFG", (int64_t)p.M >= 112 * (int64_t)E ? 0 : 1) == 0 ? 0 : 1;
+  const int forced = plan_override().gemm_cfg;
+  const int cfg = forced >= 0 ? forced : ((int64_t)p.M >= 112 * (int64_t)E ? 0 : 1);
   const int bm = cfg == 0 ? 256 : 128;
   p.tiles_n = (p.N + bm - 1) / bm;
   p.tiles_m = 0;

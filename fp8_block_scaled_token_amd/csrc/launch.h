@@ -9,6 +9,13 @@ namespace fp8q {
 // Compute units of the current device (cached per device).
 int device_cu_count();
 
+// Launch-plan override (fp8q_set_plan_override): gemm_cfg -1/0/1,
+// gemm_slots 0 or a CU count to plan for, gemm_split 0/1, decode_wide -1/0/1.
+struct PlanOverride {
+  int gemm_cfg, gemm_slots, gemm_split, decode_wide;
+};
+PlanOverride plan_override();
+
 // pow2: power-of-two fp32 scales (MX exponent rule on 128-wide groups)
 hipError_t launch_quant_group128(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                  uint8_t* q, int64_t ldq, float* scales, int col_major, int pow2,

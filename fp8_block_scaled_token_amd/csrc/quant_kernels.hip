@@ -22,10 +22,13 @@
 // elements [seg0 + 512c + 8l, +8): every load instruction of the wave reads one
 // contiguous kilobyte, and the 16 lanes of a DPP row hold exactly one
 // 128-element group (4 lanes hold one 32-element MX block), so group maxima
-// are DPP reductions.  The wave's 4*CH group scales are then computed once,
-// lane j handling group j (two IEEE divisions per wave instead of per lane
-// and chunk), and handed back with lane permutes; the same lanes store the
-// scales, so row-major scale writes are one coalesced store.  Segments that
+// are DPP reductions that leave the maximum in every lane of the row.  Every
+// lane then computes the scale s and its reciprocal r of its own groups
+// itself, without a division and without a lane exchange (group_scales: a
+// product refined by its exact FMA residual, and the hardware reciprocal
+// refined by a Newton step, both equal to the IEEE quotients), and lane l
+// stores the scale of chunk l % 16 of its DPP row (store_group_scales), so
+// the wave's row-major scales go out as one coalesced store.  Segments that
 // lie wholly inside the row take an unmasked path; only a row's last segment
 // masks.  Quantization is HBM-bound: every lane issues all CH loads first.
 #include "device_common.h"

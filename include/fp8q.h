@@ -40,10 +40,13 @@
  *   memory-safe) outputs.
  * Determinism.  No atomics on floating-point data and fixed reduction
  *   orders: repeated calls give identical bits.  Calls are re-entrant across
- *   streams and host threads: the only process-wide mutable state is a
- *   per-device cache of the architecture and of kernel occupancies (filled
- *   once) and an atomic launch counter that numbers split-K launches; the
- *   split-K workspace is the caller's and serves one launch at a time.
+ *   streams and host threads.  The only process-wide mutable state is:
+ *   a per-device cache of the architecture and of kernel occupancies
+ *   (filled once); an atomic launch counter that numbers split-K launches
+ *   (the split-K workspace is the caller's and serves one launch at a time);
+ *   and the launch-plan override set by fp8q_set_plan_override (tuning and
+ *   tests; it changes tile shapes and splits, never the formula).  Nothing is
+ *   read from the environment.
  */
 #ifndef FP8Q_H
 #define FP8Q_H
@@ -55,7 +58,7 @@
 extern "C" {
 #endif
 
-#define FP8Q_ABI_VERSION 2
+#define FP8Q_ABI_VERSION 3
 
 typedef enum {
   FP8Q_OK = 0,
@@ -81,6 +84,28 @@ const char* fp8q_status_string(fp8q_status_t s);
 
 /* FP8Q_ABI_VERSION of the loaded library. */
 int fp8q_abi_version(void);
+
+/*
+ * fp8q_set_plan_override -- force a GEMM launch plan (tuning and tests).
+ *
+ * The GEMM entry points choose tile shapes and tail splits from the problem
+ * shape and the device's compute-unit count.  This call overrides that choice
+ * for every later call in the process (all devices, all threads) until it is
+ * called again; the results stay within the same bound (only the summation
+ * order can change), so the override exists to pin each kernel variant in
+ * tests and to measure them.  Calling it while another thread launches GEMMs
+ * races with those launches.
+ *   gemm_cfg     -1 automatic; 0: 256 x 256 prefill tiles; 1: 128 x 128 tiles
+ *                (fp8q_gemm_blockscale[_splitk], fp8q_gemm_mxfp8, grouped GEMM).
+ *   gemm_slots   0: plan for the device's CU count; n > 0: plan the persistent
+ *                grid and its tail as if the device had n CUs.
+ *   gemm_split   1 (default): balance a half-empty last round of tiles; 0: off.
+ *   decode_wide  -1 automatic; 1: 96-channel decode column tiles; 0: 32-channel.
+ * fp8q_set_plan_override(-1, 0, 1, -1) restores the automatic plans.
+ * Errors: a value outside these ranges -> FP8Q_ERR_VALUE (nothing changed).
+ */
+fp8q_status_t fp8q_set_plan_override(int32_t gemm_cfg, int32_t gemm_slots, int32_t gemm_split,
+                                     int32_t decode_wide);
 
 /*
  * fp8q_quant_act_group -- dynamic per-token-group activation quantization.

@@ -27,3 +27,12 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture
+def plan():
+    """Force GEMM launch plans for one test: plan(gemm_cfg=..., gemm_slots=...,
+    gemm_split=..., decode_wide=...); the automatic plans are restored after."""
+    import fp8_block_scaled_token_amd as fq
+    yield fq.fp8q_set_plan_override
+    fq.fp8q_set_plan_override()

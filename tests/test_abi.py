@@ -48,7 +48,7 @@ def test_binding_covers_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.fp8q_abi_version() == 2
+    assert lib.fp8q_abi_version() == 3
     for s in range(8):
         assert len(lib.fp8q_status_string(s)) > 0
     assert lib.fp8q_status_string(99) == b"unknown status"
@@ -251,3 +251,22 @@ def test_quantizer_division_sequence_exhaustive(tmp_path):
     print(r.stdout)
     assert r.returncode == 0, r.stdout
     assert "fatal=0" in r.stdout
+
+
+def test_plan_override_validation(lib):
+    f = lib.fp8q_set_plan_override
+    try:
+        assert f(2, 0, 1, -1) == 7 and f(-2, 0, 1, -1) == 7         # gemm_cfg
+        assert f(-1, -1, 1, -1) == 7                                 # gemm_slots
+        assert f(-1, 0, 2, -1) == 7 and f(-1, 0, 1, 2) == 7          # split, decode_wide
+        assert f(1, 64, 0, 1) == 0 and f(0, 0, 1, 0) == 0
+    finally:
+        assert f(-1, 0, 1, -1) == 0
+
+
+def test_library_reads_no_environment():
+    # the launch plans come only from arguments and fp8q_set_plan_override
+    src = os.path.join(ROOT, "fp8_block_scaled_token_amd", "csrc")
+    for name in os.listdir(src):
+        text = open(os.path.join(src, name)).read()
+        assert "getenv" not in text and "secure_getenv" not in text, name

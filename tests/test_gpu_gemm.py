@@ -145,9 +145,9 @@ def test_gemm_mxfp8_parity(M, N, K):
 @pytest.mark.parametrize("M,N,K", [(100, 640, 7168), (260, 1028, 1024), (2048, 7168, 1024), (516, 2052, 2048),
                                    (1540, 4096, 512)])
 @pytest.mark.parametrize("cfg", [0, 1])
-def test_gemm_mxfp8_col_major_scales(monkeypatch, M, N, K, cfg):
+def test_gemm_mxfp8_col_major_scales(plan, M, N, K, cfg):
     log(f"gemm_mxfp8 col-major M={M} N={N} K={K} cfg={cfg}")
-    monkeypatch.setenv("FP8Q_GEMM_CFG", str(cfg))
+    plan(gemm_cfg=cfg)
     m = fq()
     x = workloads.activations(M, K, seed=K + 17, outlier_frac=0.001)
     w = workloads.weights(N, K, seed=K + 18, std=1.0)

@@ -2,8 +2,8 @@
 
 The decode kernel streams weights through per-wave LDS rings; its
 configuration (six or two 16-column tiles per workgroup, ring depth) depends
-on N and the CU count, so the launcher's override FP8Q_DECODE_WIDE (read at
-every call) pins each one here.  Shapes cover every row-tile count (M 1..64),
+on N and the CU count, so fp8q_set_plan_override (decode_wide) pins each
+one here.  Shapes cover every row-tile count (M 1..64),
 fewer K blocks than waves (K = 128, 384), ragged N (columns past the end of
 the last tile) and both activation-scale layouts, in block, per-tensor and
 MX scale modes.  Expected values come from the oracle; the tolerance is the
@@ -47,9 +47,9 @@ def _operands(M, N, K, seed):
 @pytest.mark.parametrize("M,N,K", SHAPES)
 @pytest.mark.parametrize("wide", [0, 1])
 @pytest.mark.parametrize("a_layout", [0, 1])
-def test_decode_blockscale(monkeypatch, M, N, K, wide, a_layout):
+def test_decode_blockscale(plan, M, N, K, wide, a_layout):
     log(f"decode block M={M} N={N} K={K} wide={wide} layout={a_layout}")
-    monkeypatch.setenv("FP8Q_DECODE_WIDE", str(wide))
+    plan(decode_wide=wide)
     m = fq()
     x, w = _operands(M, N, K, 90 + M)
     qa, sa = oq.quant_group(x)
@@ -68,9 +68,9 @@ def test_decode_blockscale(monkeypatch, M, N, K, wide, a_layout):
 
 @pytest.mark.parametrize("M,N,K", SHAPES[:4])
 @pytest.mark.parametrize("wide", [0, 1])
-def test_decode_pertensor(monkeypatch, M, N, K, wide):
+def test_decode_pertensor(plan, M, N, K, wide):
     log(f"decode per-tensor M={M} N={N} K={K} wide={wide}")
-    monkeypatch.setenv("FP8Q_DECODE_WIDE", str(wide))
+    plan(decode_wide=wide)
     m = fq()
     x, w = _operands(M, N, K, 120 + M)
     sx = np.float32(np.float32(np.abs(x).max()) / np.float32(448.0))
@@ -87,9 +87,9 @@ def test_decode_pertensor(monkeypatch, M, N, K, wide):
 
 @pytest.mark.parametrize("M,N,K", SHAPES[1:])
 @pytest.mark.parametrize("wide", [0, 1])
-def test_decode_mxfp8(monkeypatch, M, N, K, wide):
+def test_decode_mxfp8(plan, M, N, K, wide):
     log(f"decode mx M={M} N={N} K={K} wide={wide}")
-    monkeypatch.setenv("FP8Q_DECODE_WIDE", str(wide))
+    plan(decode_wide=wide)
     m = fq()
     x, w = _operands(M, N, K, 150 + M)
     qa, ea = oq.quant_mx(x)
@@ -103,9 +103,9 @@ def test_decode_mxfp8(monkeypatch, M, N, K, wide):
     check_gemm_rows(bf16_bits(y), yr, f"decode mx M={M} wide={wide}", REL)
 
 
-def test_decode_deterministic(monkeypatch):
+def test_decode_deterministic(plan):
     # fixed-order reduction of the waves' partial sums: identical bits twice
-    monkeypatch.setenv("FP8Q_DECODE_WIDE", "1")
+    plan(decode_wide=1)
     m = fq()
     M, N, K = 32, 1536, 6144
     x, w = _operands(M, N, K, 181)

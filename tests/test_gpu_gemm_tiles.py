@@ -2,8 +2,8 @@
 
 The fast kernel has two tile configurations (256x256 and 128x128) and splits
 the last, partly filled round of tiles into half-height tiles.  The plan
-depends on the CU count; the launcher's overrides (FP8Q_GEMM_CFG,
-FP8Q_GEMM_SLOTS, FP8Q_GEMM_SPLIT, read at every call) pin it here so that
+depends on the CU count; fp8q_set_plan_override (configuration, CU count
+to plan for, tail split) pins it here so that
 each configuration runs with and without split tiles on shapes the oracle
 finishes quickly.  Ragged M and N put rows and columns past the ends inside
 split tiles.  Expected values come from the oracle; the tolerance is the
@@ -42,10 +42,8 @@ def _dev_u8(a: np.ndarray, k: int) -> torch.Tensor:
     return buf[:, :k]
 
 
-def _plan(monkeypatch, cfg, slots, split):
-    monkeypatch.setenv("FP8Q_GEMM_CFG", str(cfg))
-    monkeypatch.setenv("FP8Q_GEMM_SLOTS", str(slots))
-    monkeypatch.setenv("FP8Q_GEMM_SPLIT", str(split))
+def _plan(plan, cfg, slots, split):
+    plan(gemm_cfg=cfg, gemm_slots=slots, gemm_split=split)
 
 
 @pytest.fixture(scope="module")
@@ -64,9 +62,9 @@ def _out():
 
 @pytest.mark.parametrize("cfg,slots,split", PLANS)
 @pytest.mark.parametrize("a_layout", [0, 1])
-def test_tiles_blockscale(monkeypatch, operands, cfg, slots, split, a_layout):
+def test_tiles_blockscale(plan, operands, cfg, slots, split, a_layout):
     log(f"tiles block cfg={cfg} slots={slots} split={split} layout={a_layout}")
-    _plan(monkeypatch, cfg, slots, split)
+    _plan(plan, cfg, slots, split)
     m = fq()
     o = operands
     sa = o["sa"].T if a_layout else o["sa"]
@@ -81,9 +79,9 @@ def test_tiles_blockscale(monkeypatch, operands, cfg, slots, split, a_layout):
 
 
 @pytest.mark.parametrize("cfg,slots,split", PLANS)
-def test_tiles_pertensor(monkeypatch, operands, cfg, slots, split):
+def test_tiles_pertensor(plan, operands, cfg, slots, split):
     log(f"tiles per-tensor cfg={cfg} slots={slots} split={split}")
-    _plan(monkeypatch, cfg, slots, split)
+    _plan(plan, cfg, slots, split)
     m = fq()
     o = operands
     sx = np.float32(np.float32(np.abs(o["x"]).max()) / np.float32(448.0))
@@ -99,9 +97,9 @@ def test_tiles_pertensor(monkeypatch, operands, cfg, slots, split):
 
 
 @pytest.mark.parametrize("cfg,slots,split", PLANS)
-def test_tiles_mxfp8(monkeypatch, operands, cfg, slots, split):
+def test_tiles_mxfp8(plan, operands, cfg, slots, split):
     log(f"tiles mx cfg={cfg} slots={slots} split={split}")
-    _plan(monkeypatch, cfg, slots, split)
+    _plan(plan, cfg, slots, split)
     m = fq()
     o = operands
     qa, ea = oq.quant_mx(o["x"])
@@ -116,13 +114,13 @@ def test_tiles_mxfp8(monkeypatch, operands, cfg, slots, split):
     check_gemm_rows(bf16_bits(y), yr, f"mx cfg={cfg} split={split}", REL)
 
 
-def test_tiles_split_matches_unsplit(monkeypatch, operands):
+def test_tiles_split_matches_unsplit(plan, operands):
     # a split tile computes the same sums in the same order: identical bits
     o = operands
     m = fq()
     outs = []
     for split in (0, 1):
-        _plan(monkeypatch, 0, 6, split)
+        _plan(plan, 0, 6, split)
         y = m.gemm_blockscale(_dev_u8(o["qa"], K), torch.from_numpy(o["sa"]).cuda(), _dev_u8(o["qw"], K),
                               torch.from_numpy(o["sw"]).cuda())
         torch.cuda.synchronize()

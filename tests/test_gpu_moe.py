@@ -85,10 +85,10 @@ CASES = [
 @pytest.mark.parametrize("case", range(len(CASES)))
 @pytest.mark.parametrize("cfg", [0, 1])
 @pytest.mark.parametrize("a_layout", [0, 1])
-def test_grouped_blockscale_parity(monkeypatch, case, cfg, a_layout):
+def test_grouped_blockscale_parity(plan, case, cfg, a_layout):
     counts, N, K, shard = CASES[case]
     log(f"grouped block counts={counts} N={N} K={K} shard={shard} cfg={cfg} layout={a_layout}")
-    monkeypatch.setenv("FP8Q_GEMM_CFG", str(cfg))
+    plan(gemm_cfg=cfg)
     qa, sa, qw, sw, off = _problem(counts, N, K, 11 + case, shard)
     y = _run(qa, sa, qw, sw, off, shard, a_layout, fq().GRAN_BLOCK128)
     yr = og.gemm_grouped_blockscale(qa, sa, qw, sw, off, shard=shard)
@@ -97,10 +97,10 @@ def test_grouped_blockscale_parity(monkeypatch, case, cfg, a_layout):
 
 @pytest.mark.parametrize("case", [0, 3, 5])
 @pytest.mark.parametrize("cfg", [0, 1])
-def test_grouped_pow2_parity(monkeypatch, case, cfg):
+def test_grouped_pow2_parity(plan, case, cfg):
     counts, N, K, shard = CASES[case]
     log(f"grouped pow2 counts={counts} N={N} K={K} shard={shard} cfg={cfg}")
-    monkeypatch.setenv("FP8Q_GEMM_CFG", str(cfg))
+    plan(gemm_cfg=cfg)
     qa, sa, qw, sw, off = _problem(counts, N, K, 31 + case, shard, pow2=True)
     y = _run(qa, sa, qw, sw, off, shard, 1, fq().GRAN_BLOCK128_POW2)
     yr = og.gemm_grouped_blockscale(qa, sa, qw, sw, off, shard=shard)
