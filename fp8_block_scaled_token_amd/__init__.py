@@ -45,7 +45,7 @@ _P, _I64, _I32, _F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_f
 SIGNATURES = {
     "fp8q_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "fp8q_abi_version": (ctypes.c_int, []),
-    "fp8q_set_plan_override": (ctypes.c_int, [_I32, _I32, _I32, _I32]),
+    "fp8q_set_plan_override": (ctypes.c_int, [_I32, _I32, _I32, _I32, _I32, _I32]),
     "fp8q_quant_act_group": (ctypes.c_int, [_P, _I64, _I64, _I64, _I32, _I32, _I32, _P, _P, _I64, _P, _P]),
     "fp8q_rmsnorm_quant": (ctypes.c_int, [_P, _P, _F, _I64, _I64, _I64, _I32, _P, _I64, _P, _P, _I64, _P]),
     "fp8q_add_rmsnorm_quant": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _I64, _P, _F, _I64, _I64, _I32, _I32, _P, _P,
@@ -90,16 +90,18 @@ def abi_version() -> int:
 
 
 def fp8q_set_plan_override(gemm_cfg: int = -1, gemm_slots: int = 0, gemm_split: int = 1,
-                           decode_wide: int = -1) -> None:
+                           decode_wide: int = -1, split_wait_limit: int = -1,
+                           split_publish_delay: int = 0) -> None:
     """Force GEMM launch plans process-wide (defaults: automatic plans)."""
-    _check(load_library().fp8q_set_plan_override(gemm_cfg, gemm_slots, gemm_split, decode_wide),
+    _check(load_library().fp8q_set_plan_override(gemm_cfg, gemm_slots, gemm_split, decode_wide,
+                                                 split_wait_limit, split_publish_delay),
            "fp8q_set_plan_override")
 
 
 @contextlib.contextmanager
-def plan_override(gemm_cfg: int = -1, gemm_slots: int = 0, gemm_split: int = 1, decode_wide: int = -1):
-    """fp8q_set_plan_override for the duration of a with-block."""
-    fp8q_set_plan_override(gemm_cfg, gemm_slots, gemm_split, decode_wide)
+def plan_override(**kw):
+    """fp8q_set_plan_override(**kw) for the duration of a with-block."""
+    fp8q_set_plan_override(**kw)
     try:
         yield
     finally:

@@ -70,7 +70,7 @@ constexpr int64_t kMaxK = int64_t(1) << 30;
 std::atomic<int> g_cu_count[kMaxDevices];
 
 // fp8q_set_plan_override's values (automatic plans by default)
-std::atomic<int> g_ov_cfg{-1}, g_ov_slots{0}, g_ov_split{1}, g_ov_wide{-1};
+std::atomic<int> g_ov_cfg{-1}, g_ov_slots{0}, g_ov_split{1}, g_ov_wide{-1}, g_ov_wait{-1}, g_ov_delay{0};
 
 }  // namespace
 
@@ -91,8 +91,9 @@ int device_cu_count() {
 }
 
 PlanOverride plan_override() {
-  return {g_ov_cfg.load(std::memory_order_relaxed), g_ov_slots.load(std::memory_order_relaxed),
-          g_ov_split.load(std::memory_order_relaxed), g_ov_wide.load(std::memory_order_relaxed)};
+  return {g_ov_cfg.load(std::memory_order_relaxed),   g_ov_slots.load(std::memory_order_relaxed),
+          g_ov_split.load(std::memory_order_relaxed), g_ov_wide.load(std::memory_order_relaxed),
+          g_ov_wait.load(std::memory_order_relaxed),  g_ov_delay.load(std::memory_order_relaxed)};
 }
 
 }  // namespace fp8q
@@ -116,14 +117,18 @@ const char* fp8q_status_string(fp8q_status_t s) {
 int fp8q_abi_version(void) { return FP8Q_ABI_VERSION; }
 
 fp8q_status_t fp8q_set_plan_override(int32_t gemm_cfg, int32_t gemm_slots, int32_t gemm_split,
-                                     int32_t decode_wide) {
+                                     int32_t decode_wide, int32_t split_wait_limit,
+                                     int32_t split_publish_delay) {
   if (gemm_cfg < -1 || gemm_cfg > 1 || gemm_slots < 0 || gemm_slots > 4096 || gemm_split < 0 ||
-      gemm_split > 1 || decode_wide < -1 || decode_wide > 1)
+      gemm_split > 1 || decode_wide < -1 || decode_wide > 1 || split_wait_limit < -1 ||
+      split_publish_delay < 0 || split_publish_delay > 10000)
     return FP8Q_ERR_VALUE;
   g_ov_cfg.store(gemm_cfg, std::memory_order_relaxed);
   g_ov_slots.store(gemm_slots, std::memory_order_relaxed);
   g_ov_split.store(gemm_split, std::memory_order_relaxed);
   g_ov_wide.store(decode_wide, std::memory_order_relaxed);
+  g_ov_wait.store(split_wait_limit, std::memory_order_relaxed);
+  g_ov_delay.store(split_publish_delay, std::memory_order_relaxed);
   return FP8Q_OK;
 }
 
@@ -310,7 +315,7 @@ fp8q_status_t fp8q_gemm_blockscale_splitk(const uint8_t* a, int64_t lda, const f
   FP8Q_TRY(check_matrix(y, N, ldy, 2));
   if (a_scales == nullptr || w_scale_inv == nullptr) return FP8Q_ERR_NULL;
   if ((reinterpret_cast<uintptr_t>(a_scales) & 3u) || (reinterpret_cast<uintptr_t>(w_scale_inv) & 3u) ||
-      (reinterpret_cast<uintptr_t>(workspace) & 3u))
+      (reinterpret_cast<uintptr_t>(workspace) & 7u))
     return FP8Q_ERR_MISALIGNED;
   if (bias != nullptr && (reinterpret_cast<uintptr_t>(bias) & 1u)) return FP8Q_ERR_MISALIGNED;
   FP8Q_TRY(check_device());

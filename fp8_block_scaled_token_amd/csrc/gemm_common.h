@@ -40,8 +40,10 @@ struct GemmArgs {
   int shard_blocks;     // ceil(shard / 128)
   int split_kb;         // split-K: K blocks per split (0: no split); split s = blockIdx.y
   float* partial;       // split-K: fp32 partial sums [splits][M][N] (row stride N); split
-                        // tail tiles: 256 KB per leftover tile, then a flag word each
-  uint32_t nonce;       // split tail tiles: this launch's flag value
+                        // tail tiles: 256 KB per leftover tile, then an 8-byte exchange word each
+  uint32_t tag;         // split tail tiles: this launch's exchange tag (never 0)
+  int wait_limit;       // split tail tiles: polls before the second K half stops waiting
+  int publish_delay;    // split tail tiles: sleeps before publishing (tests only; normally 0)
 };
 
 // Weight scale row of output channel j: j / 128, or with stacked shards

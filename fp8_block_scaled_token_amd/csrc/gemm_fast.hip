@@ -89,7 +89,10 @@ struct FastTile {
   // 1 KB per wave: sink for prefetch touches and for loads past the last K
   // block, so that those never write a stage
   static constexpr int SINK_OFF = NS * STAGE;
-  static constexpr int LDS_BYTES = SINK_OFF + NW * 1024;
+  // a split tail tile's consumer decision (one word, broadcast to all waves)
+  static constexpr int XCH_OFF = SINK_OFF + NW * 1024;
+  static constexpr int LDS_BYTES = XCH_OFF + 16;
+  static_assert(LDS_BYTES <= 160 * 1024, "fits the CU's LDS");
   // scale loads: one 64-word load per wave covers the BM + BN scale words
   static constexpr int SCALE_LOADS = MODE == MODE_TENSOR ? 0 : 1;
   static_assert(NW * 64 == BM + BN, "one scale word per lane");
@@ -105,10 +108,11 @@ struct FastTile {
 // first K block of the next tile (nm0, nn0, ngm, ngn; same kind) before this
 // tile's epilogue, so that its latency overlaps the output stores.
 // K range of a tile and, for the two K halves of a split tail tile, how the
-// halves meet: the producer stores its fp32 accumulators to `part` and raises
-// `flag` to `nonce`; the consumer waits for that (bounded), adds the partial
-// as first half + second half (a fixed order whichever workgroup consumes)
-// and writes the output.
+// halves meet (the exchange below): the producer (the lower-numbered
+// workgroup of the pair) publishes its fp32 accumulators to `part`; the
+// consumer adds that partial as first half + second half (a fixed order,
+// whichever half each holds) and writes the output -- or, if the partial
+// does not appear within the wait limit, computes the whole tile itself.
 // Cache policy bits of a buffer access (SC0 | SC1): system scope, i.e. a
 // store writes through to memory and a load misses the caches.
 constexpr int kCacheSystem = 1 | 16;
@@ -116,17 +120,44 @@ constexpr int kCacheSystem = 1 | 16;
 struct TileK {
   int kb0, kb1;        // K blocks [kb0, kb1)
   int next_kb0;        // first K block of the next tile (issued early when has_next)
-  int role;            // 0: whole tile, 1: producer, 2: consumer
+  int role;            // 0: whole tile, 1: producer, 2: consumer (the two K halves of a tile)
   int first;           // this workgroup holds the first K half
-  float* part;         // 256 KB slot of the pair
-  uint32_t* flag;
-  uint32_t nonce;
+  float* part;         // 256 KB partial slot of the pair
+  uint64_t* flags;     // the pair's two flag words: [0] producer's, [1] consumer's
+  uint32_t tag;        // this launch's tag (never 0)
 };
 
-// NTW: weight loads carry the non-temporal hint (the grouped GEMM, whose
-// expert weights are read once per launch; the dense kernel re-reads them).
+// Flag words of a split tail tile pair.  Only system-scope loads and stores
+// touch them (each completes at memory; no read-modify-write), so the two
+// workgroups, on different XCDs, agree without a coherent cache:
+//   producer: partial -> memory, then flags[0] = PUBLISHED; then it reads
+//             flags[1] and, if the consumer has given up, resets both words;
+//   consumer: waits (bounded) for flags[0] == PUBLISHED and then resets it;
+//             past the limit it writes flags[1] = GAVE_UP, reads flags[0]
+//             once more, and either consumes after all (resetting both) or
+//             computes the whole tile itself.
+// Each side's store completes before its next read, so at least one of
+// them sees the other's word: either the consumer finds the partial or the
+// producer finds the give-up (or both; both then reset both words).  The
+// last one to act leaves both words 0, so a graph replay, which reuses the
+// tag, starts from a clean state.  A word counts only if it holds this
+// launch's tag and marker: whatever else the workspace held is ignored.
+constexpr uint32_t kPublished = 0x5AFE0001u, kGaveUp = 0x5AFE0002u;
+__device__ __forceinline__ uint64_t flag_word(uint32_t tag, uint32_t marker) {
+  return ((uint64_t)tag << 32) | marker;
+}
+__device__ __forceinline__ void flag_store(uint64_t* w, uint64_t v) {
+  __hip_atomic_store(w, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ uint64_t flag_load(uint64_t* w) {
+  return __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// Returns true when this workgroup, the consumer of a split tail tile, gave
+// up waiting for its partner's partial: nothing was written, and the caller
+// then computes the whole tile (the producer writes no output either).
 template <class T, bool HALF, bool SPLIT, bool NTW = false>
-__device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int m0, int n0, int gm, int gn,
+__device__ __forceinline__ bool fast_tile(const GemmArgs& p, uint8_t* smem, int m0, int n0, int gm, int gn,
                                           bool preloaded, bool has_next, int nm0, int nn0, int ngm, int ngn,
                                           const TileK& tk) {
   constexpr int MODE = T::MODE, BM = T::BM, BN = T::BN, WN = T::WN, NW = T::NW;
@@ -343,13 +374,12 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
   uint32_t sav[TM] = {}, swb[TN] = {};    // activation / weight scale words
   float swv = 0.f;                        // block mode: this wave's weight scale
   int swe = 127;                          // power-of-two view: its exponent byte
-  auto load_regs = [&](int st) {
+  // the weight fragments and the scales of the block in stage st
+  auto read_w = [&](int st) {
     const uint8_t* a = smem + st * STAGE;
     const uint8_t* w = a + ABYTES;
 #pragma unroll
     for (int j = 0; j < TN; ++j) fb[j] = read_frag(w, brow + 16 * j);
-#pragma unroll
-    for (int i = 0; i < LA; ++i) fr[i] = read_frag(a, arow + 16 * i);
     if constexpr (MXC) {
       // [sub-block][row] bytes: this lane's sub-block lq, its rows
 #pragma unroll
@@ -370,14 +400,17 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
     if constexpr (MODE == MODE_BMX)
       swe = (int)((reinterpret_cast<const uint32_t*>(a + SW_OFF)[wn] >> 23) & 0xFFu);
   };
+  auto load_regs = [&](int st) {
+    read_w(st);
+    const uint8_t* a = smem + st * STAGE;
+#pragma unroll
+    for (int i = 0; i < LA; ++i) fr[i] = read_frag(a, arow + 16 * i);
+  };
 
   // The MFMAs (and block-mode folds) of 16-row tile i of the block in stage
   // st; the activation fragment of tile i + LA is read meanwhile.
-  auto tile = [&](auto I, int st) {
+  auto mfma_tile = [&](auto I, const Frag& fa) {
     constexpr int i = decltype(I)::value;
-    const uint8_t* a = smem + st * STAGE;
-    if constexpr (i + LA < TM) fr[(i + LA) % (LA + 1)] = read_frag(a, arow + 16 * (i + LA));
-    const Frag& fa = fr[i % (LA + 1)];
     if constexpr (MODE == MODE_BLOCK) {
       // fold column tile j of the previous 16-row tile (its MFMA was issued
       // TN MFMAs ago), then reuse its registers for this tile's product
@@ -411,6 +444,12 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
       for (int j = 0; j < TN; ++j)
         acc[i][j] = mfma_mx(fb[j].v, fa.v, acc[i][j], (int)((swb[j] >> sh) & 0xFF), sab);
     }
+  };
+  auto tile = [&](auto I, int st) {
+    constexpr int i = decltype(I)::value;
+    const uint8_t* a = smem + st * STAGE;
+    if constexpr (i + LA < TM) fr[(i + LA) % (LA + 1)] = read_frag(a, arow + 16 * (i + LA));
+    mfma_tile(I, fr[i % (LA + 1)]);
   };
 
   // Main loop.  Block kb sits in stage kb % 2 and block kb + 1 is being
@@ -495,44 +534,57 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
   // consumer).
   // (SPLIT: only the kernel that may split its tail carries this code, so
   // the others keep their registers.)
-  const bool producer = SPLIT && tk.role == 1, consumer = SPLIT && tk.role == 2;
+  bool consumer = false;
   const int vo = (wave * TM * TN * 64 + lane) * 16;
   int m_end = p.m_end;
-  if (SPLIT && tk.role != 0) {
-    // The partial and the flag are written through to memory (system-scope
-    // cache policy) and read back with loads that miss the caches, so the
-    // two workgroups (on different XCDs, whose L2s are not coherent) meet
-    // without an L2 write-back.  Every wave waits for its own stores to
-    // complete before the barrier; thread 0 raises the flag after it.
-    if (producer) {
-      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(tk.part, 0, T::BM * T::BN * 4, 0x00020000);
+  if (SPLIT && tk.role == 1) {
+    // The partial is written through to memory (system-scope cache policy)
+    // and read back with loads that miss the caches, so the two workgroups
+    // (on different XCDs, whose L2s are not coherent) meet without an L2
+    // write-back; every wave waits for its own stores before the barrier
+    // after which thread 0 raises the flag.
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(tk.part, 0, T::BM * T::BN * 4, 0x00020000);
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), rs, vo, (i * TN + j) * 1024,
-                                                 kCacheSystem);
-      wait_vmcnt<0>();
-    }
+      for (int j = 0; j < TN; ++j)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), rs, vo, (i * TN + j) * 1024,
+                                               kCacheSystem);
+    wait_vmcnt<0>();
     __syncthreads();
     if (threadIdx.x == 0) {
-      if (producer) {
-        __hip_atomic_store(tk.flag, tk.nonce, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-      } else {
-        // bounded wait: the producer runs in the same round and never waits
-        // itself; past the limit the tile is finished without its partner
-        for (int n = 0; n < (1 << 22); ++n) {
-          if (__hip_atomic_load(tk.flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == tk.nonce) break;
-          __builtin_amdgcn_s_sleep(2);
-        }
-        // the consumer is the flag's only reader: clear it, so that a launch
-        // replayed with the same nonce (a captured graph) never finds it set
-        // before its own producer has run
-        __hip_atomic_store(tk.flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      // a bounded delay before publishing, only when the launch plan asks
+      // for one (tests of the give-up path)
+      for (int n = 0; n < p.publish_delay; ++n) __builtin_amdgcn_s_sleep(127);
+      flag_store(tk.flags, flag_word(tk.tag, kPublished));
+      wait_vmcnt<0>();
+      if (flag_load(tk.flags + 1) == flag_word(tk.tag, kGaveUp)) {
+        flag_store(tk.flags, 0);
+        flag_store(tk.flags + 1, 0);
       }
     }
+    m_end = 0;                            // the consumer writes the output
+  } else if (SPLIT && tk.role == 2) {
+    int* decision = reinterpret_cast<int*>(smem + T::XCH_OFF);
+    if (threadIdx.x == 0) {
+      const uint64_t pub = flag_word(tk.tag, kPublished);
+      bool seen = flag_load(tk.flags) == pub;
+      for (int n = 0; !seen && n < p.wait_limit; ++n) {
+        __builtin_amdgcn_s_sleep(2);
+        seen = flag_load(tk.flags) == pub;
+      }
+      if (!seen) {
+        flag_store(tk.flags + 1, flag_word(tk.tag, kGaveUp));
+        wait_vmcnt<0>();
+        seen = flag_load(tk.flags) == pub;
+        if (seen) flag_store(tk.flags + 1, 0);
+      }
+      if (seen) flag_store(tk.flags, 0);
+      *decision = seen ? 1 : 0;
+    }
     __syncthreads();
-    if (producer) m_end = 0;              // the consumer writes the output
+    if (*decision == 0) return true;      // compute the whole tile instead
+    consumer = true;
   }
   // the consumer's partner partial, read in the epilogue one 16-row tile at
   // a time; -0 is added instead elsewhere
@@ -621,23 +673,25 @@ __device__ __forceinline__ void fast_tile(const GemmArgs& p, uint8_t* smem, int 
       }
     }
   }
+  return false;
 }
 
 // Work items [0, full) are whole tiles (in XCD-contiguous group order); the
 // remaining tiles of that order are split into two half-height tiles, items
 // [full, items) -- or, with `ksplit` (a workspace in p.partial), into their
 // two K halves: items full + 2t and full + 2t + 1 are the first and second
-// K half of leftover tile t, and the workgroup with the lower index of the
-// pair hands its partial sums to the other (see TileK).  The kernel is
-// persistent: workgroup g takes items g, g + G, g + 2G, ... (G = gridDim.x,
-// at most one workgroup per slot), so the workgroups of a round start
-// together and keep their XCD (item % 8), and no workgroup is launched per
-// tile.  Between two tiles no barrier is needed: a wave issues the next
-// tile's first LDS writes only after the last K-loop barrier of the previous
-// tile, after which nobody reads a stage, and the next tile's first barrier
-// waits for every wave.  A split pair's items are the last of their
-// workgroups (the tail is one round), and the lower-index workgroup of a
-// pair never waits, so the waits cannot form a cycle.
+// K half of leftover tile t, which meet through the pair's partial slot and
+// exchange word (see TileK).  The kernel is persistent: workgroup g takes
+// items g, g + G, g + 2G, ... (G = gridDim.x, at most one workgroup per
+// slot), so the workgroups of a round start together and keep their XCD
+// (item % 8), and no workgroup is launched per tile.  Between two tiles no
+// barrier is needed: a wave issues the next tile's first LDS writes only
+// after the last K-loop barrier of the previous tile, after which nobody
+// reads a stage, and the next tile's first barrier waits for every wave.  A
+// split pair's items are the last of their workgroups (the tail is one
+// round), and the lower-index workgroup of a pair never waits, so the
+// waits cannot form a cycle; the other stops waiting after p.wait_limit
+// polls and then computes the whole tile itself.
 template <class T, bool KSPLIT>
 __global__ __launch_bounds__(T::NW * 64) void gemm_fast_kernel(GemmArgs p, int full, int items) {
   constexpr bool ksplit = KSPLIT;
@@ -669,6 +723,7 @@ __global__ __launch_bounds__(T::NW * 64) void gemm_fast_kernel(GemmArgs p, int f
   const int half_kb = p.KB / 2;
   const int tails = (items - full) / 2;
   bool preloaded = false;
+  int redo_m0 = -1, redo_n0 = 0, redo_gm = 0, redo_gn = 0;
   for (int b = blockIdx.x; b < items; b += G) {
     int m0, n0, gm, gn, nm0 = 0, nn0 = 0, ngm = 0, ngn = 0;
     const int kind = decode(b, m0, n0, gm, gn);
@@ -687,14 +742,25 @@ __global__ __launch_bounds__(T::NW * 64) void gemm_fast_kernel(GemmArgs p, int f
       tk.first = !second;
       tk.role = (int)blockIdx.x < partner % G ? 1 : 2;
       tk.part = p.partial + (int64_t)t * (T::BM * T::BN);
-      tk.flag = reinterpret_cast<uint32_t*>(p.partial + (int64_t)tails * (T::BM * T::BN)) + t;
-      tk.nonce = p.nonce;
+      tk.flags = reinterpret_cast<uint64_t*>(p.partial + (int64_t)tails * (T::BM * T::BN)) + 2 * t;
+      tk.tag = p.tag;
     }
+    bool redo;
     if (kind == 1)
-      fast_tile<T, true, KSPLIT>(p, smem, m0, n0, gm, gn, preloaded, has_next, nm0, nn0, ngm, ngn, tk);
+      redo = fast_tile<T, true, KSPLIT>(p, smem, m0, n0, gm, gn, preloaded, has_next, nm0, nn0, ngm, ngn, tk);
     else
-      fast_tile<T, false, KSPLIT>(p, smem, m0, n0, gm, gn, preloaded, has_next, nm0, nn0, ngm, ngn, tk);
+      redo = fast_tile<T, false, KSPLIT>(p, smem, m0, n0, gm, gn, preloaded, has_next, nm0, nn0, ngm, ngn, tk);
+    if (KSPLIT && redo) {
+      redo_m0 = m0; redo_n0 = n0; redo_gm = gm; redo_gn = gn;
+    }
     preloaded = has_next;
+  }
+  if (KSPLIT && redo_m0 >= 0) {
+    // the partner's half did not appear in time: the whole tile here (a K
+    // half is its workgroup's last item, so nothing was issued early and
+    // nothing follows)
+    const TileK whole{0, p.KB, 0, 0, 1, nullptr, nullptr, 0u};   // role 0: a whole tile
+    fast_tile<T, false, false>(p, smem, redo_m0, redo_n0, redo_gm, redo_gn, false, false, 0, 0, 0, 0, whole);
   }
   // the last touches and past-the-end loads still write the LDS sink: let
   // them land before the workgroup ends
@@ -798,7 +864,7 @@ __global__ __launch_bounds__(T::NW * 64) void gemm_grouped_kernel(GemmArgs p, Gr
     pe.w = p.w + e * g.w_stride;
     pe.sw = static_cast<const float*>(p.sw) + e * g.sw_stride;
     pe.m_end = __builtin_amdgcn_readfirstlane(row_end(e));
-    const TileK tk{0, p.KB, 0, 0, 0, nullptr, nullptr, 0u};
+    const TileK tk{0, p.KB, 0, 0, 1, nullptr, nullptr, 0u};
     if (half)
       fast_tile<T, true, false, true>(pe, smem, m0, n0, gm, gn, preloaded, has_next, nm0, nn0, ngm, ngn, tk);
     else
@@ -866,17 +932,17 @@ Plan choose_plan(const GemmArgs& p) {
 }
 
 // Workspace of the split tail (configuration 0 only): 256 x 256 fp32 per
-// leftover tile, then one flag word each; 0 when the plan has no tail, or
+// leftover tile, then two 8-byte flag words each; 0 when the plan has no tail, or
 // when K is below 32 blocks: the exchange of a 256 KB partial costs about
 // what half of a short K loop saves (measured: 4096x6144x6144 158 -> 146 us,
 // 2560x7168x2048 55 -> 58 us).
 size_t tail_workspace(const Plan& pl, const GemmArgs& p) {
   const int tail = pl.tiles_m * pl.tiles_n - pl.full;
   if (pl.cfg != 0 || tail <= 0 || p.KB < 32) return 0;
-  return (size_t)tail * (256u * 256u * 4u + 4u);
+  return (size_t)tail * (256u * 256u * 4u + 16u);
 }
 
-std::atomic<uint32_t> g_nonce{0};
+std::atomic<uint32_t> g_tag{0};
 
 template <int MODE>
 void launch_plan(GemmArgs p, const Plan& pl, hipStream_t stream) {
@@ -887,12 +953,15 @@ void launch_plan(GemmArgs p, const Plan& pl, hipStream_t stream) {
   const int slots = (pl.cfg == 0 ? 1 : 2) * cu_count();
   const int grid = pl.grid < slots ? pl.grid : slots;
   // with a workspace, the leftover tiles are split along K instead of in
-  // half-height tiles; a fresh nonce per launch marks its flags
+  // half-height tiles; a fresh tag per launch marks its exchange words
   const int ksplit = p.partial != nullptr && tail_workspace(pl, p) > 0;
   if (ksplit) {
-    uint32_t n = ++g_nonce;
-    if (n == 0) n = ++g_nonce;
-    p.nonce = n;
+    uint32_t n = ++g_tag;
+    if (n == 0) n = ++g_tag;
+    p.tag = n;
+    const PlanOverride ov = plan_override();
+    p.wait_limit = ov.split_wait_limit >= 0 ? ov.split_wait_limit : (1 << 22);
+    p.publish_delay = ov.split_publish_delay;
   }
   if (pl.cfg == 0) {
     using T = FastTile<MODE, 256, 256, 2, 4, 4>;

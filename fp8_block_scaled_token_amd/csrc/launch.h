@@ -10,9 +10,10 @@ namespace fp8q {
 int device_cu_count();
 
 // Launch-plan override (fp8q_set_plan_override): gemm_cfg -1/0/1,
-// gemm_slots 0 or a CU count to plan for, gemm_split 0/1, decode_wide -1/0/1.
+// gemm_slots 0 or a CU count to plan for, gemm_split 0/1, decode_wide -1/0/1,
+// split_wait_limit -1 (default) or polls, split_publish_delay sleeps (0).
 struct PlanOverride {
-  int gemm_cfg, gemm_slots, gemm_split, decode_wide;
+  int gemm_cfg, gemm_slots, gemm_split, decode_wide, split_wait_limit, split_publish_delay;
 };
 PlanOverride plan_override();
 

@@ -101,11 +101,20 @@ int fp8q_abi_version(void);
  *                grid and its tail as if the device had n CUs.
  *   gemm_split   1 (default): balance a half-empty last round of tiles; 0: off.
  *   decode_wide  -1 automatic; 1: 96-channel decode column tiles; 0: 32-channel.
- * fp8q_set_plan_override(-1, 0, 1, -1) restores the automatic plans.
+ *   split_wait_limit     -1: the default wait of a split tail tile's second K
+ *                half for its partner's partial (2^22 polls); n >= 0: n polls.
+ *   split_publish_delay  0 (default); n in 1..10000: the first K half sleeps
+ *                n * ~3.4 us before publishing its partial.  With a short wait
+ *                limit this drives the second half into computing the whole
+ *                tile itself (the path taken if a partial never appeared);
+ *                the output is then correct to the same bound, though its bits
+ *                may differ from the split order's.
+ * fp8q_set_plan_override(-1, 0, 1, -1, -1, 0) restores the automatic plans.
  * Errors: a value outside these ranges -> FP8Q_ERR_VALUE (nothing changed).
  */
 fp8q_status_t fp8q_set_plan_override(int32_t gemm_cfg, int32_t gemm_slots, int32_t gemm_split,
-                                     int32_t decode_wide);
+                                     int32_t decode_wide, int32_t split_wait_limit,
+                                     int32_t split_publish_delay);
 
 /*
  * fp8q_quant_act_group -- dynamic per-token-group activation quantization.
@@ -286,18 +295,23 @@ fp8q_status_t fp8q_gemm_blockscale(const uint8_t* a, int64_t lda, const float* a
  *    share of the weight on otherwise idle CUs; a second kernel adds the
  *    partials in segment order 0, 1, ..., S-1;
  *  - prefill shapes whose last round of 256 x 256 tiles is at most half
- *    full: each leftover tile is computed as two K halves by two workgroups,
- *    one of which adds the other's fp32 partial (first half + second half)
- *    before the epilogue (it waits for it, bounded; the other never waits).
+ *    full: each leftover tile is computed as two K halves by two workgroups;
+ *    one publishes its fp32 partial, the other adds it (first half + second
+ *    half) before the epilogue.  The adding one waits for the partial only
+ *    up to a bound (the publishing one never waits); if the partial has not
+ *    appeared by then it computes the whole tile itself (correct to the same
+ *    bound; its bits may then differ from the split order's -- a path no
+ *    normal launch takes).
  * Both orders are fixed: repeated calls give identical bits.  Other shapes,
- * or a workspace too small, run the unsplit kernels.  The prefill split uses
- * one flag word per leftover tile in the workspace, raised to a per-launch
- * value and cleared again by the workgroup that reads it, so launches may be
+ * or a workspace too small, run the unsplit kernels.  The prefill split keeps
+ * two 8-byte flag words per leftover tile in the workspace, tagged with a
+ * per-launch value and reset to 0 by the last workgroup that uses them, so
+ * whatever the workspace held before does not matter and launches may be
  * captured in a graph and replayed; a workspace is used by one launch at a
  * time (launches that overlap on one workspace race).
  *
  *   Arguments as fp8q_gemm_blockscale (all three granularities), plus
- *   workspace  device memory for S * M * N fp32 partials (4-byte aligned),
+ *   workspace  device memory for S * M * N fp32 partials (8-byte aligned),
  *              owned by the caller, contents ignored and overwritten; NULL
  *              with workspace_bytes 0 means: never split.
  * fp8q_gemm_splitk_workspace_size returns the bytes the current device's

@@ -256,12 +256,14 @@ def test_quantizer_division_sequence_exhaustive(tmp_path):
 def test_plan_override_validation(lib):
     f = lib.fp8q_set_plan_override
     try:
-        assert f(2, 0, 1, -1) == 7 and f(-2, 0, 1, -1) == 7         # gemm_cfg
-        assert f(-1, -1, 1, -1) == 7                                 # gemm_slots
-        assert f(-1, 0, 2, -1) == 7 and f(-1, 0, 1, 2) == 7          # split, decode_wide
-        assert f(1, 64, 0, 1) == 0 and f(0, 0, 1, 0) == 0
+        assert f(2, 0, 1, -1, -1, 0) == 7 and f(-2, 0, 1, -1, -1, 0) == 7     # gemm_cfg
+        assert f(-1, -1, 1, -1, -1, 0) == 7                                    # gemm_slots
+        assert f(-1, 0, 2, -1, -1, 0) == 7 and f(-1, 0, 1, 2, -1, 0) == 7      # split, decode_wide
+        assert f(-1, 0, 1, -1, -2, 0) == 7                                     # wait limit
+        assert f(-1, 0, 1, -1, -1, -1) == 7 and f(-1, 0, 1, -1, -1, 10001) == 7   # publish delay
+        assert f(1, 64, 0, 1, 0, 5) == 0 and f(0, 0, 1, 0, -1, 0) == 0
     finally:
-        assert f(-1, 0, 1, -1) == 0
+        assert f(-1, 0, 1, -1, -1, 0) == 0
 
 
 def test_library_reads_no_environment():
@@ -270,3 +272,4 @@ def test_library_reads_no_environment():
     for name in os.listdir(src):
         text = open(os.path.join(src, name)).read()
         assert "getenv" not in text and "secure_getenv" not in text, name
+

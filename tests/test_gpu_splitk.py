@@ -137,3 +137,38 @@ def test_prefill_tail_split_parity(M, N, K, gran):
     check_gemm_rows(y[rows], yr, f"prefill split M={M} N={N} K={K}", REL)
     # fixed order, and the flags of the previous launch do not confuse the next
     np.testing.assert_array_equal(_call(qa, sa, qw, sw, gran, ws, bias, layout), y)
+
+
+@pytest.mark.parametrize("gran", [0, 2])
+def test_prefill_tail_give_up_computes_whole_tile(plan, gran):
+    """Forced from the host: the first K half of every leftover tile sleeps
+    (~100 us, bounded) before publishing and the second does not wait, so the
+    second computes the whole tile itself.  The output stays within the bound,
+    tiles outside the tail keep their bits, and the exchange words end at
+    their idle state: a normal launch afterwards gives the split bits again."""
+    m = fq()
+    M, N, K = 2304, 8192, 4096                       # 288 tiles: 32 leftover tiles as 64 K halves
+    nbytes = m.fp8q_gemm_splitk_workspace_size(M, N, K)
+    log(f"prefill tail give-up M={M} N={N} K={K} gran={gran} workspace={nbytes}")
+    assert nbytes > 0
+    ws = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    qa, sa, qw, sw, ref = _operands(M, N, K, gran, 7 + gran)
+    layout = 1
+    y_split = _call(qa, sa, qw, sw, gran, ws, None, layout)
+    plan(split_wait_limit=0, split_publish_delay=30)
+    y_alone = _call(qa, sa, qw, sw, gran, ws, None, layout)
+    plan()
+    y_again = _call(qa, sa, qw, sw, gran, ws, None, layout)
+    np.testing.assert_array_equal(y_again, y_split)
+    # the leftover tiles are the last tile row (rows 2048..2303): recomputed
+    # there in one accumulation order, elsewhere the same tiles as before
+    tail = slice(2048, M)
+    np.testing.assert_array_equal(y_alone[:2048], y_split[:2048])
+    if gran == 0:
+        # fp32 block scales round at every K block's rescale, so one
+        # accumulation order differs from the split order somewhere (with
+        # power-of-two scales the sums can be exact and the bits equal)
+        assert np.any(y_alone[tail] != y_split[tail]), "the give-up path was not taken"
+    rows = np.unique(np.r_[2048, M - 1, np.arange(2048, M, 23), 5, 1000])
+    yr = og.gemm_blockscale(qa, sa, qw, sw, rows=rows)[0]
+    check_gemm_rows(y_alone[rows], yr, f"prefill give-up M={M} N={N} K={K}", REL)

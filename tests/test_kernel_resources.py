@@ -12,10 +12,8 @@ import pytest
 
 from fp8_block_scaled_token_amd import build as B
 
-# kernels allowed a small scratch area (bytes per lane): the prefill kernel
-# variant that carries the split-tail exchange (a few spilled values outside
-# the K loop)
-ALLOWED = {r"gemm_fast_kernel.*ELb1E": 16}
+# kernels allowed a small scratch area (bytes per lane), by name pattern
+ALLOWED = {}
 
 
 def _usage(src):
