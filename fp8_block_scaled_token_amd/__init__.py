@@ -22,7 +22,8 @@ __all__ = [
     "load_library", "FP8QError", "abi_version", "fp8q_set_plan_override", "plan_override",
     "fp8q_quant_act_group", "fp8q_rmsnorm_quant", "fp8q_add_rmsnorm_quant", "fp8q_quant_weight_block",
     "fp8q_requant_weight_pow2", "fp8q_gemm_blockscale", "fp8q_gemm_blockscale_splitk",
-    "fp8q_gemm_splitk_workspace_size", "fp8q_gemm_grouped_blockscale", "fp8q_gemm_mxfp8",
+    "fp8q_gemm_splitk_workspace_size", "fp8q_gemm_blockscale_splitk_noalloc", "fp8q_gemm_grouped_blockscale",
+    "fp8q_gemm_mxfp8",
     "quant_act_group", "quant_act_group_pow2", "rmsnorm_quant_pow2", "quant_act_static", "quant_act_mx", "rmsnorm_quant", "add_rmsnorm_quant",
     "quant_weight_block", "quant_weight_block_pow2", "requant_weight_pow2", "quant_weight_mx", "quant_weight_tensor",
     "gemm_blockscale", "gemm_blockscale_pow2", "gemm_blockscale_splitk", "gemm_grouped_blockscale",
@@ -38,7 +39,7 @@ ROW_MAJOR, COL_MAJOR = 0, 1
 GRAN_BLOCK128, GRAN_PER_TENSOR, GRAN_BLOCK128_POW2 = 0, 1, 2
 
 _STATUS = {0: "ok", 1: "null", 2: "shape", 3: "unsupported", 4: "misaligned",
-           5: "device", 6: "launch", 7: "value"}
+           5: "device", 6: "launch", 7: "value", 8: "scratch"}
 
 #: exported symbol -> (restype, argtypes); mirrors include/fp8q.h
 _P, _I64, _I32, _F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
@@ -56,6 +57,8 @@ SIGNATURES = {
     "fp8q_gemm_splitk_workspace_size": (ctypes.c_size_t, [_I64, _I64, _I64]),
     "fp8q_gemm_blockscale_splitk": (ctypes.c_int, [_P, _I64, _P, _I32, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _I64,
                                                    _I32, _P, ctypes.c_size_t, _P]),
+    "fp8q_gemm_blockscale_splitk_noalloc": (ctypes.c_int, [_P, _I64, _P, _I32, _P, _I64, _P, _P, _P, _I64, _I64,
+                                                           _I64, _I64, _I32, _P]),
     "fp8q_gemm_grouped_blockscale": (ctypes.c_int, [_P, _I64, _P, _I32, _P, _I32, _P, _I64, _I64, _P, _I64, _P, _I64,
                                                     _I64, _I64, _I64, _I32, _P]),
     "fp8q_gemm_mxfp8": (ctypes.c_int, [_P, _I64, _P, _P, _I64, _P, _I32, _P, _P, _I64, _I64, _I64, _I64, _P]),
@@ -244,6 +247,21 @@ def fp8q_gemm_blockscale_splitk(a, a_scales, a_layout, w, w_scale_inv, bias, y, 
                                                       _ptr(w_scale_inv), _ptr(bias), _ptr(y), ldy, M, N, K, gran,
                                                       _ptr(workspace), ws_bytes, _stream(stream)),
            "fp8q_gemm_blockscale_splitk")
+
+
+def fp8q_gemm_blockscale_splitk_noalloc(a, a_scales, a_layout, w, w_scale_inv, bias, y, gran, stream=None):
+    """fp8q_gemm_blockscale_splitk with the library's own device scratch
+    (no workspace, nothing allocated)."""
+    a, w = _u8(a), _u8(w)
+    M, K, lda = _rows(a, torch.uint8, "a")
+    N, Kw, ldw = _rows(w, torch.uint8, "w")
+    My, Ny, ldy = _rows(y, torch.bfloat16, "y")
+    if Kw != K or (My, Ny) != (M, N):
+        raise ValueError("shape mismatch")
+    _check(load_library().fp8q_gemm_blockscale_splitk_noalloc(_ptr(a), lda, _ptr(a_scales), a_layout, _ptr(w),
+                                                              ldw, _ptr(w_scale_inv), _ptr(bias), _ptr(y), ldy, M,
+                                                              N, K, gran, _stream(stream)),
+           "fp8q_gemm_blockscale_splitk_noalloc")
 
 
 def fp8q_gemm_grouped_blockscale(a, a_scales, a_layout, expert_offsets, w, w_scale_inv, y, shard=0,

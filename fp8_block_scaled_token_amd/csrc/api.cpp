@@ -69,6 +69,23 @@ constexpr int64_t kMaxK = int64_t(1) << 30;
 
 std::atomic<int> g_cu_count[kMaxDevices];
 
+// Scratch of fp8q_gemm_blockscale_splitk_noalloc: one copy per GPU, held
+// until the process ends.  In host code `scratch` only names the symbol;
+// its device address comes from hipGetSymbolAddress (once per device, with
+// that device current) and is kept per device in g_scratch.
+__device__ __attribute__((aligned(256))) unsigned char scratch[FP8Q_SPLITK_SCRATCH_BYTES];
+std::atomic<void*> g_scratch[kMaxDevices];
+
+void* scratch_address(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  void* q = nullptr;
+  if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr) return nullptr;
+  g_scratch[dev].store(q, std::memory_order_release);
+  return q;
+}
+
 // fp8q_set_plan_override's values (automatic plans by default)
 std::atomic<int> g_ov_cfg{-1}, g_ov_slots{0}, g_ov_split{1}, g_ov_wide{-1}, g_ov_wait{-1}, g_ov_delay{0};
 
@@ -110,6 +127,7 @@ const char* fp8q_status_string(fp8q_status_t s) {
     case FP8Q_ERR_DEVICE: return "current HIP device is not gfx950 (or device query failed)";
     case FP8Q_ERR_LAUNCH: return "kernel launch failed";
     case FP8Q_ERR_VALUE: return "invalid scalar argument";
+    case FP8Q_ERR_SCRATCH: return "problem needs more split-K scratch than the allocation-free entry point holds";
   }
   return "unknown status";
 }
@@ -322,6 +340,35 @@ fp8q_status_t fp8q_gemm_blockscale_splitk(const uint8_t* a, int64_t lda, const f
   return launch_status(fp8q::launch_gemm_blockscale_splitk(
       a, lda, a_scales, a_layout == FP8Q_SCALES_COL_MAJOR, w, ldw, w_scale_inv, bias, y, ldy, M, N, K, gran,
       workspace, workspace_bytes, static_cast<hipStream_t>(stream)));
+}
+
+fp8q_status_t fp8q_gemm_blockscale_splitk_noalloc(const uint8_t* a, int64_t lda, const float* a_scales,
+                                                  int32_t a_layout, const uint8_t* w, int64_t ldw,
+                                                  const float* w_scale_inv, const uint16_t* bias,
+                                                  uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                                                  int32_t gran, void* stream) {
+  if (M < 0 || N < 0 || K <= 0 || M > kMaxRows || N > kMaxRows || K > kMaxK) return FP8Q_ERR_SHAPE;
+  if ((M / 128 + 1) * (N / 128 + 1) >= (int64_t(1) << 24)) return FP8Q_ERR_SHAPE;
+  if (gran != FP8Q_GRAN_BLOCK128 && gran != FP8Q_GRAN_PER_TENSOR && gran != FP8Q_GRAN_BLOCK128_POW2)
+    return FP8Q_ERR_UNSUPPORTED;
+  if (a_layout != FP8Q_SCALES_ROW_MAJOR && a_layout != FP8Q_SCALES_COL_MAJOR) return FP8Q_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return FP8Q_OK;
+  FP8Q_TRY(check_matrix(a, K, lda, 1));
+  FP8Q_TRY(check_matrix(w, K, ldw, 1));
+  FP8Q_TRY(check_matrix(y, N, ldy, 2));
+  if (a_scales == nullptr || w_scale_inv == nullptr) return FP8Q_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(a_scales) & 3u) || (reinterpret_cast<uintptr_t>(w_scale_inv) & 3u))
+    return FP8Q_ERR_MISALIGNED;
+  if (bias != nullptr && (reinterpret_cast<uintptr_t>(bias) & 1u)) return FP8Q_ERR_MISALIGNED;
+  FP8Q_TRY(check_device());
+  if (fp8q::gemm_splitk_workspace(M, N, K) > FP8Q_SPLITK_SCRATCH_BYTES) return FP8Q_ERR_SCRATCH;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return FP8Q_ERR_DEVICE;
+  void* ws = scratch_address(dev);
+  if (ws == nullptr) return FP8Q_ERR_DEVICE;
+  return launch_status(fp8q::launch_gemm_blockscale_splitk(
+      a, lda, a_scales, a_layout == FP8Q_SCALES_COL_MAJOR, w, ldw, w_scale_inv, bias, y, ldy, M, N, K, gran,
+      ws, FP8Q_SPLITK_SCRATCH_BYTES, static_cast<hipStream_t>(stream)));
 }
 
 fp8q_status_t fp8q_gemm_grouped_blockscale(const uint8_t* a, int64_t lda, const float* a_scales,

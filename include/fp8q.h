@@ -69,7 +69,9 @@ typedef enum {
   FP8Q_ERR_MISALIGNED = 4,   /* pointer or stride breaks the alignment rule     */
   FP8Q_ERR_DEVICE = 5,       /* current device is not gfx950, or HIP query failed */
   FP8Q_ERR_LAUNCH = 6,       /* HIP reported an error when launching            */
-  FP8Q_ERR_VALUE = 7         /* invalid scalar argument (e.g. eps <= 0)         */
+  FP8Q_ERR_VALUE = 7,        /* invalid scalar argument (e.g. eps <= 0)         */
+  FP8Q_ERR_SCRATCH = 8       /* the problem needs more scratch than the
+                                allocation-free entry point holds             */
 } fp8q_status_t;
 
 /* FP8Q_SCALE_F32_POW2: fp32 scales restricted to powers of two 2^e (e from the
@@ -324,6 +326,33 @@ fp8q_status_t fp8q_gemm_blockscale_splitk(const uint8_t* a, int64_t lda, const f
                                           uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K,
                                           int32_t gran, void* workspace, size_t workspace_bytes,
                                           void* stream);
+
+/*
+ * fp8q_gemm_blockscale_splitk_noalloc -- fp8q_gemm_blockscale_splitk without a
+ * caller workspace, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).
+ *
+ * The same kernels and split choice as fp8q_gemm_blockscale_splitk (hence
+ * the same bits); the partials and exchange words live in a device array of
+ * FP8Q_SPLITK_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends.  Nothing in it needs to start at zero.  The call
+ * allocates nothing (no hipMalloc, no hipFree).  Every call on one GPU shares
+ * that GPU's array: calls that overlap on one GPU (other streams, other
+ * threads) race and give undefined results; calls ordered on one stream are
+ * safe.
+ *   Arguments as fp8q_gemm_blockscale (all three granularities).
+ * Errors: as fp8q_gemm_blockscale_splitk, and FP8Q_ERR_SCRATCH (nothing
+ *   launched) when fp8q_gemm_splitk_workspace_size(M, N, K) exceeds
+ *   FP8Q_SPLITK_SCRATCH_BYTES; FP8Q_ERR_DEVICE if the array's address cannot
+ *   be obtained.
+ */
+#define FP8Q_SPLITK_SCRATCH_BYTES ((size_t)33 << 20)
+fp8q_status_t fp8q_gemm_blockscale_splitk_noalloc(const uint8_t* a, int64_t lda, const float* a_scales,
+                                                  int32_t a_layout, const uint8_t* w, int64_t ldw,
+                                                  const float* w_scale_inv, const uint16_t* bias,
+                                                  uint16_t* y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                                                  int32_t gran, void* stream);
 
 /*
  * fp8q_gemm_grouped_blockscale -- MoE expert GEMMs over expert-sorted rows.

@@ -49,7 +49,7 @@ def test_binding_covers_every_declared_symbol():
 
 def test_abi_version_and_status_strings(lib):
     assert lib.fp8q_abi_version() == 3
-    for s in range(8):
+    for s in range(9):
         assert len(lib.fp8q_status_string(s)) > 0
     assert lib.fp8q_status_string(99) == b"unknown status"
 
@@ -273,3 +273,14 @@ def test_library_reads_no_environment():
         text = open(os.path.join(src, name)).read()
         assert "getenv" not in text and "secure_getenv" not in text, name
 
+
+def test_gemm_splitk_noalloc_validation(lib):
+    f = lib.fp8q_gemm_blockscale_splitk_noalloc
+    assert f(A, 128, C, 0, B, 128, C, None, C, 256, -1, 256, 128, 0, None) == 2        # M < 0
+    assert f(A, 128, C, 0, B, 128, C, None, C, 256, 4, 256, 128, 5, None) == 3         # gran
+    assert f(A, 128, C, 2, B, 128, C, None, C, 256, 4, 256, 128, 0, None) == 3         # layout
+    assert f(A, 128, None, 0, B, 128, C, None, C, 256, 4, 256, 128, 0, None) == 1      # no scales
+    assert f(A, 128, ctypes.c_void_p(0x300002), 0, B, 128, C, None, C, 256, 4, 256, 128, 0, None) == 4
+    assert f(A, 128, C, 0, B, 128, C, None, C, 256, 0, 256, 128, 0, None) == 0         # M == 0
+    assert f(A, 128, C, 0, B, 128, C, None, C, 256, 4, 256, 128, 0, None) == 5         # no device here
+    assert lib.fp8q_status_string(8).startswith(b"problem needs more split-K scratch")
