@@ -364,19 +364,26 @@ __device__ __forceinline__ void store_row_seg(uint16_t* zr, const uint4 (&z)[CH]
   }
 }
 
-// fp64 sum of squares of a segment (squares of bf16 values are exact)
+// fp64 sum of squares of a segment (squares of bf16 values are exact); one
+// accumulation chain per chunk, so the chains overlap instead of forming
+// one dependent chain of 8*CH fused multiply-adds
 template <int CH>
 __device__ __forceinline__ double sumsq_seg(const uint4 (&raw)[CH], double ss) {
+  double part[CH];
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     float v[8];
     unpack8(raw[c], v);
+    double t = 0.0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const double d = (double)v[e];
-      ss = __builtin_fma(d, d, ss);
+      t = __builtin_fma(d, d, t);
     }
+    part[c] = t;
   }
+#pragma unroll
+  for (int c = 0; c < CH; ++c) ss += part[c];
   return ss;
 }
 
@@ -418,7 +425,9 @@ __device__ __forceinline__ void norm_quant_seg(const RmsArgs& a, uint4 (&raw)[CH
   const bool full = seg0 + 512 * CH <= K;
   uint8_t* qr = a.q + row * a.ldq;
   uint16_t* yr = a.y_out != nullptr ? a.y_out + row * a.ldy : nullptr;
-  float amax[CH];
+  // y[c]: the bf16 values of y as fp32, unpacked once from their rounding
+  // and used by both the group maximum and the quotients
+  float amax[CH], y[CH][8];
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int64_t k0 = seg0 + 512 * c + 8 * lane;
@@ -433,16 +442,21 @@ __device__ __forceinline__ void norm_quant_seg(const RmsArgs& a, uint4 (&raw)[CH
       if (full) *reinterpret_cast<uint4*>(yr + k0) = raw[c];
       else if (k0 < K) store8_bf16_masked(yr, k0, K, raw[c]);
     }
-    if (EXIT != EXIT_STATIC) amax[c] = max_row16(absmax8(raw[c]));
+    unpack8(raw[c], y[c]);
+    if (EXIT != EXIT_STATIC) {
+      float m = fabsf(y[c][0]);
+#pragma unroll
+      for (int e = 1; e < 8; ++e) m = fmaxf(m, fabsf(y[c][e]));
+      amax[c] = max_row16(m);
+    }
   }
   if (EXIT == EXIT_STATIC) {
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int64_t k0 = seg0 + 512 * c + 8 * lane;
-      float v[8], t[8];
-      unpack8(raw[c], v);
+      float t[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) t[e] = clamp448(v[e] / s_stat);   // IEEE division
+      for (int e = 0; e < 8; ++e) t[e] = clamp448(y[c][e] / s_stat);   // IEEE division
       const uint2 o = encode8(t);
       if (full) st8_nt(qr + k0, o);
       else if (k0 < K) store8_masked(qr, k0, K, o);
@@ -456,7 +470,17 @@ __device__ __forceinline__ void norm_quant_seg(const RmsArgs& a, uint4 (&raw)[CH
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int64_t k0 = seg0 + 512 * c + 8 * lane;
-    const uint2 o = EXIT == EXIT_POW2 ? quant8_mx(raw[c], byte[c]) : quant8(raw[c], s[c], r[c]);
+    float t[8];
+    if constexpr (EXIT == EXIT_POW2) {
+      // 2^-e = 2^(127 - byte) exactly; x * 2^-e is exact (see quant8_mx)
+      const float inv = __uint_as_float((254u - byte[c]) << 23);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) t[e] = y[c][e] * inv;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) t[e] = div_by_scale(y[c][e], s[c], r[c]);
+    }
+    const uint2 o = encode8(t);
     if (full) st8_nt(qr + k0, o);
     else if (k0 < K) store8_masked(qr, k0, K, o);
   }
