@@ -73,7 +73,8 @@ def kernel_source_sha() -> str:
 
 
 def measured_traffic(workload: str):
-    """HBM bytes per GEMM launch from committed rocprofv3 counters, or None
+    """L2<->fabric bytes per GEMM launch (FETCH_SIZE and WRITE_SIZE, scaled by
+    a device copy) from committed rocprofv3 counters, or None
     when the kernels have changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
