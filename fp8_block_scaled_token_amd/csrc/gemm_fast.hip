@@ -105,14 +105,17 @@ struct FastTile {
 // BM / 2 (HALF).
 // `preloaded`: the previous tile of this workgroup already issued this tile's
 // first K block (and its touches) before its epilogue.  `has_next`: issue the
-// first K block of the next tile (nm0, nn0, ngm, ngn; same kind) before this
-// tile's epilogue, so that its latency overlaps the output stores.
+// first K block of the next tile (nm0, nn0, ngm, ngn) before this tile's
+// epilogue, so that its latency overlaps the output stores.
 // K range of a tile and, for the two K halves of a split tail tile, how the
-// halves meet (the exchange below): the producer (the lower-numbered
-// workgroup of the pair) publishes its fp32 accumulators to `part`; the
-// consumer adds that partial as first half + second half (a fixed order,
-// whichever half each holds) and writes the output -- or, if the partial
-// does not appear within the wait limit, computes the whole tile itself.
+// halves meet (the exchange below).  The producer computes K blocks
+// [0, KB/2) as its workgroup's first item and leaves its fp32 accumulators in
+// `part`; the consumer computes [KB/2, KB) as its workgroup's last item,
+// starting from those accumulators instead of zeros, and writes the output.
+// Each output element thus sees the same sequence of rescaled block products
+// as in an unsplit tile, so the split changes no bit of the result.  If the
+// partial has not appeared when the consumer arrives (within the wait
+// limit), the consumer computes the whole tile itself.
 // Cache policy bits of a buffer access (SC0 | SC1): system scope, i.e. a
 // store writes through to memory and a load misses the caches.
 constexpr int kCacheSystem = 1 | 16;
@@ -121,30 +124,39 @@ struct TileK {
   int kb0, kb1;        // K blocks [kb0, kb1)
   int next_kb0;        // first K block of the next tile (issued early when has_next)
   int role;            // 0: whole tile, 1: producer, 2: consumer (the two K halves of a tile)
-  int first;           // this workgroup holds the first K half
   float* part;         // 256 KB partial slot of the pair
-  uint64_t* flags;     // the pair's two flag words: [0] producer's, [1] consumer's
+  uint64_t* flags;     // the pair's words: [0] producer's flag, [1] consumer's flag, [2] outcome
   uint32_t tag;        // this launch's tag (never 0)
+  // the previous item was a producer's K half: publish its partial (these
+  // flag words) once this tile's first wait has seen its stores complete
+  uint64_t* publish;
 };
 
-// Flag words of a split tail tile pair.  Only system-scope loads and stores
-// touch them (each completes at memory; no read-modify-write), so the two
+// Words of a split tail tile pair.  Only system-scope loads and stores touch
+// them (each completes at memory; no read-modify-write), so the two
 // workgroups, on different XCDs, agree without a coherent cache:
-//   producer: partial -> memory, then flags[0] = PUBLISHED; then it reads
-//             flags[1] and, if the consumer has given up, resets both words;
+//   producer: partial -> memory, then flags[0] = PUBLISHED; later (at the
+//             end of the kernel) it reads flags[1] and, if the consumer has
+//             given up, resets both flag words;
 //   consumer: waits (bounded) for flags[0] == PUBLISHED and then resets it;
 //             past the limit it writes flags[1] = GAVE_UP, reads flags[0]
 //             once more, and either consumes after all (resetting both) or
 //             computes the whole tile itself.
-// Each side's store completes before its next read, so at least one of
-// them sees the other's word: either the consumer finds the partial or the
-// producer finds the give-up (or both; both then reset both words).  The
-// last one to act leaves both words 0, so a graph replay, which reuses the
-// tag, starts from a clean state.  A word counts only if it holds this
-// launch's tag and marker: whatever else the workspace held is ignored.
-constexpr uint32_t kPublished = 0x5AFE0001u, kGaveUp = 0x5AFE0002u;
+// Each side's store completes before its read of the other's word, so at
+// least one of them sees the other's word: either the consumer finds the
+// partial or the producer finds the give-up (or both; both then reset both
+// words).  The last one to act leaves both flag words 0, so a graph replay,
+// which reuses the tag, starts from a clean state.  A word counts only if it
+// holds this launch's tag and marker: whatever else the workspace held is
+// ignored.  flags[2] records the consumer's outcome (CONSUMED or GAVE_UP with
+// the tag) for inspection; nothing reads it on the device.
+constexpr uint32_t kPublished = 0x5AFE0001u, kGaveUp = 0x5AFE0002u, kConsumed = 0x5AFE0003u;
 __device__ __forceinline__ uint64_t flag_word(uint32_t tag, uint32_t marker) {
-  return ((uint64_t)tag << 32) | marker;
+  // formed where it is used (rarely): kept opaque so that the compiler does
+  // not hoist the word out of the tile loop and hold a register for it
+  uint64_t w = ((uint64_t)tag << 32) | marker;
+  asm volatile("" : "+s"(w));
+  return w;
 }
 __device__ __forceinline__ void flag_store(uint64_t* w, uint64_t v) {
   __hip_atomic_store(w, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
@@ -312,13 +324,67 @@ __device__ __forceinline__ bool fast_tile(const GemmArgs& p, uint8_t* smem, int 
     dma4(rw, sink, o.pfw, kofs);
   };
 
+  // A consumer (second K half of a split tail tile) first waits for its
+  // producer's partial: thread 0 polls the flag (bounded) and passes the
+  // decision to every wave through LDS.  Giving up leaves everything to the
+  // caller, which computes the whole tile.
+  bool from_partial = false;
+  if (SPLIT && tk.role == 2) {
+    int* decision = reinterpret_cast<int*>(smem + T::XCH_OFF);
+    if (threadIdx.x == 0) {
+      const uint64_t pub = flag_word(tk.tag, kPublished);
+      bool seen = flag_load(tk.flags) == pub;
+      for (int n = 0; !seen && n < p.wait_limit; ++n) {
+        __builtin_amdgcn_s_sleep(2);
+        seen = flag_load(tk.flags) == pub;
+      }
+      if (!seen) {
+        flag_store(tk.flags + 1, flag_word(tk.tag, kGaveUp));
+        wait_vmcnt<0>();
+        seen = flag_load(tk.flags) == pub;
+        if (seen) flag_store(tk.flags + 1, 0);
+      }
+      if (seen) flag_store(tk.flags, 0);
+      flag_store(tk.flags + 2, flag_word(tk.tag, seen ? kConsumed : kGaveUp));
+      *decision = seen ? 1 : 0;
+    }
+    __syncthreads();
+    if (*decision == 0) {
+      // this half's first K block was issued early into stage 0: let it land
+      // before the whole tile refills that stage
+      wait_vmcnt<0>();
+      return true;
+    }
+    from_partial = true;
+  }
+
   // acc[i][j]: output rows m0 + wm*WTM + 16i + lane%16, columns
-  // n0 + wn*WTN + 16j + 4*(lane/16) + r (r = 0..3)
+  // n0 + wn*WTN + 16j + 4*(lane/16) + r (r = 0..3).  A consumer starts from
+  // the producer's accumulators (read past the caches; they were written
+  // through to memory).  Partial layout: float4 ((wave * TM + i) * TN + j) *
+  // 64 + lane, i.e. every store and load of a wave is 1 KB contiguous.
   v4f acc[TM][TN];
+  if (SPLIT && from_partial) {
+    const int vo = (wave * TM * TN * 64 + lane) * 16;
+    const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(tk.part, 0, T::BM * T::BN * 4, 0x00020000);
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rl, vo, (i * TN + j) * 1024,
+                                                                                 kCacheSystem));
+    // wait for them here, with a wait the compiler sees (vmcnt 0; expcnt and
+    // lgkmcnt unconstrained): it then places no wait for them inside the K
+    // loop, which would drain the operand loads of every block.  (The first
+    // wait below would wait for them anyway: they follow this tile's first
+    // block's loads.)
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+  } else {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
 
   // n consecutive scale words (n = 1, 2 or a multiple of 4) from LDS
   auto read_words = [&](const uint32_t* src, uint32_t* dst, auto NN) {
@@ -490,6 +556,14 @@ __device__ __forceinline__ bool fast_tile(const GemmArgs& p, uint8_t* smem, int 
     issue_all(0, kb0, cur);
     wait_vmcnt_barrier<2>();
   }
+  // Every wave's stores of the previous item (a producer's partial, issued
+  // before this tile's loads) have completed: publish it.
+  if (SPLIT && tk.publish != nullptr && threadIdx.x == 0) {
+    // a bounded delay before publishing, only when the launch plan asks for
+    // one (tests of the give-up path)
+    for (int n = 0; n < p.publish_delay; ++n) __builtin_amdgcn_s_sleep(127);
+    flag_store(tk.publish, flag_word(p.tag, kPublished));
+  }
   static_for<SLOTS>([&](auto S) { if constexpr (decltype(S)::value == 0) issue_slot(S, 1, kb0 + 1); });
   load_regs(0);
   for (int kb = kb0; kb < KB; ++kb) {
@@ -525,24 +599,16 @@ __device__ __forceinline__ bool fast_tile(const GemmArgs& p, uint8_t* smem, int 
     for (int j = 0; j < TN; ++j) fold_one(std::integral_constant<int, TM - 1>{}, j);
   }
 
-  // Split tail tile: the two K halves meet here.  Partial layout: float4
-  // ((wave * TM + i) * TN + j) * 64 + lane, i.e. every store and load of a
-  // wave is 1 KB contiguous.
-  // The accumulators are not modified here (an update inside a branch made
-  // the register allocator keep two copies of them): the partner's partial
-  // is added in the epilogue, to every tile (-0, an identity, outside the
-  // consumer).
+  // A producer's K half ends here: its accumulators go to the pair's
+  // partial slot, written through to memory (system-scope cache policy), so
+  // that the consumer, on another XCD whose L2 is not coherent with this
+  // one, reads them past its caches without an L2 write-back.  The stores
+  // are not waited for here: the next tile's first wait covers them, and
+  // the flag is raised after it (TileK::publish).
   // (SPLIT: only the kernel that may split its tail carries this code, so
   // the others keep their registers.)
-  bool consumer = false;
-  const int vo = (wave * TM * TN * 64 + lane) * 16;
-  int m_end = p.m_end;
   if (SPLIT && tk.role == 1) {
-    // The partial is written through to memory (system-scope cache policy)
-    // and read back with loads that miss the caches, so the two workgroups
-    // (on different XCDs, whose L2s are not coherent) meet without an L2
-    // write-back; every wave waits for its own stores before the barrier
-    // after which thread 0 raises the flag.
+    const int vo = (wave * TM * TN * 64 + lane) * 16;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(tk.part, 0, T::BM * T::BN * 4, 0x00020000);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -550,45 +616,9 @@ __device__ __forceinline__ bool fast_tile(const GemmArgs& p, uint8_t* smem, int 
       for (int j = 0; j < TN; ++j)
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), rs, vo, (i * TN + j) * 1024,
                                                kCacheSystem);
-    wait_vmcnt<0>();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      // a bounded delay before publishing, only when the launch plan asks
-      // for one (tests of the give-up path)
-      for (int n = 0; n < p.publish_delay; ++n) __builtin_amdgcn_s_sleep(127);
-      flag_store(tk.flags, flag_word(tk.tag, kPublished));
-      wait_vmcnt<0>();
-      if (flag_load(tk.flags + 1) == flag_word(tk.tag, kGaveUp)) {
-        flag_store(tk.flags, 0);
-        flag_store(tk.flags + 1, 0);
-      }
-    }
-    m_end = 0;                            // the consumer writes the output
-  } else if (SPLIT && tk.role == 2) {
-    int* decision = reinterpret_cast<int*>(smem + T::XCH_OFF);
-    if (threadIdx.x == 0) {
-      const uint64_t pub = flag_word(tk.tag, kPublished);
-      bool seen = flag_load(tk.flags) == pub;
-      for (int n = 0; !seen && n < p.wait_limit; ++n) {
-        __builtin_amdgcn_s_sleep(2);
-        seen = flag_load(tk.flags) == pub;
-      }
-      if (!seen) {
-        flag_store(tk.flags + 1, flag_word(tk.tag, kGaveUp));
-        wait_vmcnt<0>();
-        seen = flag_load(tk.flags) == pub;
-        if (seen) flag_store(tk.flags + 1, 0);
-      }
-      if (seen) flag_store(tk.flags, 0);
-      *decision = seen ? 1 : 0;
-    }
-    __syncthreads();
-    if (*decision == 0) return true;      // compute the whole tile instead
-    consumer = true;
+    return false;
   }
-  // the consumer's partner partial, read in the epilogue one 16-row tile at
-  // a time; -0 is added instead elsewhere
-  const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(tk.part, 0, T::BM * T::BN * 4, 0x00020000);
+  const int m_end = p.m_end;
 
   // Epilogue.  After the MFMAs, lane (r16, q) = (lane % 16, lane / 16) holds
   // for column tile j the four columns 16j + 4q + 0..3 of row r16 (+16i).
@@ -612,21 +642,6 @@ __device__ __forceinline__ bool fast_tile(const GemmArgs& p, uint8_t* smem, int 
   const int col0 = n0 + wn * WTN + 16 * lq;           // this lane's columns after the exchange
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
-    // split tail tile: first K half + second K half
-    // (loads only in the consumer: an issued load, even one reading
-    // nothing, would make this wait for the next tile's loads in flight)
-    v4f o[TN];
-    if constexpr (!SPLIT) {
-#pragma unroll
-      for (int j = 0; j < TN; ++j) o[j] = v4f{-0.f, -0.f, -0.f, -0.f};
-    } else if (consumer) {
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        o[j] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rl, vo, (i * TN + j) * 1024, kCacheSystem));
-    } else {
-#pragma unroll
-      for (int j = 0; j < TN; ++j) o[j] = v4f{-0.f, -0.f, -0.f, -0.f};
-    }
     // D[j][h]: bf16 pair h (columns 16j + 4q + 2h, +1) of column tile j
     uint32_t d[TN][2];
 #pragma unroll
@@ -634,7 +649,7 @@ __device__ __forceinline__ bool fast_tile(const GemmArgs& p, uint8_t* smem, int 
       float v[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        v[r] = tk.first ? acc[i][j][r] + o[j][r] : o[j][r] + acc[i][j][r];
+        v[r] = acc[i][j][r];
         if (MODE == MODE_TENSOR) v[r] = v[r] * mul;
         v[r] = v[r] + bias[j][r];
       }
@@ -681,17 +696,19 @@ __device__ __forceinline__ bool fast_tile(const GemmArgs& p, uint8_t* smem, int 
 // [full, items) -- or, with `ksplit` (a workspace in p.partial), into their
 // two K halves: items full + 2t and full + 2t + 1 are the first and second
 // K half of leftover tile t, which meet through the pair's partial slot and
-// exchange word (see TileK).  The kernel is persistent: workgroup g takes
+// flag words (see TileK).  The kernel is persistent: workgroup g takes
 // items g, g + G, g + 2G, ... (G = gridDim.x, at most one workgroup per
 // slot), so the workgroups of a round start together and keep their XCD
-// (item % 8), and no workgroup is launched per tile.  Between two tiles no
-// barrier is needed: a wave issues the next tile's first LDS writes only
-// after the last K-loop barrier of the previous tile, after which nobody
-// reads a stage, and the next tile's first barrier waits for every wave.  A
-// split pair's items are the last of their workgroups (the tail is one
-// round), and the lower-index workgroup of a pair never waits, so the
-// waits cannot form a cycle; the other stops waiting after p.wait_limit
-// polls and then computes the whole tile itself.
+// (item % 8), and no workgroup is launched per tile.  full is a multiple of
+// G and items - full <= G, so a workgroup holds at most one K half; a first
+// K half (the producer's) is moved to the front of its workgroup's items and
+// a second one stays last, so the partial is written while the consumer
+// still works on its whole tiles.  Between two tiles no barrier is needed: a
+// wave issues the next tile's first LDS writes only after the last K-loop
+// barrier of the previous tile, after which nobody reads a stage, and the
+// next tile's first barrier waits for every wave.  A producer never waits,
+// so the waits cannot form a cycle; a consumer stops waiting after
+// p.wait_limit polls and then computes the whole tile itself.
 template <class T, bool KSPLIT>
 __global__ __launch_bounds__(T::NW * 64) void gemm_fast_kernel(GemmArgs p, int full, int items) {
   constexpr bool ksplit = KSPLIT;
@@ -720,30 +737,39 @@ __global__ __launch_bounds__(T::NW * 64) void gemm_fast_kernel(GemmArgs p, int f
     gn = tn % T::NTN;
     return kind;
   };
+  const int g = blockIdx.x;
   const int half_kb = p.KB / 2;
   const int tails = (items - full) / 2;
+  // this workgroup's items in order: g, g + G, ... (< items), except that a
+  // first K half (full + g, the last of them) is moved to the front
+  const bool front = ksplit && g < items - full && (g & 1) == 0;
+  auto next_item = [&](int x) {
+    if (front && x == full + g) return g;
+    const int y = x + G;
+    return (y >= items || (front && y == full + g)) ? -1 : y;
+  };
   bool preloaded = false;
+  uint64_t* publish = nullptr;         // flag words of a partial stored by the previous item
+  uint64_t* produced = nullptr;        // flag words of this workgroup's K half as producer
   int redo_m0 = -1, redo_n0 = 0, redo_gm = 0, redo_gn = 0;
-  for (int b = blockIdx.x; b < items; b += G) {
+  for (int b = g >= items ? -1 : (front ? full + g : g); b >= 0; b = next_item(b)) {
     int m0, n0, gm, gn, nm0 = 0, nn0 = 0, ngm = 0, ngn = 0;
     const int kind = decode(b, m0, n0, gm, gn);
-    const int nb = b + G;
+    const int nb = next_item(b);
     // the next tile's first block is issued early between tiles of one
-    // kind, and from a whole tile to a K half (at that half's first block)
-    const int nkind = nb < items ? decode(nb, nm0, nn0, ngm, ngn) : -1;
-    const bool has_next = nkind >= 0 && (nkind == kind || (kind == 0 && nkind == 2));
-    TileK tk{0, p.KB, 0, 0, 0, nullptr, nullptr, 0u};
+    // kind, and between a whole tile and a K half either way (at that
+    // tile's first block)
+    const int nkind = nb >= 0 ? decode(nb, nm0, nn0, ngm, ngn) : -1;
+    const bool has_next = nkind >= 0 && (nkind == kind || (kind == 0 && nkind == 2) || (kind == 2 && nkind == 0));
+    TileK tk{0, p.KB, 0, 0, nullptr, nullptr, p.tag, publish};
     if (nkind == 2) tk.next_kb0 = ((nb - full) & 1) ? half_kb : 0;
     if (kind == 2) {
       const int t = (b - full) >> 1, second = (b - full) & 1;
-      const int partner = second ? b - 1 : b + 1;
       tk.kb0 = second ? half_kb : 0;
       tk.kb1 = second ? p.KB : half_kb;
-      tk.first = !second;
-      tk.role = (int)blockIdx.x < partner % G ? 1 : 2;
+      tk.role = second ? 2 : 1;
       tk.part = p.partial + (int64_t)t * (T::BM * T::BN);
-      tk.flags = reinterpret_cast<uint64_t*>(p.partial + (int64_t)tails * (T::BM * T::BN)) + 2 * t;
-      tk.tag = p.tag;
+      tk.flags = reinterpret_cast<uint64_t*>(p.partial + (int64_t)tails * (T::BM * T::BN)) + 3 * t;
     }
     bool redo;
     if (kind == 1)
@@ -753,14 +779,30 @@ __global__ __launch_bounds__(T::NW * 64) void gemm_fast_kernel(GemmArgs p, int f
     if (KSPLIT && redo) {
       redo_m0 = m0; redo_n0 = n0; redo_gm = gm; redo_gn = gn;
     }
+    publish = nullptr;
+    if (KSPLIT && tk.role == 1) publish = produced = tk.flags;
     preloaded = has_next;
+  }
+  if (KSPLIT && publish != nullptr) {
+    // a producer's K half with no tile after it: wait for its stores here
+    wait_vmcnt_barrier<0>();
+    if (threadIdx.x == 0) flag_store(publish, flag_word(p.tag, kPublished));
   }
   if (KSPLIT && redo_m0 >= 0) {
     // the partner's half did not appear in time: the whole tile here (a K
     // half is its workgroup's last item, so nothing was issued early and
     // nothing follows)
-    const TileK whole{0, p.KB, 0, 0, 1, nullptr, nullptr, 0u};   // role 0: a whole tile
+    const TileK whole{0, p.KB, 0, 0, nullptr, nullptr, p.tag, nullptr};   // role 0: a whole tile
     fast_tile<T, false, false>(p, smem, redo_m0, redo_n0, redo_gm, redo_gn, false, false, 0, 0, 0, 0, whole);
+  }
+  if (KSPLIT && produced != nullptr && threadIdx.x == 0) {
+    // the producer's read of the consumer's flag, after its own flag store
+    // has completed
+    wait_vmcnt<0>();
+    if (flag_load(produced + 1) == flag_word(p.tag, kGaveUp)) {
+      flag_store(produced, 0);
+      flag_store(produced + 1, 0);
+    }
   }
   // the last touches and past-the-end loads still write the LDS sink: let
   // them land before the workgroup ends
@@ -864,7 +906,7 @@ __global__ __launch_bounds__(T::NW * 64) void gemm_grouped_kernel(GemmArgs p, Gr
     pe.w = p.w + e * g.w_stride;
     pe.sw = static_cast<const float*>(p.sw) + e * g.sw_stride;
     pe.m_end = __builtin_amdgcn_readfirstlane(row_end(e));
-    const TileK tk{0, p.KB, 0, 0, 1, nullptr, nullptr, 0u};
+    const TileK tk{0, p.KB, 0, 0, nullptr, nullptr, 0u, nullptr};
     if (half)
       fast_tile<T, true, false, true>(pe, smem, m0, n0, gm, gn, preloaded, has_next, nm0, nn0, ngm, ngn, tk);
     else
@@ -932,14 +974,13 @@ Plan choose_plan(const GemmArgs& p) {
 }
 
 // Workspace of the split tail (configuration 0 only): 256 x 256 fp32 per
-// leftover tile, then two 8-byte flag words each; 0 when the plan has no tail, or
-// when K is below 32 blocks: the exchange of a 256 KB partial costs about
-// what half of a short K loop saves (measured: 4096x6144x6144 158 -> 146 us,
-// 2560x7168x2048 55 -> 58 us).
+// leftover tile, then three 8-byte words each (two flags, the outcome); 0
+// when the plan has no tail, or when K is below 32 blocks: for a short K
+// loop the exchange of a 256 KB partial costs about what the split saves.
 size_t tail_workspace(const Plan& pl, const GemmArgs& p) {
   const int tail = pl.tiles_m * pl.tiles_n - pl.full;
   if (pl.cfg != 0 || tail <= 0 || p.KB < 32) return 0;
-  return (size_t)tail * (256u * 256u * 4u + 16u);
+  return (size_t)tail * (256u * 256u * 4u + 24u);
 }
 
 std::atomic<uint32_t> g_tag{0};

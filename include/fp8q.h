@@ -297,20 +297,25 @@ fp8q_status_t fp8q_gemm_blockscale(const uint8_t* a, int64_t lda, const float* a
  *    share of the weight on otherwise idle CUs; a second kernel adds the
  *    partials in segment order 0, 1, ..., S-1;
  *  - prefill shapes whose last round of 256 x 256 tiles is at most half
- *    full: each leftover tile is computed as two K halves by two workgroups;
- *    one publishes its fp32 partial, the other adds it (first half + second
- *    half) before the epilogue.  The adding one waits for the partial only
- *    up to a bound (the publishing one never waits); if the partial has not
- *    appeared by then it computes the whole tile itself (correct to the same
- *    bound; its bits may then differ from the split order's -- a path no
- *    normal launch takes).
+ *    full: each leftover tile is computed as two K halves by two workgroups.
+ *    The first half runs first in its workgroup and leaves its fp32
+ *    accumulators in the workspace; the second half runs last in the other
+ *    workgroup and continues from those accumulators instead of zeros.
+ *    Every output element so sees the same sequence of operations as in an
+ *    unsplit tile: this split gives exactly the unsplit kernel's bits.  The
+ *    continuing workgroup waits for the partial only up to a bound (the
+ *    other never waits); if it has not appeared by then, it computes the
+ *    whole tile itself (the same bits again).
  * Both orders are fixed: repeated calls give identical bits.  Other shapes,
  * or a workspace too small, run the unsplit kernels.  The prefill split keeps
- * two 8-byte flag words per leftover tile in the workspace, tagged with a
- * per-launch value and reset to 0 by the last workgroup that uses them, so
- * whatever the workspace held before does not matter and launches may be
- * captured in a graph and replayed; a workspace is used by one launch at a
- * time (launches that overlap on one workspace race).
+ * three 8-byte words per leftover tile in the workspace after the partials:
+ * two flag words, tagged with a per-launch value and reset to 0 by the last
+ * workgroup that uses them, so whatever the workspace held before does not
+ * matter and launches may be captured in a graph and replayed; and one
+ * outcome word that the second half sets to (tag << 32) | 0x5AFE0003 when it
+ * continued from the partial, or | 0x5AFE0002 when it computed the whole
+ * tile (for inspection; the kernels never read it).  A workspace is used by
+ * one launch at a time (launches that overlap on one workspace race).
  *
  *   Arguments as fp8q_gemm_blockscale (all three granularities), plus
  *   workspace  device memory for S * M * N fp32 partials (8-byte aligned),

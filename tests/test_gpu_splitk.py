@@ -1,10 +1,15 @@
-"""GPU parity of the split-K GEMM entry point (fp32 partial sums per K
-segment, added in segment order by a second kernel): decode shapes whose
-column tiles leave CUs idle, all three scale granularities, ragged M and N,
+"""GPU parity of the split-K GEMM entry point.  Decode shapes whose column
+tiles leave CUs idle (fp32 partial sums per K segment, added in segment
+order by a second kernel): all three scale granularities, ragged M and N,
 against the oracle (the method's per-row bound); repeated calls give the
 same bits; a workspace too small for two segments, and shapes the split does
 not serve (M > 64, or K below 96 blocks), give exactly the unsplit kernels'
-bits."""
+bits.  Prefill shapes whose last round of tiles is at most half full (the
+leftover tiles as two K halves, the second continuing from the first's
+accumulators): against the oracle, bit for bit equal to the unsplit entry,
+every second half recorded as having continued from the partial; and, forced
+from the host, the give-up path (the second half computes the whole tile)
+with the same bits."""
 import numpy as np
 import pytest
 import torch
@@ -56,17 +61,36 @@ def _operands(M, N, K, gran, seed):
 
 
 def _call(qa, sa, qw, sw, gran, ws, bias=None, a_layout=0):
+    """The split entry with workspace ws (None: the unsplit entry)."""
     m = fq()
     M, K = qa.shape
     N = qw.shape[0]
     yb, y = padded(M, N, torch.bfloat16, 8, CANARY_BF16)
     b_d = None if bias is None else torch.from_numpy(bias.astype(np.float32)).to(torch.bfloat16).cuda()
     sa_d = torch.from_numpy(np.ascontiguousarray(sa.T if a_layout else sa)).cuda()
-    m.fp8q_gemm_blockscale_splitk(_dev_u8(qa, K), sa_d, a_layout, _dev_u8(qw, K),
-                                  torch.from_numpy(np.ascontiguousarray(sw)).cuda(), b_d, y, gran, ws)
+    sw_d = torch.from_numpy(np.ascontiguousarray(sw)).cuda()
+    if ws is None:
+        m.fp8q_gemm_blockscale(_dev_u8(qa, K), sa_d, a_layout, _dev_u8(qw, K), sw_d, b_d, y, gran)
+    else:
+        m.fp8q_gemm_blockscale_splitk(_dev_u8(qa, K), sa_d, a_layout, _dev_u8(qw, K), sw_d, b_d, y, gran, ws)
     torch.cuda.synchronize()
     assert canary_intact(yb, N, CANARY_BF16)
     return bf16_bits(y)
+
+
+# Layout of the prefill split's workspace: per leftover tile a 256 x 256
+# fp32 partial, then per leftover tile three 8-byte words (two flags and the
+# outcome of the second half: tag << 32 | marker).
+PARTIAL_BYTES, WORDS = 256 * 256 * 4, 3
+CONSUMED, GAVE_UP = 0x5AFE0003, 0x5AFE0002
+
+
+def _outcomes(ws, nbytes):
+    tails = nbytes // (PARTIAL_BYTES + 8 * WORDS)
+    assert tails * (PARTIAL_BYTES + 8 * WORDS) == nbytes
+    words = ws.view(torch.int64)[tails * PARTIAL_BYTES // 8: tails * PARTIAL_BYTES // 8 + WORDS * tails]
+    w = words.cpu().numpy().view(np.uint64).reshape(tails, WORDS)[:, 2]
+    return w & np.uint64(0xFFFFFFFF), w >> np.uint64(32)
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
@@ -135,17 +159,27 @@ def test_prefill_tail_split_parity(M, N, K, gran):
     else:
         yr = og.gemm_blockscale(qa, sa, qw, sw, bias=bias, rows=rows)[0]
     check_gemm_rows(y[rows], yr, f"prefill split M={M} N={N} K={K}", REL)
+    # every second half continued from its partner's partial, all with this
+    # launch's tag
+    marker, tag = _outcomes(ws, nbytes)
+    assert np.all(marker == CONSUMED) and np.all(tag == tag[0]) and tag[0] != 0
+    # the split keeps each element's sequence of operations: the unsplit
+    # kernel's bits exactly
+    np.testing.assert_array_equal(_call(qa, sa, qw, sw, gran, None, bias, layout), y)
     # fixed order, and the flags of the previous launch do not confuse the next
     np.testing.assert_array_equal(_call(qa, sa, qw, sw, gran, ws, bias, layout), y)
+    marker2, tag2 = _outcomes(ws, nbytes)
+    assert np.all(marker2 == CONSUMED) and np.all(tag2 != tag[0])
 
 
-@pytest.mark.parametrize("gran", [0, 2])
+@pytest.mark.parametrize("gran", [0, 1, 2])
 def test_prefill_tail_give_up_computes_whole_tile(plan, gran):
-    """Forced from the host: the first K half of every leftover tile sleeps
-    (~100 us, bounded) before publishing and the second does not wait, so the
-    second computes the whole tile itself.  The output stays within the bound,
-    tiles outside the tail keep their bits, and the exchange words end at
-    their idle state: a normal launch afterwards gives the split bits again."""
+    """Forced from the host: every first K half publishes its partial only
+    after a bounded sleep (~340 us) and every second half does not wait, so
+    the second halves compute their whole tiles themselves.  The outcome
+    words say so, the output keeps its bits (the same sequence of operations
+    either way), and the exchange words end at their idle state: a normal
+    launch afterwards continues from the partials again."""
     m = fq()
     M, N, K = 2304, 8192, 4096                       # 288 tiles: 32 leftover tiles as 64 K halves
     nbytes = m.fp8q_gemm_splitk_workspace_size(M, N, K)
@@ -153,22 +187,20 @@ def test_prefill_tail_give_up_computes_whole_tile(plan, gran):
     assert nbytes > 0
     ws = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device="cuda")
     qa, sa, qw, sw, ref = _operands(M, N, K, gran, 7 + gran)
-    layout = 1
+    layout = 0 if gran == 1 else 1
     y_split = _call(qa, sa, qw, sw, gran, ws, None, layout)
-    plan(split_wait_limit=0, split_publish_delay=30)
+    assert np.all(_outcomes(ws, nbytes)[0] == CONSUMED)
+    plan(split_wait_limit=0, split_publish_delay=100)
     y_alone = _call(qa, sa, qw, sw, gran, ws, None, layout)
     plan()
+    assert np.all(_outcomes(ws, nbytes)[0] == GAVE_UP), "the give-up path was not taken"
+    np.testing.assert_array_equal(y_alone, y_split)
     y_again = _call(qa, sa, qw, sw, gran, ws, None, layout)
+    assert np.all(_outcomes(ws, nbytes)[0] == CONSUMED)
     np.testing.assert_array_equal(y_again, y_split)
-    # the leftover tiles are the last tile row (rows 2048..2303): recomputed
-    # there in one accumulation order, elsewhere the same tiles as before
-    tail = slice(2048, M)
-    np.testing.assert_array_equal(y_alone[:2048], y_split[:2048])
-    if gran == 0:
-        # fp32 block scales round at every K block's rescale, so one
-        # accumulation order differs from the split order somewhere (with
-        # power-of-two scales the sums can be exact and the bits equal)
-        assert np.any(y_alone[tail] != y_split[tail]), "the give-up path was not taken"
     rows = np.unique(np.r_[2048, M - 1, np.arange(2048, M, 23), 5, 1000])
-    yr = og.gemm_blockscale(qa, sa, qw, sw, rows=rows)[0]
+    if gran == 1:
+        yr = og.gemm_pertensor(qa, sa[0], qw, sw[0], rows=rows)[0]
+    else:
+        yr = og.gemm_blockscale(qa, sa, qw, sw, rows=rows)[0]
     check_gemm_rows(y_alone[rows], yr, f"prefill give-up M={M} N={N} K={K}", REL)
