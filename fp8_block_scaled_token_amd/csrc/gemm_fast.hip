@@ -101,8 +101,9 @@ struct FastTile {
   static_assert(STAGE % 1024 == 0, "stages stay 1 KB aligned");
 };
 
-// One tile: rows [m0, m0 + RM) x columns [n0, n0 + BN), RM = BM (full) or
-// BM / 2 (HALF).
+// One tile: rows [m0, m0 + RM) x columns [n0, n0 + BN), RM = BM * RQ / 4:
+// a whole tile (RQ = 4), or a short one for the last rows of an expert in
+// the grouped GEMM (3/4: RQ = 3) or a half-height tile (RQ = 2).
 // `preloaded`: the previous tile of this workgroup already issued this tile's
 // first K block (and its touches) before its epilogue.  `has_next`: issue the
 // first K block of the next tile (nm0, nn0, ngm, ngn) before this tile's
@@ -168,15 +169,16 @@ __device__ __forceinline__ uint64_t flag_load(uint64_t* w) {
 // Returns true when this workgroup, the consumer of a split tail tile, gave
 // up waiting for its partner's partial: nothing was written, and the caller
 // then computes the whole tile (the producer writes no output either).
-template <class T, bool HALF, bool SPLIT, bool NTW = false>
+template <class T, int RQ, bool SPLIT, bool NTW = false>
 __device__ __forceinline__ bool fast_tile(const GemmArgs& p, uint8_t* smem, int m0, int n0, int gm, int gn,
                                           bool preloaded, bool has_next, int nm0, int nn0, int ngm, int ngn,
                                           const TileK& tk) {
   constexpr int MODE = T::MODE, BM = T::BM, BN = T::BN, WN = T::WN, NW = T::NW;
   constexpr bool FP32S = T::FP32S, MXC = MODE == MODE_MXC;
-  constexpr int RM = HALF ? T::BM / 2 : T::BM;
+  static_assert(RQ >= 2 && RQ <= 4, "tile height in quarters");
+  constexpr int RM = T::BM * RQ / 4;
   constexpr int WTM = RM / T::WM, TM = WTM / 16, WTN = T::WTN, TN = T::TN;
-  // a half tile's activation rows are spread over all waves too
+  // a short tile's activation rows are spread over all waves too
   constexpr int A_PER = RM * 128 / 1024 / NW, W_PER = T::W_PER, STAGE = T::STAGE;
   static_assert(A_PER >= 1 && A_PER * NW * 1024 == RM * 128, "whole 1 KB activation loads");
   constexpr int ABYTES = T::ABYTES, SA_OFF = T::SA_OFF, SW_OFF = T::SW_OFF;
@@ -386,7 +388,9 @@ __device__ __forceinline__ bool fast_tile(const GemmArgs& p, uint8_t* smem, int 
       for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   }
 
-  // n consecutive scale words (n = 1, 2 or a multiple of 4) from LDS
+  // n consecutive scale words from LDS: 16-byte reads where n is a multiple
+  // of 4 (the run then starts 16-byte aligned), else 8-byte reads where n is
+  // even, else single words
   auto read_words = [&](const uint32_t* src, uint32_t* dst, auto NN) {
     constexpr int n = decltype(NN)::value;
     if constexpr (n % 4 == 0) {
@@ -395,12 +399,15 @@ __device__ __forceinline__ bool fast_tile(const GemmArgs& p, uint8_t* smem, int 
         const uint4 s4 = *reinterpret_cast<const uint4*>(src + i);
         dst[i] = s4.x; dst[i + 1] = s4.y; dst[i + 2] = s4.z; dst[i + 3] = s4.w;
       }
-    } else if constexpr (n == 2) {
-      const uint2 s2 = *reinterpret_cast<const uint2*>(src);
-      dst[0] = s2.x; dst[1] = s2.y;
+    } else if constexpr (n % 2 == 0) {
+#pragma unroll
+      for (int i = 0; i < n; i += 2) {
+        const uint2 s2 = *reinterpret_cast<const uint2*>(src + i);
+        dst[i] = s2.x; dst[i + 1] = s2.y;
+      }
     } else {
-      static_assert(n == 1, "scale word count");
-      dst[0] = src[0];
+#pragma unroll
+      for (int i = 0; i < n; ++i) dst[i] = src[i];
     }
   };
 
@@ -773,9 +780,9 @@ __global__ __launch_bounds__(T::NW * 64) void gemm_fast_kernel(GemmArgs p, int f
     }
     bool redo;
     if (kind == 1)
-      redo = fast_tile<T, true, KSPLIT>(p, smem, m0, n0, gm, gn, preloaded, has_next, nm0, nn0, ngm, ngn, tk);
+      redo = fast_tile<T, 2, KSPLIT>(p, smem, m0, n0, gm, gn, preloaded, has_next, nm0, nn0, ngm, ngn, tk);
     else
-      redo = fast_tile<T, false, KSPLIT>(p, smem, m0, n0, gm, gn, preloaded, has_next, nm0, nn0, ngm, ngn, tk);
+      redo = fast_tile<T, 4, KSPLIT>(p, smem, m0, n0, gm, gn, preloaded, has_next, nm0, nn0, ngm, ngn, tk);
     if (KSPLIT && redo) {
       redo_m0 = m0; redo_n0 = n0; redo_gm = gm; redo_gn = gn;
     }
@@ -793,7 +800,7 @@ __global__ __launch_bounds__(T::NW * 64) void gemm_fast_kernel(GemmArgs p, int f
     // half is its workgroup's last item, so nothing was issued early and
     // nothing follows)
     const TileK whole{0, p.KB, 0, 0, nullptr, nullptr, p.tag, nullptr};   // role 0: a whole tile
-    fast_tile<T, false, false>(p, smem, redo_m0, redo_n0, redo_gm, redo_gn, false, false, 0, 0, 0, 0, whole);
+    fast_tile<T, 4, false>(p, smem, redo_m0, redo_n0, redo_gm, redo_gn, false, false, 0, 0, 0, 0, whole);
   }
   if (KSPLIT && produced != nullptr && threadIdx.x == 0) {
     // the producer's read of the consumer's flag, after its own flag store
@@ -863,9 +870,10 @@ __global__ __launch_bounds__(T::NW * 64) void gemm_grouped_kernel(GemmArgs p, Gr
     __syncthreads();
   }
   const int items = __builtin_amdgcn_readfirstlane(tiles_before[E - 1]);
-  // item -> expert (first e with tiles_before[e] > x), tile origin, and
-  // whether it is a half-height tile: an expert's last row tile holding at
-  // most BM/2 rows computes only those (it loads half the activation rows)
+  // item -> expert (first e with tiles_before[e] > x), tile origin, and the
+  // tile's height in quarters of BM: an expert's last row tile holding at
+  // most BM/2 (3BM/4) rows computes only that many (and loads only those
+  // activation rows)
   auto decode = [&](int x, int& e, int& m0, int& n0, int& gm, int& gn) {
     // branch-free binary search (straight-line code: a loop here made the
     // register allocator spill around the tile bodies); e = the number of
@@ -889,30 +897,33 @@ __global__ __launch_bounds__(T::NW * 64) void gemm_grouped_kernel(GemmArgs p, Gr
     n0 = tn * T::BN;
     gm = tm % 8;
     gn = tn % T::NTN;
-    return cnt - tm * T::BM <= T::BM / 2;
+    const int left = cnt - tm * T::BM;
+    return left <= T::BM / 2 ? 2 : left <= 3 * T::BM / 4 ? 3 : 4;
   };
   bool preloaded = false;
   // the next item's decode is carried into the next iteration
   int e = 0, m0 = 0, n0 = 0, gm = 0, gn = 0;
-  bool half = false;
-  if ((int)blockIdx.x < items) half = decode(blockIdx.x, e, m0, n0, gm, gn);
+  int rq = 4;
+  if ((int)blockIdx.x < items) rq = decode(blockIdx.x, e, m0, n0, gm, gn);
   for (int b = blockIdx.x; b < items; b += gridDim.x) {
     int ne = -1, nm0 = 0, nn0 = 0, ngm = 0, ngn = 0;
     const int nb = b + gridDim.x;
-    bool nhalf = false;
-    if (nb < items) nhalf = decode(nb, ne, nm0, nn0, ngm, ngn);
-    const bool has_next = ne == e && nhalf == half;
+    int nrq = 4;
+    if (nb < items) nrq = decode(nb, ne, nm0, nn0, ngm, ngn);
+    const bool has_next = ne == e && nrq == rq;
     GemmArgs pe = p;
     pe.w = p.w + e * g.w_stride;
     pe.sw = static_cast<const float*>(p.sw) + e * g.sw_stride;
     pe.m_end = __builtin_amdgcn_readfirstlane(row_end(e));
     const TileK tk{0, p.KB, 0, 0, nullptr, nullptr, 0u, nullptr};
-    if (half)
-      fast_tile<T, true, false, true>(pe, smem, m0, n0, gm, gn, preloaded, has_next, nm0, nn0, ngm, ngn, tk);
+    if (rq == 2)
+      fast_tile<T, 2, false, true>(pe, smem, m0, n0, gm, gn, preloaded, has_next, nm0, nn0, ngm, ngn, tk);
+    else if (rq == 3)
+      fast_tile<T, 3, false, true>(pe, smem, m0, n0, gm, gn, preloaded, has_next, nm0, nn0, ngm, ngn, tk);
     else
-      fast_tile<T, false, false, true>(pe, smem, m0, n0, gm, gn, preloaded, has_next, nm0, nn0, ngm, ngn, tk);
+      fast_tile<T, 4, false, true>(pe, smem, m0, n0, gm, gn, preloaded, has_next, nm0, nn0, ngm, ngn, tk);
     preloaded = has_next;
-    e = ne; m0 = nm0; n0 = nn0; gm = ngm; gn = ngn; half = nhalf;
+    e = ne; m0 = nm0; n0 = nn0; gm = ngm; gn = ngn; rq = nrq;
   }
   wait_vmcnt<0>();
 }

@@ -79,6 +79,10 @@ CASES = [
     ([129, 40, 7], 384, 512, 192),                # shard not a multiple of 128
     ([100, 300], 2 * 1088, 256, 1088),            # I_p = 1088: 2 x 9 scale rows
     ([1000, 1500, 600, 900], 1024, 1024, 512),
+    # last row tiles of every height class: <= BM/2, <= 3BM/4 and above
+    # (BM = 256: 150, 190, 192 and 129 take the three-quarter tile; BM = 128:
+    # 90 and 96)
+    ([150, 190, 193, 192, 129, 90, 96, 97], 512, 768, 0),
 ]
 
 
