@@ -67,12 +67,39 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_sha() -> str:
+def code_text(src: str) -> str:
+    """C/C++ source without its comments, trailing blanks and empty lines
+    (string and character literals kept as they are)."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    lines = (line.rstrip() for line in "".join(out).split("\n"))
+    return "\n".join(line for line in lines if line)
+
+
+def kernel_source_sha(csrc: str | None = None) -> str:
+    """Hash of the kernel sources' code (comments and blank lines excluded,
+    so that a change of documentation keeps the counters taken before it)."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "fp8_block_scaled_token_amd", "csrc")
+    csrc = csrc or os.path.join(ROOT, "fp8_block_scaled_token_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
         h.update(f.encode())
-        h.update(open(os.path.join(csrc, f), "rb").read())
+        h.update(code_text(open(os.path.join(csrc, f), encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -9,9 +9,10 @@
 //    holds four consecutive output COLUMNS of one output ROW.  In block mode
 //    the four partial products of a lane then share one activation scale:
 //    the per-K-block rescale is 4 FMAs per MFMA plus one scale product per
-//    16 rows, which fits the VALU issue slots that an fp8 MFMA leaves free
-//    (about 4 per MFMA on one SIMD, measured), and the epilogue writes
-//    8-byte runs of bf16.
+//    16 rows, close to the VALU issue slots that an fp8 MFMA leaves free
+//    (three to four wave64 instructions per MFMA on one SIMD, measured).
+//    The epilogue exchanges bf16 pairs across the four lanes of a row and
+//    writes 16-byte runs.
 //  * Large workgroup tiles.  One K block of a BM x BN tile moves
 //    (BM + BN) * 128 bytes from L2 through the CU's vector cache into LDS;
 //    the big configuration is 256 x 256 with 8 waves (2 x 4, 128 rows x 64
@@ -29,7 +30,11 @@
 //    of one 16-row tile with the MFMAs of the next.
 //  * Tail balancing: when the last round of tiles would leave at least half
 //    of the CUs idle, those tiles are split into two half-height tiles, which
-//    fill the machine and take half as long.
+//    fill the machine and take half as long -- or, given a workspace, into
+//    their two K halves, the second continuing from the first's fp32
+//    accumulators (full-height tiles, the same bits as unsplit).  The
+//    grouped (MoE) kernel sizes an expert's last row tile to its rows: a
+//    half- or three-quarter-height tile where they fit.
 //  * Workgroup ids are renumbered XCD-aware and tiles walked in groups of
 //    tile rows, so tiles sharing A rows or W rows meet in the same L2, and
 //    every workgroup touches its share of the operand lines a few K blocks

@@ -33,6 +33,21 @@ def test_kernel_source_sha_tracks_sources():
     assert bench.kernel_source_sha() == sha          # deterministic
 
 
+def test_kernel_source_sha_sees_code_not_comments(tmp_path):
+    src = tmp_path / "csrc"
+    src.mkdir()
+    f = src / "k.hip"
+    f.write_text('int a = 1;  // one\n/* block\n comment */\nconst char* s = "// kept";\n')
+    base = bench.kernel_source_sha(str(src))
+    f.write_text('int a = 1;  // the value one\n\n/* another\n block comment */\nconst char* s = "// kept";\n')
+    assert bench.kernel_source_sha(str(src)) == base
+    f.write_text('int a = 2;  // one\n/* block\n comment */\nconst char* s = "// kept";\n')
+    assert bench.kernel_source_sha(str(src)) != base
+    f.write_text('int a = 1;  // one\n/* block\n comment */\nconst char* s = "// kEpt";\n')
+    assert bench.kernel_source_sha(str(src)) != base
+    assert bench.code_text('x = "a\\"b"; // c') == 'x = "a\\"b";'
+
+
 def _with_traffic(tmp_path, monkeypatch, record):
     prof = tmp_path / "profiles"
     prof.mkdir()
