@@ -92,12 +92,19 @@ def code_text(src: str) -> str:
     return "\n".join(line for line in lines if line)
 
 
+# sources that do not build the GEMM kernels (whose traffic the counters give)
+NON_GEMM_SOURCES = {"quant_kernels.hip"}
+
+
 def kernel_source_sha(csrc: str | None = None) -> str:
-    """Hash of the kernel sources' code (comments and blank lines excluded,
-    so that a change of documentation keeps the counters taken before it)."""
+    """Hash of the code of the sources the GEMM kernels are built from (every
+    source but the quantizers'; comments and blank lines excluded, so that a
+    change of documentation keeps the counters taken before it)."""
     h = hashlib.sha256()
     csrc = csrc or os.path.join(ROOT, "fp8_block_scaled_token_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
+        if f in NON_GEMM_SOURCES:
+            continue
         h.update(f.encode())
         h.update(code_text(open(os.path.join(csrc, f), encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]
@@ -106,7 +113,7 @@ def kernel_source_sha(csrc: str | None = None) -> str:
 def measured_traffic(workload: str):
     """L2<->fabric bytes per GEMM launch (FETCH_SIZE and WRITE_SIZE, scaled by
     a device copy) from committed rocprofv3 counters, or None
-    when the kernels have changed since the counters were taken."""
+    when the GEMM kernels have changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None

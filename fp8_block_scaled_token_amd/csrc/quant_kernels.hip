@@ -707,20 +707,22 @@ __global__ void finalize_tensor_scale_kernel(uint32_t* slot) {
 
 static inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Row quantizers: segments of 512*CH elements per wave.  Short rows take
-// fewer chunks so that lanes are not idle; longer rows take 4, or 3, 5 or 7
-// when that divides the row into whole segments and 4 does not (a ragged
+// Row quantizers: segments of 512*CH elements per wave.  Rows of at most 512
+// take one chunk; longer rows take 2, or 3, 5 or 7 when the row is an odd
+// number of whole 512-element chunks that one of them divides (a ragged
 // last segment runs the masked path: 12 % slower at K = 7168, measured),
-// else 4 with a masked last segment.
+// else 2 with a masked last segment.  Two chunks per wave measured best or
+// equal for the group, MX and static quantizers on 2048x7168, 4096x6144 and
+// 8192x7168 (against 1, 3, 4 and 7: MX 2-7 % and static 0-3 % faster than
+// with 4 or 7, the group quantizer within 1 %).
 static inline int row_chunks(int64_t K) {
   if (K <= 512) return 1;
-  if (K <= 1024) return 2;
-  if (K % 512 == 0) {
+  if (K % 1024 == 512) {
     const int64_t n = K / 512;
-    for (const int c : {4, 3, 5, 7})
+    for (const int c : {3, 5, 7})
       if (n % c == 0) return c;
   }
-  return 4;
+  return 2;
 }
 
 // LAUNCH(C) for the chunk count row_chunks chose
@@ -728,11 +730,10 @@ static inline int row_chunks(int64_t K) {
   do {                              \
     switch (ch) {                   \
       case 1: LAUNCH(1); break;     \
-      case 2: LAUNCH(2); break;     \
       case 3: LAUNCH(3); break;     \
       case 5: LAUNCH(5); break;     \
       case 7: LAUNCH(7); break;     \
-      default: LAUNCH(4); break;    \
+      default: LAUNCH(2); break;    \
     }                               \
   } while (0)
 

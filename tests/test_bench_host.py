@@ -46,6 +46,11 @@ def test_kernel_source_sha_sees_code_not_comments(tmp_path):
     f.write_text('int a = 1;  // one\n/* block\n comment */\nconst char* s = "// kEpt";\n')
     assert bench.kernel_source_sha(str(src)) != base
     assert bench.code_text('x = "a\\"b"; // c') == 'x = "a\\"b";'
+    (src / "quant_kernels.hip").write_text("int q = 1;\n")       # not a GEMM source
+    f.write_text('int a = 1;  // one\n/* block\n comment */\nconst char* s = "// kept";\n')
+    with_q = bench.kernel_source_sha(str(src))
+    (src / "quant_kernels.hip").write_text("int q = 2;\n")
+    assert bench.kernel_source_sha(str(src)) == with_q == base
 
 
 def _with_traffic(tmp_path, monkeypatch, record):
